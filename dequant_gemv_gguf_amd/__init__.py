@@ -1,0 +1,26 @@
+"""Fused GGUF K-quant dequant-GEMV for AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libkqgemv.so`` whose C ABI is declared in
+``include/kqgemv.h``.  The functions keep the C names and only marshal
+arguments (torch tensors -> device pointers, the current torch stream ->
+hipStream_t); every step of the computation runs in the HIP kernels.  There is
+no fallback: if the shared library is missing, loading it raises.
+"""
+from ._binding import (  # noqa: F401
+    KQError,
+    KQ_TYPE_Q2_K,
+    KQ_TYPE_Q4_K,
+    KQ_TYPE_Q6_K,
+    KQ_TYPE_Q8_0,
+    STATUS,
+    kq_block_info,
+    kq_dequant,
+    kq_qgemv,
+    kq_qmoe_gemv,
+    kq_qmoe_workspace_bytes,
+    kq_row_bytes,
+    kq_status_string,
+    kq_version,
+    lib,
+    lib_path,
+)

@@ -1,0 +1,110 @@
+"""ctypes marshalling for libkqgemv.so (see include/kqgemv.h for semantics)."""
+import ctypes
+import os
+
+KQ_TYPE_Q8_0, KQ_TYPE_Q2_K, KQ_TYPE_Q4_K, KQ_TYPE_Q6_K = 8, 10, 12, 14
+
+STATUS = {
+    0: "KQ_OK", -1: "KQ_ERR_TYPE", -2: "KQ_ERR_SHAPE", -3: "KQ_ERR_M", -4: "KQ_ERR_NULL",
+    -5: "KQ_ERR_ALIGN", -6: "KQ_ERR_ARG", -7: "KQ_ERR_LAUNCH", -8: "KQ_ERR_DEVICE",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libkqgemv.so")
+
+_lib = None
+
+
+class KQError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, kq_status_string(status), status))
+
+
+def lib():
+    """Load the in-tree shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError("libkqgemv.so is not built; run __graft_entry__.build() or "
+                              "python dequant_gemv_gguf_amd/build.py")
+        L = ctypes.CDLL(lib_path)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.kq_version.restype = I
+        L.kq_status_string.argtypes = [I]
+        L.kq_status_string.restype = ctypes.c_char_p
+        L.kq_block_info.argtypes = [I, P, P]
+        L.kq_row_bytes.argtypes = [I, I64]
+        L.kq_row_bytes.restype = I64
+        L.kq_dequant.argtypes = [I, P, I64, P, P]
+        L.kq_qgemv.argtypes = [I, P, I64, I64, P, I, P, P]
+        L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
+        L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
+        L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a torch tensor, an int address, or None (NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, like):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    if like is not None and not isinstance(like, int) and like.is_cuda:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream(like.device).cuda_stream)
+    return None
+
+
+def _check(fn, r):
+    if r != 0:
+        raise KQError(fn, r)
+
+
+def kq_version():
+    return lib().kq_version()
+
+
+def kq_status_string(status):
+    return lib().kq_status_string(int(status)).decode()
+
+
+def kq_block_info(qtype):
+    qk, nb = ctypes.c_int(), ctypes.c_int()
+    _check("kq_block_info", lib().kq_block_info(int(qtype), ctypes.byref(qk), ctypes.byref(nb)))
+    return qk.value, nb.value
+
+
+def kq_row_bytes(qtype, K):
+    r = lib().kq_row_bytes(int(qtype), int(K))
+    if r < 0:
+        raise KQError("kq_row_bytes", int(r))
+    return int(r)
+
+
+def kq_dequant(qtype, src, n_elems, dst, stream=None):
+    _check("kq_dequant", lib().kq_dequant(int(qtype), _ptr(src), int(n_elems), _ptr(dst),
+                                          _stream(stream, dst)))
+
+
+def kq_qgemv(qtype, W, N, K, x, M, y, stream=None):
+    _check("kq_qgemv", lib().kq_qgemv(int(qtype), _ptr(W), int(N), int(K), _ptr(x), int(M), _ptr(y),
+                                      _stream(stream, y)))
+
+
+def kq_qmoe_workspace_bytes(T, k, N):
+    return int(lib().kq_qmoe_workspace_bytes(int(T), int(k), int(N)))
+
+
+def kq_qmoe_gemv(qtype, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, workspace=None,
+                 err_flag=None, stream=None):
+    _check("kq_qmoe_gemv", lib().kq_qmoe_gemv(int(qtype), _ptr(W_exps), int(E), int(N), int(K), _ptr(ids),
+                                              _ptr(route_w), int(T), int(k), _ptr(x), int(x_mode), _ptr(y),
+                                              _ptr(workspace), _ptr(err_flag), _stream(stream, y)))

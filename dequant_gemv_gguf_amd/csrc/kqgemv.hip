@@ -1,0 +1,969 @@
+// kqgemv.hip -- fused GGUF K-quant dequant-GEMV kernels for AMD MI355X
+// (gfx950, CDNA4) behind the C ABI of include/kqgemv.h.
+//
+// Prior art on the pages: fused dequant-matmul kernels that expand quantized
+// weights only in registers (Kortex summary, section Approach; Kortex article,
+// section Key components, item 3) and native K-quant kernels for Q2_K..Q6_K and
+// Q8_0 (RunNburn post).  Their designs target other hardware; this file is a
+// gfx950 design of the same operation.
+//
+// Design (memory-bound matvec, one pass over the packed weights):
+//  * Weights are read with 128-bit buffer loads (raw buffer resources give
+//    hardware bounds checks: a read past the tile returns zeros, never faults).
+//    Q6_K and Q8_0 blocks may start 2 bytes off a dword; their fields are
+//    read from the dword-aligned address below and realigned with
+//    v_alignbyte.
+//  * Each lane owns "units" of 64 weights (32 for Q8_0) that share their
+//    scales; a group of LPR lanes (16, 32 or 64) walks the units of R rows, so
+//    one read of the activations serves R rows.  Unit u of a row always goes
+//    to lane u % LPR in ascending order, whatever M, R or the K chunk, so the
+//    rounding of a row's result does not depend on M (an M = 8 call gives the
+//    M = 1 bits on each row).
+//  * Activations are staged in LDS per K chunk (padded by 16 B every 64
+//    floats so that lanes reading 256-B-strided unit slices hit distinct
+//    banks), together with exact-order fp32 sums of every 16 activations for
+//    the factored min / offset terms.
+//  * Quants are turned into fp16 *subnormal* bit patterns with one mask per
+//    two weights (a 4-bit q in the low bits of a half is exactly q * 2^-24; a
+//    nibble kept in place is 16q * 2^-24) and multiplied by the fp32
+//    activation with v_fma_mix_f32, which widens the half exactly.  The
+//    power-of-two factors are folded into the per-sub-block scales.
+//  * Per unit and sub-block: acc += (d*sc) * sum(q*x) - (dmin*m) * sum(x)
+//    (Q6_K: d*sc*(sum(q*x) - 32*sum(x)); Q8_0: d*(sum((q+128)*x) - 128*sum(x))).
+//  * Lane partials are summed with DPP inside 16-lane rows and lane swizzles
+//    across rows; one lane per row group stores y.  No atomics anywhere.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kqgemv.h"
+
+#define KQ_VERSION 10000
+
+namespace {
+
+typedef uint32_t u32;
+typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef u32 u4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int WG_THREADS = 256;   // 4 waves of 64
+constexpr int WAVES = WG_THREADS / 64;
+constexpr u32 OOB = 0x80000000u;  // an offset past every tile: loads return 0
+
+// ---------------------------------------------------------------------------
+// Format constants (GGUF convention)
+
+enum { T_Q8_0 = KQ_TYPE_Q8_0, T_Q2_K = KQ_TYPE_Q2_K, T_Q4_K = KQ_TYPE_Q4_K, T_Q6_K = KQ_TYPE_Q6_K };
+
+template <int T> struct Fmt;
+template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BYTES = 144, UPB = 4, KM = 1; };
+template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BYTES = 210, UPB = 4, KM = 32; };
+template <> struct Fmt<T_Q2_K> { static constexpr int QK = 256, BYTES = 84, UPB = 4, KM = 1; };
+template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BYTES = 34, UPB = 1, KM = 128; };
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+
+// A raw buffer over [base, base + nbytes).  The range check zeroes every
+// dword that is not entirely inside the range, so the size is rounded up to a
+// whole dword: a dword holding a valid byte never crosses a page boundary, and
+// bytes past the data in it are never used.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, u32 nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)((nbytes + 3u) & ~3u),
+                                             0x00020000);
+}
+__device__ __forceinline__ u4 ld16(rsrc_t r, u32 off) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32 ld4(rsrc_t r, u32 off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ u32 realign(u32 hi, u32 lo, u32 sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+__device__ __forceinline__ float half_lo(u32 v) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+}
+__device__ __forceinline__ hf2 as_h2(u32 v) { return __builtin_bit_cast(hf2, v); }
+__device__ __forceinline__ f4 lds4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+
+// x element e of a staged chunk lives at e + 4 * (e / 64)
+__device__ __forceinline__ int xpad(int e) { return e + ((e >> 6) << 2); }
+
+// Sum across the LPR lanes of a lane group; every lane of the group ends with
+// the total.  Order is fixed by lane position only.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+    int iv = __builtin_bit_cast(int, v);
+    int t;
+    switch (ctrl_sel) {
+    case 0: t = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: t = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: t = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: t = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return v + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float group_sum(float v, int lpr) {
+    v = dpp_add(v, 0);
+    v = dpp_add(v, 1);
+    v = dpp_add(v, 2);
+    v = dpp_add(v, 3);
+    if (lpr >= 32) v += __shfl_xor(v, 16);
+    if (lpr >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-format unit loaders and multiply-accumulate.
+//
+// A unit's raw registers are loaded for R rows at once; `xo` is the LDS
+// offset of the unit's first activation in row 0 of the staged chunk, `so`
+// the offset of its first 16-sum; rows of x are XS floats apart and rows of
+// sums SS floats apart.
+
+// ---- Q4_K: unit (block b, group g) = quant bytes 32g..32g+31, i.e. weights
+// 64g..64g+31 (low nibbles, sub-block 2g) and 64g+32..64g+63 (high nibbles,
+// sub-block 2g+1); plus the 16-byte header.
+struct RawQ4K { u4 h, qa, qb; };
+
+__device__ __forceinline__ void load_q4k(RawQ4K &r, rsrc_t rs, u32 off, int g) {
+    r.h = ld16(rs, off);
+    r.qa = ld16(rs, off + 16 + 32 * g);
+    r.qb = ld16(rs, off + 32 + 32 * g);
+}
+
+template <int M, int R>
+__device__ __forceinline__ void mac_q4k(const RawQ4K (&raw)[R], int g, const float *xs, int xo, int XS,
+                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+    float dsc0[R], dsc1[R], dm0[R], dm1[R];
+    const u32 sel = (u32)(2 * g) | ((u32)(2 * g + 1) << 8) | 0x0C0C0000u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const u32 h0 = raw[r].h.x, h1 = raw[r].h.y, h2 = raw[r].h.z, h3 = raw[r].h.w;
+        const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
+        const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
+        const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+        const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+        const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel);
+        const u32 mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
+        dsc0[r] = d * (float)(sc & 0xFFu);
+        dsc1[r] = (d * 0.0625f) * (float)((sc >> 8) & 0xFFu);
+        dm0[r] = dmin * (float)(mm & 0xFFu);
+        dm1[r] = dmin * (float)((mm >> 8) & 0xFFu);
+    }
+    float slo[R][M], shi[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) slo[r][m] = shi[r][m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f4 xl[M], xh[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            xl[m] = lds4(xs + m * XS + xo + xpad(4 * i) - xpad(0));
+            xh[m] = lds4(xs + m * XS + xo + xpad(32 + 4 * i) - xpad(0));
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32 D = i < 4 ? raw[r].qa[i & 3] : raw[r].qb[i & 3];
+            const u32 D8 = D >> 8;
+            const hf2 a = as_h2(D & 0x000F000Fu), b = as_h2(D8 & 0x000F000Fu);
+            const hf2 c = as_h2(D & 0x00F000F0u), e = as_h2(D8 & 0x00F000F0u);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s = slo[r][m];
+                s = __builtin_fmaf((float)a.x, xl[m].x, s);
+                s = __builtin_fmaf((float)b.x, xl[m].y, s);
+                s = __builtin_fmaf((float)a.y, xl[m].z, s);
+                s = __builtin_fmaf((float)b.y, xl[m].w, s);
+                slo[r][m] = s;
+                float t = shi[r][m];
+                t = __builtin_fmaf((float)c.x, xh[m].x, t);
+                t = __builtin_fmaf((float)e.x, xh[m].y, t);
+                t = __builtin_fmaf((float)c.y, xh[m].z, t);
+                t = __builtin_fmaf((float)e.y, xh[m].w, t);
+                shi[r][m] = t;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const f4 sx = lds4(ss + m * SS + so);
+        const float s_lo = sx.x + sx.y, s_hi = sx.z + sx.w;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            aq[r][m] = __builtin_fmaf(dsc0[r], slo[r][m], aq[r][m]);
+            aq[r][m] = __builtin_fmaf(dsc1[r], shi[r][m], aq[r][m]);
+            am[r][m] = __builtin_fmaf(dm0[r], s_lo, am[r][m]);
+            am[r][m] = __builtin_fmaf(dm1[r], s_hi, am[r][m]);
+        }
+    }
+}
+
+// ---- Q6_K: unit (block b, half h, quarter q2) = the 64 weights
+// 128h + 32g + 16*q2 + i (g = 0..3, i = 0..15): low bits from bytes
+// 64h + 16*q2 + i (g = 0, 2) and 64h + 32 + 16*q2 + i (g = 1, 3), high bits
+// from byte 128 + 32h + 16*q2 + i, scales 8h + 2g + q2.
+struct RawQ6K { u32 a[4], b[4], hq[4], s0, s1; float d; };
+
+__device__ __forceinline__ void load_q6k(RawQ6K &r, rsrc_t rs, u32 off, int h, int q2) {
+    const u32 sh = off & 3u, base = off - sh;
+    const u32 oa = base + 64 * h + 16 * q2;
+    const u4 a = ld16(rs, oa), b = ld16(rs, oa + 32), hq = ld16(rs, base + 128 + 32 * h + 16 * q2);
+    const u32 a4 = ld4(rs, oa + 16), b4 = ld4(rs, oa + 48), h4 = ld4(rs, base + 144 + 32 * h + 16 * q2);
+    const u4 sc = ld16(rs, base + 192 + 8 * h);
+    const u32 dw = ld4(rs, base + 208);
+    r.a[0] = realign(a.y, a.x, sh); r.a[1] = realign(a.z, a.y, sh);
+    r.a[2] = realign(a.w, a.z, sh); r.a[3] = realign(a4, a.w, sh);
+    r.b[0] = realign(b.y, b.x, sh); r.b[1] = realign(b.z, b.y, sh);
+    r.b[2] = realign(b.w, b.z, sh); r.b[3] = realign(b4, b.w, sh);
+    r.hq[0] = realign(hq.y, hq.x, sh); r.hq[1] = realign(hq.z, hq.y, sh);
+    r.hq[2] = realign(hq.w, hq.z, sh); r.hq[3] = realign(h4, hq.w, sh);
+    r.s0 = realign(sc.y, sc.x, sh);
+    r.s1 = realign(sc.z, sc.y, sh);
+    r.d = half_lo(dw >> (8 * sh));
+}
+
+template <int M, int R>
+__device__ __forceinline__ void mac_q6k(const RawQ6K (&raw)[R], int q2, const float *xs, int xo, int XS,
+                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+    float dsc[R][4];
+    const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const u32 p = __builtin_amdgcn_perm(raw[r].s1, raw[r].s0, sel);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dsc[r][g] = raw[r].d * (float)(int)(signed char)(p >> (8 * g));
+    }
+    float acc[R][M][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[r][m][g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f4 xv[M][4];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) xv[m][g] = lds4(xs + m * XS + xo + xpad(32 * g + 4 * k) - xpad(0));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32 A = raw[r].a[k], B = raw[r].b[k], H = raw[r].hq[k];
+            const u32 A8 = A >> 8, B8 = B >> 8;
+            const u32 H4l = H << 4, H4r = H >> 4, H2l = H << 2, H6r = H >> 6;
+            hf2 w[4][2];
+            w[0][0] = as_h2((A & 0x000F000Fu) | (H4l & 0x00300030u));
+            w[0][1] = as_h2((A8 & 0x000F000Fu) | (H4r & 0x00300030u));
+            w[1][0] = as_h2((B & 0x000F000Fu) | (H2l & 0x00300030u));
+            w[1][1] = as_h2((B8 & 0x000F000Fu) | (H6r & 0x00300030u));
+            w[2][0] = as_h2((A & 0x00F000F0u) | (H4l & 0x03000300u));
+            w[2][1] = as_h2((A8 & 0x00F000F0u) | (H4r & 0x03000300u));
+            w[3][0] = as_h2((B & 0x00F000F0u) | (H2l & 0x03000300u));
+            w[3][1] = as_h2((B8 & 0x00F000F0u) | (H6r & 0x03000300u));
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float s = acc[r][m][g];
+                    s = __builtin_fmaf((float)w[g][0].x, xv[m][g].x, s);
+                    s = __builtin_fmaf((float)w[g][1].x, xv[m][g].y, s);
+                    s = __builtin_fmaf((float)w[g][0].y, xv[m][g].z, s);
+                    s = __builtin_fmaf((float)w[g][1].y, xv[m][g].w, s);
+                    acc[r][m][g] = s;
+                }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float *sp = ss + m * SS + so;
+        const float sx[4] = {sp[0], sp[2], sp[4], sp[6]};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            aq[r][m] = __builtin_fmaf(dsc[r][0], acc[r][m][0], aq[r][m]);
+            aq[r][m] = __builtin_fmaf(dsc[r][1], acc[r][m][1], aq[r][m]);
+            aq[r][m] = __builtin_fmaf(dsc[r][2] * 0.0625f, acc[r][m][2], aq[r][m]);
+            aq[r][m] = __builtin_fmaf(dsc[r][3] * 0.0625f, acc[r][m][3], aq[r][m]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) am[r][m] = __builtin_fmaf(dsc[r][g], sx[g], am[r][m]);
+        }
+    }
+}
+
+// ---- Q2_K: unit (block b, half h, quarter q2) = the 64 weights
+// 128h + 32s + 16*q2 + i (s = 0..3, i = 0..15): bits 2s..2s+1 of quant byte
+// 32h + 16*q2 + i, scale/min byte 8h + 2s + q2.
+struct RawQ2K { u4 q; u32 s0, s1, dd; };
+
+__device__ __forceinline__ void load_q2k(RawQ2K &r, rsrc_t rs, u32 off, int h, int q2) {
+    r.q = ld16(rs, off + 16 + 32 * h + 16 * q2);
+    const u4 sc = ld16(rs, off + 8 * h);   // bytes 8h .. 8h+15 (only 8 used)
+    r.s0 = sc.x;
+    r.s1 = sc.y;
+    r.dd = ld4(rs, off + 80);
+}
+
+template <int M, int R>
+__device__ __forceinline__ void mac_q2k(const RawQ2K (&raw)[R], int q2, const float *xs, int xo, int XS,
+                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+    float dsc[R][4], dmm[R][4];
+    const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const u32 p = __builtin_amdgcn_perm(raw[r].s1, raw[r].s0, sel);
+        const float d = half_lo(raw[r].dd), dmin = half_lo(raw[r].dd >> 16);
+        const float dq[4] = {d, d * 0.25f, d * 0.0625f, d * 0.015625f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            dsc[r][s] = dq[s] * (float)((p >> (8 * s)) & 15u);
+            dmm[r][s] = dmin * (float)((p >> (8 * s + 4)) & 15u);
+        }
+    }
+    float acc[R][M][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[r][m][s] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f4 xv[M][4];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xv[m][s] = lds4(xs + m * XS + xo + xpad(32 * s + 4 * k) - xpad(0));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32 D = raw[r].q[k], D8 = D >> 8;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32 mask = 0x00030003u << (2 * s);
+                const hf2 we = as_h2(D & mask), wo = as_h2(D8 & mask);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float t = acc[r][m][s];
+                    t = __builtin_fmaf((float)we.x, xv[m][s].x, t);
+                    t = __builtin_fmaf((float)wo.x, xv[m][s].y, t);
+                    t = __builtin_fmaf((float)we.y, xv[m][s].z, t);
+                    t = __builtin_fmaf((float)wo.y, xv[m][s].w, t);
+                    acc[r][m][s] = t;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float *sp = ss + m * SS + so;
+        const float sx[4] = {sp[0], sp[2], sp[4], sp[6]};
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                aq[r][m] = __builtin_fmaf(dsc[r][s], acc[r][m][s], aq[r][m]);
+                am[r][m] = __builtin_fmaf(dmm[r][s], sx[s], am[r][m]);
+            }
+    }
+}
+
+// ---- Q8_0: unit = one block of 32 weights.
+struct RawQ80 { u32 q[8]; float d; };
+
+__device__ __forceinline__ void load_q80(RawQ80 &r, rsrc_t rs, u32 off) {
+    const u32 qo = off + 2, sh = qo & 3u, qb = qo - sh;
+    const u4 a = ld16(rs, qb), b = ld16(rs, qb + 16);
+    const u32 c = ld4(rs, qb + 32);
+    const u32 dw = ld4(rs, off & ~3u);
+    r.q[0] = realign(a.y, a.x, sh); r.q[1] = realign(a.z, a.y, sh);
+    r.q[2] = realign(a.w, a.z, sh); r.q[3] = realign(b.x, a.w, sh);
+    r.q[4] = realign(b.y, b.x, sh); r.q[5] = realign(b.z, b.y, sh);
+    r.q[6] = realign(b.w, b.z, sh); r.q[7] = realign(c, b.w, sh);
+    r.d = half_lo(dw >> (8 * (off & 3u)));
+}
+
+template <int M, int R>
+__device__ __forceinline__ void mac_q80(const RawQ80 (&raw)[R], const float *xs, int xo, int XS,
+                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = lds4(xs + m * XS + xo + xpad(4 * i) - xpad(0));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32 U = raw[r].q[i] ^ 0x80808080u;    // q + 128 as unsigned bytes
+            const hf2 we = as_h2(U & 0x00FF00FFu), wo = as_h2((U >> 8) & 0x00FF00FFu);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float t = acc[r][m];
+                t = __builtin_fmaf((float)we.x, xv[m].x, t);
+                t = __builtin_fmaf((float)wo.x, xv[m].y, t);
+                t = __builtin_fmaf((float)we.y, xv[m].z, t);
+                t = __builtin_fmaf((float)wo.y, xv[m].w, t);
+                acc[r][m] = t;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float sx = ss[m * SS + so] + ss[m * SS + so + 1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            aq[r][m] = __builtin_fmaf(raw[r].d, acc[r][m], aq[r][m]);
+            am[r][m] = __builtin_fmaf(raw[r].d, sx, am[r][m]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Activation staging: rows xr[0..M) of the chunk [c0, c0 + kc) go to LDS with
+// 16 B of padding every 64 floats; sums[m][j] = sum of x[c0 + 16j .. +16) in a
+// fixed order.  kc is a multiple of 32.
+
+template <int M>
+__device__ __forceinline__ void stage_x(float *xs, float *ss, int XS, int SS, const float *const (&xr)[M],
+                                        int c0, int kc) {
+    const int n16 = kc >> 4;
+    for (int idx = threadIdx.x; idx < M * n16; idx += WG_THREADS) {
+        const int m = idx / n16, j = idx - m * n16;
+        const f4 *src = reinterpret_cast<const f4 *>(xr[m] + c0 + 16 * j);
+        const f4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+        float *dst = xs + m * XS + xpad(16 * j);
+        reinterpret_cast<f4 *>(dst)[0] = v0;
+        reinterpret_cast<f4 *>(dst)[1] = v1;
+        reinterpret_cast<f4 *>(dst)[2] = v2;
+        reinterpret_cast<f4 *>(dst)[3] = v3;
+        const float s = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
+                        (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
+        ss[m * SS + j] = s;
+    }
+}
+
+// LDS row strides (multiples of 4 floats, so every row starts 16-B aligned)
+// and the LDS floats needed for M rows and a chunk of kc columns.
+__host__ __device__ constexpr int x_stride(int kc) { return (kc + (kc >> 4) + 3) & ~3; }
+__host__ __device__ constexpr int s_stride(int kc) { return ((kc >> 4) + 3) & ~3; }
+__host__ __device__ constexpr int lds_floats(int M, int kc) { return M * (x_stride(kc) + s_stride(kc)); }
+
+// ---------------------------------------------------------------------------
+// One work-group computes `nrows` rows starting at `row0` of one matrix for M
+// activation rows xr[] and writes yr[m][row] for each of them.
+
+template <int T, int M, int R>
+__device__ __forceinline__ void gemv_tile(float *smem, const uint8_t *W, int64_t row_bytes, int row0, int nrows,
+                                          int K, int KC, int lpr, const float *const (&xr)[M],
+                                          float *const (&yr)[M]) {
+    typedef Fmt<T> F;
+    const int G = 64 / lpr;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int grp = lane / lpr, slot = lane - grp * lpr;
+    const int rfirst = (wave * G + grp) * R;     // first tile-relative row of this group
+
+    const uintptr_t ta = (uintptr_t)(W + (int64_t)row0 * row_bytes);
+    const u32 delta = (u32)(ta & 3u);
+    const rsrc_t rs = make_rsrc((const void *)(ta - delta), delta + (u32)((int64_t)nrows * row_bytes));
+    u32 roff[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int rr = rfirst + r;
+        roff[r] = rr < nrows ? delta + (u32)((int64_t)rr * row_bytes) : OOB;
+    }
+
+    float aq[R][M], am[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) aq[r][m] = am[r][m] = 0.f;
+
+    const int kcmax = KC < K ? KC : K;
+    const int XS = x_stride(kcmax);
+    const int SS = s_stride(kcmax);
+    float *xs = smem;
+    float *ss = smem + M * XS;
+
+    for (int c0 = 0; c0 < K; c0 += KC) {
+        const int kc = (K - c0) < KC ? (K - c0) : KC;
+        if (c0) __syncthreads();
+        stage_x<M>(xs, ss, XS, SS, xr, c0, kc);
+        __syncthreads();
+        const int units = (kc / F::QK) * F::UPB;
+        const int b0 = c0 / F::QK;
+        for (int ul = slot; ul < units; ul += lpr) {
+            const int bl = ul / F::UPB, sub = ul - bl * F::UPB;
+            const u32 boff = (u32)(b0 + bl) * F::BYTES;
+            const int xe = bl * F::QK;              // chunk-relative first weight of the block
+            if constexpr (T == T_Q4_K) {
+                RawQ4K raw[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) load_q4k(raw[r], rs, roff[r] + boff, sub);
+                const int e0 = xe + 64 * sub;
+                mac_q4k<M, R>(raw, sub, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
+            } else if constexpr (T == T_Q6_K) {
+                const int h = sub >> 1, q2 = sub & 1;
+                RawQ6K raw[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) load_q6k(raw[r], rs, roff[r] + boff, h, q2);
+                const int e0 = xe + 128 * h + 16 * q2;
+                mac_q6k<M, R>(raw, q2, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
+            } else if constexpr (T == T_Q2_K) {
+                const int h = sub >> 1, q2 = sub & 1;
+                RawQ2K raw[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) load_q2k(raw[r], rs, roff[r] + boff, h, q2);
+                const int e0 = xe + 128 * h + 16 * q2;
+                mac_q2k<M, R>(raw, q2, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
+            } else {
+                RawQ80 raw[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) load_q80(raw[r], rs, roff[r] + boff);
+                mac_q80<M, R>(raw, xs, xpad(xe), XS, ss, xe >> 4, SS, aq, am);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = __builtin_fmaf(aq[r][m], 16777216.0f, -(float)F::KM * am[r][m]);
+            const float tot = group_sum(v, lpr);
+            const int rr = rfirst + r;
+            if (slot == 0 && rr < nrows) yr[m][row0 + rr] = tot;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels
+
+template <int T, int M, int R>
+__global__ __launch_bounds__(WG_THREADS) void qgemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes,
+                                                           int N, int K, int KC, int lpr,
+                                                           const float *__restrict__ x, float *__restrict__ y) {
+    extern __shared__ float smem[];
+    const int rows_per_wg = WAVES * (64 / lpr) * R;
+    const int row0 = blockIdx.x * rows_per_wg;
+    const int nrows = (N - row0) < rows_per_wg ? (N - row0) : rows_per_wg;
+    const float *xr[M];
+    float *yr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        xr[m] = x + (int64_t)m * K;
+        yr[m] = y + (int64_t)m * N;
+    }
+    gemv_tile<T, M, R>(smem, W, row_bytes, row0, nrows, K, KC, lpr, xr, yr);
+}
+
+// Routed experts: work-group (row tile, slot s).  Only the lowest slot that
+// routes to an expert does the work; it collects every slot that routes to the
+// same expert and serves them in batches of up to MAXM activation rows with one
+// pass over the expert's weights per batch.  Invalid ids: zero output, flag.
+template <int T, int M>
+__device__ __forceinline__ void moe_batch(float *smem, const uint8_t *We, int64_t row_bytes, int row0, int nrows,
+                                          int K, int KC, int lpr, const int *members, int x_mode, int k,
+                                          const float *x, float *y, int N) {
+    const float *xr[M];
+    float *yr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int s = members[m];
+        xr[m] = x + (int64_t)(x_mode ? s : s / k) * K;
+        yr[m] = y + (int64_t)s * N;
+    }
+    gemv_tile<T, M, 1>(smem, We, row_bytes, row0, nrows, K, KC, lpr, xr, yr);
+}
+
+template <int T, int MAXM>
+__global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int E,
+                                                          int N, int K, int KC, int lpr,
+                                                          const int32_t *__restrict__ ids, int nslots, int k,
+                                                          const float *__restrict__ x, int x_mode,
+                                                          float *__restrict__ y, int32_t *err_flag) {
+    extern __shared__ float smem[];
+    __shared__ int members[128];
+    const int s = blockIdx.y;
+    const int rows_per_wg = WAVES * (64 / lpr);
+    const int row0 = blockIdx.x * rows_per_wg;
+    const int nrows = (N - row0) < rows_per_wg ? (N - row0) : rows_per_wg;
+    const int e = ids[s];
+    if (e < 0 || e >= E) {
+        for (int i = threadIdx.x; i < nrows; i += WG_THREADS) y[(int64_t)s * N + row0 + i] = 0.f;
+        if (err_flag && threadIdx.x == 0 && blockIdx.x == 0) *err_flag = 1;
+        return;
+    }
+    for (int t = 0; t < s; ++t)
+        if (ids[t] == e) return;               // a lower slot serves this expert
+    int n = 0;
+    for (int t = s; t < nslots; ++t)
+        if (ids[t] == e) {
+            if (threadIdx.x == 0) members[n] = t;
+            ++n;
+        }
+    __syncthreads();
+    const uint8_t *We = W + (int64_t)e * N * row_bytes;
+    for (int b0 = 0; b0 < n; b0 += MAXM) {
+        const int mb = (n - b0) < MAXM ? (n - b0) : MAXM;
+        if (b0) __syncthreads();
+        switch (mb) {
+#define KQ_MOE_CASE(MM) \
+    case MM: if constexpr (MM <= MAXM) moe_batch<T, MM>(smem, We, row_bytes, row0, nrows, K, KC, lpr, members + b0, x_mode, k, x, y, N); break;
+            KQ_MOE_CASE(1) KQ_MOE_CASE(2) KQ_MOE_CASE(3) KQ_MOE_CASE(4)
+            KQ_MOE_CASE(5) KQ_MOE_CASE(6) KQ_MOE_CASE(7) KQ_MOE_CASE(8)
+#undef KQ_MOE_CASE
+        default: break;
+        }
+    }
+}
+
+// y[t][o] = sum_j route_w[t][j] * ys[t][j][o], ascending j.
+__global__ __launch_bounds__(WG_THREADS) void moe_combine_kernel(const float *__restrict__ ys,
+                                                                 const float *__restrict__ rw, int T, int k, int N,
+                                                                 float *__restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * WG_THREADS + threadIdx.x;
+    if (i >= (int64_t)T * N) return;
+    const int t = (int)(i / N);
+    const int64_t o = i - (int64_t)t * N;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = __builtin_fmaf(rw[t * k + j], ys[((int64_t)t * k + j) * N + o], acc);
+    y[i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Standalone dequantization, one unit per thread.  Each weight is the exact
+// product(s) with a single rounding at the subtraction; + 0.0f maps -0 to +0.
+
+template <int T>
+__global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__restrict__ src, int64_t nunits,
+                                                             float *__restrict__ dst) {
+    typedef Fmt<T> F;
+    const int64_t ufirst = (int64_t)blockIdx.x * WG_THREADS;
+    const int64_t u = ufirst + threadIdx.x;
+    const int64_t bfirst = ufirst / F::UPB;
+    const int64_t blast = (ufirst + WG_THREADS + F::UPB - 1) / F::UPB;
+    const int64_t nblocks = nunits / F::UPB;
+    const int64_t bend = blast < nblocks ? blast : nblocks;
+    const uintptr_t ta = (uintptr_t)(src + bfirst * F::BYTES);
+    const u32 delta = (u32)(ta & 3u);
+    const rsrc_t rs = make_rsrc((const void *)(ta - delta), delta + (u32)((bend - bfirst) * F::BYTES));
+    if (u >= nunits) return;
+    const int64_t b = u / F::UPB;
+    const int sub = (int)(u - b * F::UPB);
+    const u32 off = delta + (u32)((b - bfirst) * F::BYTES);
+    float *out = dst + b * F::QK;
+    if constexpr (T == T_Q4_K) {
+        RawQ4K r;
+        load_q4k(r, rs, off, sub);
+        const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
+        const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
+        const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
+        const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+        const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+        const u32 sel = (u32)(2 * sub) | ((u32)(2 * sub + 1) << 8) | 0x0C0C0000u;
+        const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel), mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
+        const float ds0 = d * (float)(sc & 0xFFu), ds1 = d * (float)((sc >> 8) & 0xFFu);
+        const float dm0 = dmin * (float)(mm & 0xFFu), dm1 = dmin * (float)((mm >> 8) & 0xFFu);
+        float lo[32], hi[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32 D = i < 4 ? r.qa[i & 3] : r.qb[i & 3];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32 byte = (D >> (8 * j)) & 0xFFu;
+                lo[4 * i + j] = __builtin_fmaf(ds0, (float)(byte & 15u), -dm0) + 0.0f;
+                hi[4 * i + j] = __builtin_fmaf(ds1, (float)(byte >> 4), -dm1) + 0.0f;
+            }
+        }
+        f4 *o4 = reinterpret_cast<f4 *>(out + 64 * sub);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o4[i] = f4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
+    } else if constexpr (T == T_Q6_K) {
+        const int h = sub >> 1, q2 = sub & 1;
+        RawQ6K r;
+        load_q6k(r, rs, off, h, q2);
+        const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+        const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float dsc = r.d * (float)(int)(signed char)(p >> (8 * g));
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const u32 lowb = (g & 1) ? r.b[i >> 2] : r.a[i >> 2];
+                const u32 byte = (lowb >> (8 * (i & 3))) & 0xFFu;
+                const u32 lo4 = (g < 2) ? (byte & 15u) : (byte >> 4);
+                const u32 hi2 = (r.hq[i >> 2] >> (8 * (i & 3) + 2 * g)) & 3u;
+                w[i] = dsc * (float)((int)(lo4 | (hi2 << 4)) - 32) + 0.0f;
+            }
+            f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * g + 16 * q2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        }
+    } else if constexpr (T == T_Q2_K) {
+        const int h = sub >> 1, q2 = sub & 1;
+        RawQ2K r;
+        load_q2k(r, rs, off, h, q2);
+        const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+        const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
+        const float d = half_lo(r.dd), dmin = half_lo(r.dd >> 16);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float dsc = d * (float)((p >> (8 * s)) & 15u);
+            const float dm = dmin * (float)((p >> (8 * s + 4)) & 15u);
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const u32 q = (r.q[i >> 2] >> (8 * (i & 3) + 2 * s)) & 3u;
+                w[i] = __builtin_fmaf(dsc, (float)q, -dm) + 0.0f;
+            }
+            f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * s + 16 * q2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        }
+    } else {
+        RawQ80 r;
+        load_q80(r, rs, off);
+        float w[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) w[i] = r.d * (float)(int)(signed char)(r.q[i >> 2] >> (8 * (i & 3))) + 0.0f;
+        f4 *o4 = reinterpret_cast<f4 *>(out);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+
+int fmt_of(int type, int *qk, int *bytes, int *upb) {
+    switch (type) {
+    case KQ_TYPE_Q4_K: *qk = 256; *bytes = 144; *upb = 4; return 0;
+    case KQ_TYPE_Q6_K: *qk = 256; *bytes = 210; *upb = 4; return 0;
+    case KQ_TYPE_Q2_K: *qk = 256; *bytes = 84; *upb = 4; return 0;
+    case KQ_TYPE_Q8_0: *qk = 32; *bytes = 34; *upb = 1; return 0;
+    default: return KQ_ERR_TYPE;
+    }
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// K chunk staged in LDS per M: a multiple of 4096 so that the lane owning a
+// unit never depends on the chunking (units per 4096 columns are a multiple of
+// 64 for every format).
+int chunk_for(int M) { return M == 1 ? 8192 : 4096; }
+
+int lanes_per_row(int units) { return units >= 64 ? 64 : (units > 16 ? 32 : 16); }
+
+template <typename Kern>
+hipError_t allow_lds(Kern k, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+template <int T, int M, int R>
+int launch_qgemv_t(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st,
+                   int lpr) {
+    const int KC = chunk_for(M);
+    const int kc = KC < K ? KC : K;
+    const size_t lds = (size_t)lds_floats(M, kc) * sizeof(float);
+    const int rows_per_wg = WAVES * (64 / lpr) * R;
+    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
+    auto kern = qgemv_kernel<T, M, R>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WG_THREADS), lds, st, (const uint8_t *)W, row_bytes, N, K, KC, lpr,
+                       x, y);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+template <int T>
+int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const float *x, float *y,
+                   hipStream_t st) {
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int G = 64 / lpr;
+    switch (M) {
+    case 1: {
+        const int R = N >= 8192 * G ? 4 : (N >= 4096 * G ? 2 : 1);
+        if (R == 4) return launch_qgemv_t<T, 1, 4>(W, row_bytes, N, K, x, y, st, lpr);
+        if (R == 2) return launch_qgemv_t<T, 1, 2>(W, row_bytes, N, K, x, y, st, lpr);
+        return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    }
+    case 2: return launch_qgemv_t<T, 2, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 3: return launch_qgemv_t<T, 3, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 4: return launch_qgemv_t<T, 4, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 5: return launch_qgemv_t<T, 5, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 6: return launch_qgemv_t<T, 6, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 7: return launch_qgemv_t<T, 7, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    default: return launch_qgemv_t<T, 8, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    }
+}
+
+template <int T, int MAXM>
+int launch_qmoe_t(const void *W, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_, int k,
+                  const float *x, int x_mode, float *ys, int32_t *err, hipStream_t st) {
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int KC = chunk_for(MAXM);
+    const int kc = KC < K ? KC : K;
+    const size_t lds = (size_t)lds_floats(MAXM, kc) * sizeof(float);
+    const int rows_per_wg = WAVES * (64 / lpr);
+    dim3 grid((N + rows_per_wg - 1) / rows_per_wg, T_ * k);
+    auto kern = qmoe_kernel<T, MAXM>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, grid, dim3(WG_THREADS), lds, st, (const uint8_t *)W, row_bytes, E, N, K, KC, lpr, ids,
+                       T_ * k, k, x, x_mode, ys, err);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+template <int T>
+int launch_qmoe_m(int maxm, const void *W, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_,
+                  int k, const float *x, int x_mode, float *ys, int32_t *err, hipStream_t st) {
+    switch (maxm) {
+    case 1: return launch_qmoe_t<T, 1>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
+    case 2: return launch_qmoe_t<T, 2>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
+    case 3: case 4: return launch_qmoe_t<T, 4>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
+    default: return launch_qmoe_t<T, 8>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
+    }
+}
+
+template <int T>
+int launch_dequant_t(const void *src, int64_t n, float *dst, hipStream_t st) {
+    const int64_t nunits = (n / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int64_t grid = (nunits + WG_THREADS - 1) / WG_THREADS;
+    hipLaunchKernelGGL(dequant_kernel<T>, dim3((unsigned)grid), dim3(WG_THREADS), 0, st, (const uint8_t *)src,
+                       nunits, dst);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+} // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int kq_version(void) { return KQ_VERSION; }
+
+const char *kq_status_string(int status) {
+    switch (status) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_TYPE: return "unsupported quant type";
+    case KQ_ERR_SHAPE: return "invalid shape";
+    case KQ_ERR_M: return "row count M (or T) outside 1..8";
+    case KQ_ERR_NULL: return "required pointer is NULL";
+    case KQ_ERR_ALIGN: return "pointer misaligned";
+    case KQ_ERR_ARG: return "invalid argument";
+    case KQ_ERR_LAUNCH: return "kernel launch failed";
+    case KQ_ERR_DEVICE: return "no usable device";
+    default: return "unknown status";
+    }
+}
+
+int kq_block_info(int type, int *block_elems, int *block_bytes) {
+    int qk, nb, upb;
+    if (fmt_of(type, &qk, &nb, &upb)) return KQ_ERR_TYPE;
+    if (!block_elems || !block_bytes) return KQ_ERR_NULL;
+    *block_elems = qk;
+    *block_bytes = nb;
+    return KQ_OK;
+}
+
+int64_t kq_row_bytes(int type, int64_t K) {
+    int qk, nb, upb;
+    if (fmt_of(type, &qk, &nb, &upb)) return KQ_ERR_TYPE;
+    if (K <= 0 || K % qk) return KQ_ERR_SHAPE;
+    return (K / qk) * nb;
+}
+
+int kq_dequant(int type, const void *src, int64_t n_elems, float *dst, void *stream) {
+    int qk, nb, upb;
+    if (fmt_of(type, &qk, &nb, &upb)) return KQ_ERR_TYPE;
+    if (n_elems < 0 || n_elems % qk || n_elems > ((int64_t)1 << 40)) return KQ_ERR_SHAPE;
+    if (n_elems == 0) return KQ_OK;
+    if (!src || !dst) return KQ_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return KQ_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    switch (type) {
+    case KQ_TYPE_Q4_K: return launch_dequant_t<T_Q4_K>(src, n_elems, dst, st);
+    case KQ_TYPE_Q6_K: return launch_dequant_t<T_Q6_K>(src, n_elems, dst, st);
+    case KQ_TYPE_Q2_K: return launch_dequant_t<T_Q2_K>(src, n_elems, dst, st);
+    default: return launch_dequant_t<T_Q8_0>(src, n_elems, dst, st);
+    }
+}
+
+static int check_gemv_shape(int type, int64_t N, int64_t K, int64_t *row_bytes) {
+    int qk, nb, upb;
+    if (fmt_of(type, &qk, &nb, &upb)) return KQ_ERR_TYPE;
+    if (K <= 0 || K % qk || K > ((int64_t)1 << 20)) return KQ_ERR_SHAPE;
+    if (N < 0 || N >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
+    *row_bytes = (K / qk) * nb;
+    // one work-group tile (at most 64 rows) must stay below 2^31 bytes
+    if (64 * *row_bytes >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
+    return KQ_OK;
+}
+
+int kq_qgemv(int type, const void *W, int64_t N, int64_t K, const float *x, int M, float *y, void *stream) {
+    int64_t row_bytes;
+    int r = check_gemv_shape(type, N, K, &row_bytes);
+    if (r) return r;
+    if (M < 1 || M > 8) return KQ_ERR_M;
+    if (N == 0) return KQ_OK;
+    if (!W || !x || !y) return KQ_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return KQ_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    switch (type) {
+    case KQ_TYPE_Q4_K: return launch_qgemv_m<T_Q4_K>(M, W, row_bytes, (int)N, (int)K, x, y, st);
+    case KQ_TYPE_Q6_K: return launch_qgemv_m<T_Q6_K>(M, W, row_bytes, (int)N, (int)K, x, y, st);
+    case KQ_TYPE_Q2_K: return launch_qgemv_m<T_Q2_K>(M, W, row_bytes, (int)N, (int)K, x, y, st);
+    default: return launch_qgemv_m<T_Q8_0>(M, W, row_bytes, (int)N, (int)K, x, y, st);
+    }
+}
+
+size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N) {
+    if (T < 1 || T > 8 || k < 1 || k > 16 || N < 0 || N >= ((int64_t)1 << 31)) return 0;
+    return (size_t)T * (size_t)k * (size_t)N * sizeof(float);
+}
+
+int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, const int32_t *ids,
+                 const float *route_w, int T, int k, const float *x, int x_mode, float *y, float *workspace,
+                 int32_t *err_flag, void *stream) {
+    int64_t row_bytes;
+    int r = check_gemv_shape(type, N, K, &row_bytes);
+    if (r) return r;
+    if (T < 1 || T > 8) return KQ_ERR_M;
+    if (E < 1 || E >= ((int64_t)1 << 31) || k < 1 || k > 16 || k > E || (x_mode != 0 && x_mode != 1))
+        return KQ_ERR_ARG;
+    if (N == 0) return KQ_OK;
+    if (!W_exps || !ids || !x || !y || (route_w && !workspace)) return KQ_ERR_NULL;
+    if (!aligned(W_exps, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) ||
+        (route_w && (!aligned(route_w, 4) || !aligned(workspace, 16))) || (err_flag && !aligned(err_flag, 4)))
+        return KQ_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    float *ys = route_w ? workspace : y;
+    // a batch never holds more slots than there are tokens unless a token
+    // repeats an expert; MAXM = T covers the distinct-ids case in one pass
+    const int maxm = T;
+    switch (type) {
+    case KQ_TYPE_Q4_K: r = launch_qmoe_m<T_Q4_K>(maxm, W_exps, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode, ys, err_flag, st); break;
+    case KQ_TYPE_Q6_K: r = launch_qmoe_m<T_Q6_K>(maxm, W_exps, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode, ys, err_flag, st); break;
+    case KQ_TYPE_Q2_K: r = launch_qmoe_m<T_Q2_K>(maxm, W_exps, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode, ys, err_flag, st); break;
+    default: r = launch_qmoe_m<T_Q8_0>(maxm, W_exps, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode, ys, err_flag, st); break;
+    }
+    if (r || !route_w) return r;
+    const int64_t total = (int64_t)T * N;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + WG_THREADS - 1) / WG_THREADS)), dim3(WG_THREADS),
+                       0, st, workspace, route_w, T, k, (int)N, y);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+} // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * kqgemv.h -- C ABI of the fused GGUF K-quant dequant-GEMV library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the calls compute.  Decode-time LLM engines spend their time streaming
+ * quantized weights through a matrix-vector product; the weights are expanded
+ * to real values only inside the product, in registers, never written back
+ * (Kortex: "Out-of-core LLM inference engine written from scratch in Rust",
+ * section Approach, and "Kortex: Streaming 70B Models on Consumer GPUs",
+ * section Key components, item 3).  The block formats are the GGUF K-quants
+ * the RunNburn post lists native kernels for ("RunNburn - Run a 295B Moe from
+ * a 98GB GGUF on a 64GB RAM Desktop"): Q2_K, Q4_K, Q6_K and Q8_0.  A
+ * speculative-verify pass runs several positions through one pass of the
+ * weights (Kortex summary, section Approach): here M <= 8 activation rows.  The
+ * MoE variant applies the experts each token selected (the RunNburn post).
+ *
+ * Block formats (GGUF convention; the pages name the formats but print no
+ * layout, so this is a reading):
+ *   Q4_K  256 weights / 144 B   w = d*sc*q - dmin*m   (6-bit sc, m per 32)
+ *   Q6_K  256 weights / 210 B   w = d*sc*(q - 32)     (int8 sc per 16)
+ *   Q2_K  256 weights /  84 B   w = d*sc*q - dmin*m   (4-bit sc, m per 16)
+ *   Q8_0   32 weights /  34 B   w = d*q
+ * d and dmin are IEEE fp16 (subnormals honoured).  A weight matrix W of N rows
+ * and K columns is N consecutive rows of K/QK blocks each (K fastest).  MoE
+ * expert tensors are E such matrices back to back.
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises.  Outputs are overwritten, never
+ *    accumulated.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Every call is asynchronous on that stream.
+ *  - Argument errors are returned synchronously as a negative kq_status before
+ *    any HIP call is made.  A failed launch returns KQ_ERR_LAUNCH.  Faults in
+ *    a kernel surface at the caller's next synchronisation.
+ *  - The library holds no state; calls are reentrant and thread-safe.
+ *  - Alignment: W, W_exps and src 16 B; x, y, dst, workspace 16 B; ids,
+ *    route_w, err_flag 4 B.  Rows of Q6_K and Q8_0 matrices may start at any
+ *    even byte offset (e.g. 630-byte rows); that is handled inside.
+ */
+#ifndef KQGEMV_H
+#define KQGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids of the supported block formats. */
+typedef enum kq_type {
+    KQ_TYPE_Q8_0 = 8,
+    KQ_TYPE_Q2_K = 10,
+    KQ_TYPE_Q4_K = 12,
+    KQ_TYPE_Q6_K = 14
+} kq_type;
+
+typedef enum kq_status {
+    KQ_OK = 0,
+    KQ_ERR_TYPE = -1,     /* unknown or unsupported quant type              */
+    KQ_ERR_SHAPE = -2,    /* K not a positive multiple of the block size,
+                             N < 0, or a size beyond the documented limits   */
+    KQ_ERR_M = -3,        /* M (or T) outside 1..8                          */
+    KQ_ERR_NULL = -4,     /* a required pointer is NULL                     */
+    KQ_ERR_ALIGN = -5,    /* a pointer violates its alignment requirement   */
+    KQ_ERR_ARG = -6,      /* any other invalid argument (x_mode, k, E)      */
+    KQ_ERR_LAUNCH = -7,   /* the HIP launch itself failed                   */
+    KQ_ERR_DEVICE = -8    /* no usable gfx950 device                        */
+} kq_status;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int kq_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kq_status_string(int status);
+
+/* Weights per block and bytes per block of `type`.  Returns KQ_OK or
+ * KQ_ERR_TYPE / KQ_ERR_NULL.  Host-only, no HIP call. */
+int kq_block_info(int type, int *block_elems, int *block_bytes);
+
+/* Bytes of one row of K weights of `type`, or a negative kq_status when K is
+ * not a positive multiple of the block size.  Host-only, no HIP call. */
+int64_t kq_row_bytes(int type, int64_t K);
+
+/* Standalone dequantization: dst[i] = fp32 weight i of the packed blocks at
+ * src, for i in [0, n_elems).  n_elems must be a multiple of the block size
+ * (0 is allowed and launches nothing).  Every value is the correctly rounded
+ * fp32 of the exact weight (the products are exact, one rounding at the final
+ * subtraction); an exact zero is written as +0.  src: n_elems/QK blocks. */
+int kq_dequant(int type, const void *src, int64_t n_elems, float *dst, void *stream);
+
+/* Fused dequant-GEMV: y[m][o] = sum_i w[o][i] * x[m][i] for m < M, o < N.
+ *   W  N x K matrix of `type` blocks (row-major, K fastest), 16-B aligned.
+ *   x  M rows of K fp32, contiguous (row stride K).
+ *   y  M rows of N fp32, contiguous (row stride N), overwritten.
+ * 1 <= M <= 8; K a positive multiple of the block size, K <= 2^20;
+ * 0 <= N < 2^31 (N == 0 launches nothing).  The weights are expanded only in
+ * registers.  Accumulation is fp32; for every output the error against the
+ * exact sum is far below 1e-4 * sum_i |w*x| + 1e-6.  Row m of the result does
+ * not depend on M or on the other rows of x (bit-identical to an M = 1 call on
+ * that row), and reruns are bit-identical (no atomics). */
+int kq_qgemv(int type, const void *W, int64_t N, int64_t K,
+             const float *x, int M, float *y, void *stream);
+
+/* Workspace bytes kq_qmoe_gemv needs for T tokens, k slots and N rows when a
+ * routing-weighted combine is requested (T*k*N*4); 0 on invalid sizes. */
+size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N);
+
+/* Routed-expert GEMV over a stacked expert tensor.
+ *   W_exps  E matrices of N x K `type` blocks, expert-major, 16-B aligned.
+ *   ids     [T][k] int32 expert ids (device memory; never read by the host).
+ *   x       x_mode 0: [T][K] fp32, one activation row per token, shared by
+ *           its k slots (gate/up projections); x_mode 1: [T][k][K], one row
+ *           per slot (down projection).
+ *   route_w NULL: y is [T][k][N], y[t][j] = W_exps[ids[t][j]] . x_(t,j).
+ *           non-NULL: [T][k] fp32 routing weights, y is [T][N],
+ *           y[t] = sum_j route_w[t][j] * W_exps[ids[t][j]] . x_(t,j), summed
+ *           in ascending j; `workspace` must then hold
+ *           kq_qmoe_workspace_bytes(T, k, N) bytes (its contents are scratch).
+ *   err_flag NULL or a device int32 the kernel sets to 1 (plain store) when
+ *           an id is outside [0, E); such a slot contributes zero.  It is
+ *           never cleared by the library.
+ * 1 <= T <= 8, 1 <= k <= 16, k <= E.  Slots that route to the same expert are
+ * served by one pass over that expert's weights (up to 8 slots per pass).
+ * Results per slot are bit-identical to kq_qgemv with M = 1 on the expert's
+ * matrix and that slot's activation row. */
+int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,
+                 const int32_t *ids, const float *route_w, int T, int k,
+                 const float *x, int x_mode, float *y, float *workspace,
+                 int32_t *err_flag, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQGEMV_H */

@@ -1,0 +1,120 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and every synchronous argument error is reported before any
+HIP call (no GPU is touched here: each call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_gemv_gguf_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kqgemv.h")
+
+Q4, Q6, Q2, Q8 = kq.KQ_TYPE_Q4_K, kq.KQ_TYPE_Q6_K, kq.KQ_TYPE_Q2_K, kq.KQ_TYPE_Q8_0
+FAKE = 0x10000          # a 16-B aligned non-NULL address that is never dereferenced
+ODD = 0x10002           # 2-B aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
+                            "kq_dequant", "kq_qgemv", "kq_qmoe_workspace_bytes", "kq_qmoe_gemv"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(kq.lib_path)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert hasattr(kq, name), name          # binding keeps the C names
+
+
+def test_version_and_status_strings():
+    assert kq.kq_version() >= 10000
+    for code in kq.STATUS:
+        s = kq.kq_status_string(code)
+        assert isinstance(s, str) and s
+    assert kq.kq_status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("qtype,qk,nb", [(Q4, 256, 144), (Q6, 256, 210), (Q2, 256, 84), (Q8, 32, 34)])
+def test_block_info_and_row_bytes(qtype, qk, nb):
+    assert kq.kq_block_info(qtype) == (qk, nb)
+    assert kq.kq_row_bytes(qtype, 8 * qk) == 8 * nb
+    with pytest.raises(kq.KQError):
+        kq.kq_row_bytes(qtype, qk + 1)
+    with pytest.raises(kq.KQError):
+        kq.kq_row_bytes(qtype, 0)
+
+
+def test_unknown_type():
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_block_info(3)
+    assert e.value.status == -1
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except kq.KQError as e:
+        return e.status
+    return 0
+
+
+def test_qgemv_argument_errors():
+    g = kq.kq_qgemv
+    assert _status(g, 99, FAKE, 4, 256, FAKE, 1, FAKE) == -1            # type
+    assert _status(g, Q4, FAKE, 4, 100, FAKE, 1, FAKE) == -2            # K not a multiple
+    assert _status(g, Q4, FAKE, 4, 0, FAKE, 1, FAKE) == -2
+    assert _status(g, Q4, FAKE, -1, 256, FAKE, 1, FAKE) == -2           # N < 0
+    assert _status(g, Q4, FAKE, 4, 1 << 21, FAKE, 1, FAKE) == -2        # K too large
+    assert _status(g, Q4, FAKE, 4, 256, FAKE, 0, FAKE) == -3            # M
+    assert _status(g, Q4, FAKE, 4, 256, FAKE, 9, FAKE) == -3
+    assert _status(g, Q4, None, 4, 256, FAKE, 1, FAKE) == -4            # NULL
+    assert _status(g, Q4, FAKE, 4, 256, None, 1, FAKE) == -4
+    assert _status(g, Q4, FAKE, 4, 256, FAKE, 1, None) == -4
+    assert _status(g, Q4, ODD, 4, 256, FAKE, 1, FAKE) == -5             # alignment
+    assert _status(g, Q4, FAKE, 4, 256, ODD, 1, FAKE) == -5
+    assert _status(g, Q4, FAKE, 4, 256, FAKE, 1, ODD) == -5
+    assert _status(g, Q4, None, 0, 256, None, 1, None) == 0             # N == 0: nothing to do
+
+
+def test_dequant_argument_errors():
+    d = kq.kq_dequant
+    assert _status(d, 99, FAKE, 256, FAKE) == -1
+    assert _status(d, Q4, FAKE, 100, FAKE) == -2
+    assert _status(d, Q8, FAKE, -32, FAKE) == -2
+    assert _status(d, Q4, None, 256, FAKE) == -4
+    assert _status(d, Q4, FAKE, 256, None) == -4
+    assert _status(d, Q4, ODD, 256, FAKE) == -5
+    assert _status(d, Q6, FAKE, 256, ODD) == -5
+    assert _status(d, Q6, None, 0, None) == 0
+
+
+def test_qmoe_argument_errors():
+    def m(qtype=Q4, W=FAKE, E=8, N=16, K=256, ids=FAKE, rw=None, T=1, k=2, x=FAKE, xm=0, y=FAKE, ws=None, flag=None):
+        return _status(kq.kq_qmoe_gemv, qtype, W, E, N, K, ids, rw, T, k, x, xm, y, ws, flag)
+    assert m(qtype=5) == -1
+    assert m(K=300) == -2
+    assert m(N=-3) == -2
+    assert m(T=0) == -3 and m(T=9) == -3
+    assert m(k=0) == -6 and m(k=17) == -6 and m(E=1, k=2) == -6 and m(E=0) == -6
+    assert m(xm=2) == -6
+    assert m(W=None) == -4 and m(ids=None) == -4 and m(x=None) == -4 and m(y=None) == -4
+    assert m(rw=FAKE, ws=None) == -4                                     # combine needs a workspace
+    assert m(W=ODD) == -5 and m(ids=FAKE + 2) == -5 and m(y=ODD) == -5
+    assert m(rw=FAKE, ws=ODD) == -5 and m(flag=FAKE + 1) == -5
+    assert m(N=0, W=None, ids=None, x=None, y=None) == 0
+
+
+def test_workspace_bytes():
+    assert kq.kq_qmoe_workspace_bytes(8, 8, 2048) == 8 * 8 * 2048 * 4
+    assert kq.kq_qmoe_workspace_bytes(0, 8, 2048) == 0
+    assert kq.kq_qmoe_workspace_bytes(8, 17, 2048) == 0

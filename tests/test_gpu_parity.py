@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.  Dequantized values must be bit-exact; GEMV outputs must
+satisfy |y_gpu - y_oracle| <= 1e-4 * sum|w*x| + 1e-6 element by element.
+Shapes span several work-group tiles, ragged row and unit tails, several K
+chunks, 2-byte-aligned rows (Q6_K with K = 768, Q8_0 with an odd block count)
+and the degenerate cases (one block, one row, N = 0)."""
+import sys
+
+import numpy as np
+import pytest
+
+import kqsynth
+import oracle
+
+torch = pytest.importorskip("torch")
+import dequant_gemv_gguf_amd as kq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [kqsynth.Q4_K, kqsynth.Q6_K, kqsynth.Q2_K, kqsynth.Q8_0]
+TOL_REL, TOL_ABS = 1e-4, 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def qmat(qtype, N, K, seed):
+    return kqsynth.matrix(qtype, N, K, kqsynth.rng_for(seed, qtype, N, K))
+
+
+def gpu_gemv(qtype, W, N, K, x):
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    kq.kq_qgemv(qtype, dev(W) if isinstance(W, np.ndarray) else W, N, K, dev(x), M, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check_close(y, yo, S, what=""):
+    err = np.abs(y.astype(np.float64) - yo)
+    bound = TOL_REL * S + TOL_ABS
+    worst = float((err / bound).max()) if err.size else 0.0
+    assert np.all(err <= bound), "%s: worst |dy|/bound = %.3g" % (what, worst)
+    return worst
+
+
+# ---- dequant: bit-exact -------------------------------------------------------
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("nblocks", [1, 3, 257, 1000])
+def test_dequant_bit_exact(qtype, nblocks):
+    say("dequant", kqsynth.TYPE_NAMES[qtype], nblocks)
+    rng = kqsynth.rng_for(11, qtype, nblocks)
+    blk = kqsynth.blocks(qtype, nblocks, rng)
+    # plant fp16 subnormal and negative scales in a third of the blocks
+    qk, nb, d_off, dmin_off = kqsynth.BLOCK[qtype]
+    sub = rng.integers(1, 1024, size=nblocks).astype(np.uint16)
+    sub[::2] |= 0x8000
+    pick = np.arange(nblocks) % 3 == 0
+    blk[pick, d_off:d_off + 2] = sub[pick].view(np.uint8).reshape(-1, 2)
+    n = nblocks * qk
+    ref = oracle.dequant(qtype, blk, n)
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    kq.kq_dequant(qtype, dev(blk), n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ---- qgemv: tolerance, over shapes and M ----------------------------------------
+
+SHAPES = {
+    kqsynth.Q4_K: [(1, 256), (7, 1280), (37, 4096), (130, 12544), (300, 2048)],
+    kqsynth.Q6_K: [(1, 256), (9, 768), (37, 4096), (130, 12544), (70, 1280)],
+    kqsynth.Q2_K: [(1, 256), (7, 1280), (37, 4096), (130, 12544), (300, 2048)],
+    kqsynth.Q8_0: [(1, 32), (9, 1184), (37, 4096), (130, 12544), (70, 96)],
+}
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_qgemv_matches_oracle(qtype, M):
+    worst = 0.0
+    for (N, K) in SHAPES[qtype]:
+        say("qgemv", kqsynth.TYPE_NAMES[qtype], "M", M, "N", N, "K", K)
+        W = qmat(qtype, N, K, 1)
+        x = kqsynth.activations(M, K, kqsynth.rng_for(2, M, K))
+        y = gpu_gemv(qtype, W, N, K, x)
+        yo, S = oracle.gemv(qtype, W, N, K, x)
+        worst = max(worst, check_close(y, yo, S, "%s N=%d K=%d M=%d" % (kqsynth.TYPE_NAMES[qtype], N, K, M)))
+    say("  worst |dy|/bound", worst)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+def test_qgemv_one_hot_is_bit_exact(qtype):
+    # one nonzero product per output: every partial is exact, so y is the
+    # dequantized column itself
+    N, K = 45, 4096 + 256
+    W = qmat(qtype, N, K, 3)
+    dense = oracle.dequant(qtype, W, N * K).reshape(N, K)
+    cols = [0, 1, 17, 63, 64, 255, 4100, K - 1]
+    x = np.zeros((8, K), dtype=np.float32)
+    for r, c in enumerate(cols):
+        x[r, c] = 1.0
+    y = gpu_gemv(qtype, W, N, K, x)
+    for r, c in enumerate(cols):
+        assert np.array_equal(y[r], dense[:, c]), (r, c)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+def test_qgemv_rows_do_not_depend_on_M_and_reruns_are_identical(qtype):
+    N, K = 96, 12544
+    W = dev(qmat(qtype, N, K, 4))
+    x = kqsynth.activations(8, K, kqsynth.rng_for(4, 8))
+    y8 = gpu_gemv(qtype, W, N, K, x)
+    for m in range(8):
+        y1 = gpu_gemv(qtype, W, N, K, x[m:m + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), m
+    for M in (3, 5):
+        yM = gpu_gemv(qtype, W, N, K, x[:M])
+        assert np.array_equal(yM.view(np.uint32), y8[:M].view(np.uint32))
+    again = gpu_gemv(qtype, W, N, K, x)
+    assert np.array_equal(again.view(np.uint32), y8.view(np.uint32))
+
+
+def test_qgemv_degenerate_sizes():
+    K = 256
+    W = qmat(kqsynth.Q4_K, 1, K, 5)
+    x = kqsynth.activations(1, K, kqsynth.rng_for(5))
+    y = gpu_gemv(kqsynth.Q4_K, W, 1, K, x)
+    yo, S = oracle.gemv(kqsynth.Q4_K, W, 1, K, x)
+    check_close(y, yo, S)
+    # N = 0 launches nothing and leaves y untouched
+    yt = torch.full((1, 4), 7.0, device="cuda")
+    kq.kq_qgemv(kqsynth.Q4_K, dev(W), 0, K, dev(x), 1, yt)
+    torch.cuda.synchronize()
+    assert torch.all(yt == 7.0)
+
+
+def test_qgemv_zero_weights_and_large_activations():
+    # zero scales give exact zeros whatever x holds; huge x stays finite
+    K, N = 2048, 20
+    W = qmat(kqsynth.Q4_K, N, K, 6).reshape(N, -1, 144).copy()
+    W[:, :, 0:4] = 0                       # d = dmin = 0
+    W = W.reshape(N, -1)
+    x = (kqsynth.activations(2, K, kqsynth.rng_for(6)) * 1e30).astype(np.float32)
+    y = gpu_gemv(kqsynth.Q4_K, W, N, K, x)
+    assert np.all(y == 0)
+
+
+# ---- full-size shapes, sampled rows -----------------------------------------------
+
+FULL = [
+    ("70B w1", kqsynth.Q4_K, 28672, 8192),
+    ("70B w2", kqsynth.Q6_K, 8192, 28672),
+    ("70B wk", kqsynth.Q4_K, 1024, 8192),
+    ("70B w1 Q2_K", kqsynth.Q2_K, 28672, 8192),
+    ("70B w2 Q8_0", kqsynth.Q8_0, 8192, 28672),
+]
+
+
+@pytest.mark.parametrize("name,qtype,N,K", FULL)
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_size_sampled_rows(name, qtype, N, K, M):
+    say("full", name, "M", M)
+    W = kqsynth.device_matrix(qtype, N, K, seed=1234 + qtype, device="cuda")
+    x = kqsynth.activations(M, K, kqsynth.rng_for(7, M, K))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    kq.kq_qgemv(qtype, W, N, K, dev(x), M, y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, N - 1, N - 2], np.random.default_rng(N + K).integers(0, N, 60)]))
+    Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
+    worst = check_close(y.cpu().numpy()[:, rows], yo, S, name)
+    say("  worst |dy|/bound", worst)
+    del W
+
+
+# ---- routed experts ---------------------------------------------------------------
+
+def moe_inputs(qtype, E, N, K, T, k, seed, x_mode):
+    rng = kqsynth.rng_for(seed, qtype, E, N, K)
+    W = kqsynth.blocks(qtype, E * N * (K // kqsynth.BLOCK[qtype][0]), rng)
+    ids, p = kqsynth.routing(T, k, E, kqsynth.rng_for(seed, 1))
+    x = kqsynth.activations(T * (k if x_mode else 1), K, kqsynth.rng_for(seed, 2))
+    return W, ids, p, x
+
+
+def gpu_moe(qtype, W, E, N, K, ids, p, x, x_mode):
+    T, k = ids.shape
+    shape = (T, k, N) if p is None else (T, N)
+    y = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    ws = None if p is None else torch.empty(kq.kq_qmoe_workspace_bytes(T, k, N) // 4, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kq.kq_qmoe_gemv(qtype, W if not isinstance(W, np.ndarray) else dev(W), E, N, K, dev(ids),
+                    None if p is None else dev(p), T, k, dev(x), x_mode, y, ws, flag)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), int(flag.item())
+
+
+MOE_CASES = [
+    # (qtype, E, N, K, T, k, x_mode): the MoE FFN shapes (gate/up Q4_K 768x2048,
+    # down Q6_K 2048x768 with 630-byte rows) and smaller ragged ones
+    (kqsynth.Q4_K, 128, 768, 2048, 1, 8, 0),
+    (kqsynth.Q4_K, 128, 768, 2048, 8, 8, 0),
+    (kqsynth.Q6_K, 128, 2048, 768, 1, 8, 1),
+    (kqsynth.Q6_K, 128, 2048, 768, 8, 8, 1),
+    (kqsynth.Q2_K, 16, 100, 512, 5, 4, 0),
+    (kqsynth.Q8_0, 12, 70, 96, 3, 5, 1),
+]
+
+
+@pytest.mark.parametrize("case", MOE_CASES)
+@pytest.mark.parametrize("combine", [False, True])
+def test_qmoe_matches_oracle(case, combine):
+    qtype, E, N, K, T, k, x_mode = case
+    say("qmoe", kqsynth.TYPE_NAMES[qtype], E, N, K, T, k, x_mode, combine)
+    W, ids, p, x = moe_inputs(qtype, E, N, K, T, k, 8, x_mode)
+    pw = p if combine else None
+    y, flag = gpu_moe(qtype, W, E, N, K, ids, pw, x, x_mode)
+    yo, S, oflag = oracle.moe(qtype, W, E, N, K, ids, pw, x, x_mode)
+    assert flag == 0 and oflag == 0
+    check_close(y, yo, S, "qmoe")
+
+
+def test_qmoe_single_slot_equals_qgemv_bits():
+    qtype, E, N, K = kqsynth.Q4_K, 16, 768, 2048
+    W, _, _, x = moe_inputs(qtype, E, N, K, 1, 1, 9, 0)
+    Wd = dev(W.reshape(-1))
+    per = N * kqsynth.row_bytes(qtype, K)
+    for e in (0, 7, 15):
+        y, _ = gpu_moe(qtype, Wd, E, N, K, np.array([[e]], np.int32), np.ones((1, 1), np.float32), x, 0)
+        yg = gpu_gemv(qtype, Wd[e * per:(e + 1) * per], N, K, x)
+        assert np.array_equal(y.view(np.uint32), yg.view(np.uint32))
+
+
+def test_qmoe_shared_expert_groups_and_bad_ids():
+    # every slot routes to one expert: a group of T*k = 40 slots served in
+    # batches of up to 8 rows; then out-of-range ids give zeros and the flag
+    qtype, E, N, K, T, k = kqsynth.Q6_K, 9, 64, 768, 5, 8
+    W, _, p, x = moe_inputs(qtype, E, N, K, T, k, 10, 1)
+    ids = np.full((T, k), 3, dtype=np.int32)
+    y, flag = gpu_moe(qtype, W, E, N, K, ids, None, x, 1)
+    yo, S, _ = oracle.moe(qtype, W, E, N, K, ids, None, x, 1)
+    assert flag == 0
+    check_close(y, yo, S, "shared expert")
+    ids[1, 2] = E
+    ids[4, 7] = -5
+    y, flag = gpu_moe(qtype, W, E, N, K, ids, None, x, 1)
+    yo, S, oflag = oracle.moe(qtype, W, E, N, K, ids, None, x, 1)
+    assert flag == 1 and oflag == 1
+    assert np.all(y[1, 2] == 0) and np.all(y[4, 7] == 0)
+    check_close(y, yo, S, "bad ids")
+    yc, flag = gpu_moe(qtype, W, E, N, K, ids, p, x, 1)
+    yoc, Sc, _ = oracle.moe(qtype, W, E, N, K, ids, p, x, 1)
+    check_close(yc, yoc, Sc, "bad ids combined")
+
+
+def test_qmoe_slot_rows_do_not_depend_on_grouping():
+    # a slot's output is bit-identical whether its expert is shared or not
+    qtype, E, N, K, T, k = kqsynth.Q4_K, 32, 256, 2048, 8, 4
+    W, ids, _, x = moe_inputs(qtype, E, N, K, T, k, 11, 0)
+    Wd = dev(W.reshape(-1))
+    ids[:, 0] = 5                        # expert 5 shared by all 8 tokens
+    y, _ = gpu_moe(qtype, Wd, E, N, K, ids, None, x, 0)
+    per = N * kqsynth.row_bytes(qtype, K)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            yg = gpu_gemv(qtype, Wd[e * per:(e + 1) * per], N, K, x[t:t + 1])
+            assert np.array_equal(y[t, j].view(np.uint32), yg[0].view(np.uint32)), (t, j)
