@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Throughput of the fused K-quant dequant-GEMV on one MI355X.
+
+Default workload: one decode step of a Llama-3-70B-shaped model at batch 1 --
+80 distinct layers, each wq/wo 8192x8192, wk 1024x8192, w1/w3 28672x8192 in
+Q4_K and wv 1024x8192, w2 8192x28672 in Q6_K (the Q4_K_M mix), all resident
+in HBM (43.5 GB of packed weights).  One step = one qgemv over every one of
+the 560 matrices.  The metric is packed-weight bytes moved per second
+(algorithmic bytes: every weight byte read once), reported in GB/s, as a
+fraction of the 8 TB/s HBM3E peak and as equivalent tokens/s.
+
+Other workloads (--workload) measure the remaining shapes the same way:
+  8b      Llama-3-8B-shaped layers x32
+  single  one Q4_K 4096x4096 matrix, rotated over 1 GB of copies
+  verify  70B shapes, M activation rows (--m), all-Q4_K_M / all-Q2_K / all-Q8_0
+  moe     Qwen3-30B-A3B-shaped MoE FFN x48, T tokens (--m) routed top-8
+
+Inputs are seeded synthetic data drawn directly in device memory.  Only one
+GPU is supported: the path has no collectives.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved weight GB/s (% of 8 TB/s HBM) + equiv tok/s, 70B-layer Q4_K_M GEMV M=1"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_gguf_amd", "csrc", "kqgemv.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe"])
+    ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
+    ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the model's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on exactly one GPU (no collectives, no sharding); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import kqsynth
+    import dequant_gemv_gguf_amd as kq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- build the workload: a list of launches, each a closure + its bytes
+    launches = []          # (fn, weight_bytes, is_dominant)
+    host_sample = []       # (qtype, N, K, device tensor) used for the CPU oracle sample
+    M = 1
+    if args.workload in ("70b", "8b", "verify"):
+        spec = kqsynth.LLAMA3_70B if args.workload != "8b" else kqsynth.LLAMA3_8B
+        layers = args.layers or spec["layers"]
+        layer = kqsynth.dense_layer(spec["hidden"], spec["ffn"], spec["kv"])
+        if args.workload == "verify":
+            M = args.m
+            if args.quant == "q2_k":
+                layer = kqsynth.reencode(layer, kqsynth.Q2_K)
+            elif args.quant == "q8_0":
+                layer = kqsynth.reencode(layer, kqsynth.Q8_0)
+        xs = {K: torch.randn(M, K, device=dev, generator=torch.Generator(device=dev).manual_seed(K))
+              for K in {K for (_, _, _, K) in layer}}
+        ys = {(N, M): torch.empty(M, N, device=dev) for (_, _, N, _) in layer}
+        weights = []
+        for L in range(layers):
+            if L % 20 == 0:
+                log("generating layer %d of %d" % (L, layers))
+            for ti, (name, qt, N, K) in enumerate(layer):
+                W = kqsynth.device_matrix(qt, N, K, seed=1000 * L + ti, device=dev)
+                weights.append(W)
+                nbytes = N * kq.kq_row_bytes(qt, K)
+                dominant = (qt == kqsynth.Q4_K and N >= 8192)
+                x, y = xs[K], ys[(N, M)]
+                launches.append(((lambda qt=qt, W=W, N=N, K=K, x=x, y=y:
+                                  kq.kq_qgemv(qt, W, N, K, x, M, y, stream)), nbytes, dominant))
+                if L == 0:
+                    host_sample.append((qt, N, K, W))
+        workload = {"70b": "llama3-70b decode layer x%d, Q4_K_M mix, M=1" % layers,
+                    "8b": "llama3-8b decode layer x%d, Q4_K_M mix, M=1" % layers,
+                    "verify": "llama3-70b layer shapes x%d, %s, M=%d" % (layers, args.quant, M)}[args.workload]
+        config = {"workload": workload, "layers": layers, "hidden": spec["hidden"], "ffn": spec["ffn"],
+                  "kv_dim": spec["kv"], "M": M, "matrices_per_step": len(launches)}
+    elif args.workload == "single":
+        N = K = 4096
+        qt = kqsynth.Q4_K
+        nbytes = N * kq.kq_row_bytes(qt, K)
+        copies = max(1, (1 << 30) // nbytes + 1)          # > MALL: rotate over >= 1 GB
+        x = torch.randn(1, K, device=dev)
+        y = torch.empty(1, N, device=dev)
+        weights = [kqsynth.device_matrix(qt, N, K, seed=c, device=dev) for c in range(copies)]
+        for W in weights:
+            launches.append(((lambda W=W: kq.kq_qgemv(qt, W, N, K, x, 1, y, stream)), nbytes, True))
+        host_sample.append((qt, N, K, weights[0]))
+        workload = "single Q4_K 4096x4096 M=1, rotated over %d copies" % copies
+        config = {"workload": workload, "N": N, "K": K, "M": 1, "copies": copies}
+    else:  # moe
+        spec = kqsynth.QWEN3_30B_A3B_MOE
+        layers = args.layers or spec["layers"]
+        T, k, E, H, F = args.m, spec["top_k"], spec["experts"], spec["hidden"], spec["ffn"]
+        M = T
+        g = torch.Generator(device=dev).manual_seed(7)
+        x = torch.randn(T, H, device=dev, generator=g)
+        h = torch.randn(T * k, F, device=dev, generator=g)
+        yg = torch.empty(T, k, F, device=dev)
+        yd = torch.empty(T, H, device=dev)
+        ws = torch.empty(kq.kq_qmoe_workspace_bytes(T, k, H) // 4, device=dev)
+        weights = []
+        for L in range(layers):
+            rng = kqsynth.rng_for(0, 5, L)
+            ids_np, p_np = kqsynth.routing(T, k, E, rng)
+            ids = torch.from_numpy(ids_np).to(dev)
+            p = torch.from_numpy(p_np).to(dev)
+            distinct = len(set(ids_np.reshape(-1).tolist()))
+            for (name, qt, EE, N, K) in kqsynth.moe_layer(H, E, F):
+                W = kqsynth.device_matrix(qt, EE * N, K, seed=100 * L + len(weights), device=dev)
+                weights.append(W)
+                per_expert = N * kq.kq_row_bytes(qt, K)
+                if name == "down":
+                    fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids, p=p:
+                          kq.kq_qmoe_gemv(qt, W, E, N, K, ids, p, T, k, h, 1, yd, ws, None, stream))
+                else:
+                    fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids:
+                          kq.kq_qmoe_gemv(qt, W, E, N, K, ids, None, T, k, x, 0, yg, None, None, stream))
+                launches.append((fn, distinct * per_expert, name != "down"))
+        workload = "qwen3-30b-a3b MoE FFN x%d, top-%d of %d experts, T=%d" % (layers, k, E, T)
+        config = {"workload": workload, "layers": layers, "experts": E, "top_k": k, "hidden": H,
+                  "expert_ffn": F, "tokens": T}
+    torch.cuda.synchronize()
+    step_bytes = sum(b for (_, b, _) in launches)
+
+    def run_step(ev=None):
+        for (fn, _, dom) in launches:
+            if ev is not None and dom:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev.append((a, b))
+            else:
+                fn()
+
+    log("inputs resident: %.2f GB of packed weights per step, %d launches" % (step_bytes / 1e9, len(launches)))
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # ---- timed region: exactly `steps` steps, events around the dominant kernel
+    pairs = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(pairs)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+    gbs = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
+
+    dom_ms = [a.elapsed_time(b) for (a, b) in pairs]
+    dom_bytes_per_launch = (sum(b for (_, b, d) in launches if d) / max(1, sum(1 for (_, _, d) in launches if d)))
+    dom_avg_us = 1e3 * sum(dom_ms) / max(1, len(dom_ms))
+    dom_gbs = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9 if dom_ms else None
+
+    traffic = None
+    tfile = os.path.join(PROFILES, "traffic_%s.json" % args.workload)
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha256_16") == source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC if args.workload == "70b" else "achieved weight GB/s (%s)" % args.workload,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, drawn in device memory)",
+        "config": config,
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tok_per_s_equiv": round(1e3 / ms_per_step, 2),
+        "weight_bytes_per_step": step_bytes,
+        "wall_s_timed": round(wall1 - wall0, 3),
+        "roofline": {
+            "kernel": "qgemv Q4_K M=1 (N >= 8192 matrices)" if args.workload in ("70b", "8b") else "dominant launches",
+            "bound": "hbm",
+            "achieved": round(dom_gbs, 1) if dom_gbs else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4) if dom_gbs else None,
+            "traffic": traffic,
+            "avg_launch_us": round(dom_avg_us, 3),
+            "algorithmic_bytes_per_launch": int(dom_bytes_per_launch),
+            "launches_timed": len(dom_ms),
+        },
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample, host cores
+    log("timed %d steps: %.3f ms/step, %.1f GB/s" % (args.steps, ms_per_step, gbs))
+    if not args.no_cpu_baseline and host_sample:
+        log("timing the CPU oracle on a bounded sample")
+        import oracle
+        threads = oracle.set_threads(0)
+        done_bytes, t_cpu, used = 0, 0.0, []
+        for (qt, N, K, W) in host_sample:
+            rows = N
+            rb = kq.kq_row_bytes(qt, K)
+            # bound the sample: at most ~1/4 of the remaining budget per matrix
+            Wh = W.view(N, rb)[:rows].cpu().numpy()
+            xh = np.random.default_rng(0).standard_normal((M, K)).astype(np.float32)
+            s = time.perf_counter()
+            oracle.gemv(qt, Wh, rows, K, xh)
+            dt = time.perf_counter() - s
+            done_bytes += rows * rb
+            t_cpu += dt
+            used.append("%s %dx%d" % (kqsynth.TYPE_NAMES[qt], rows, K))
+            if t_cpu > args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {
+            "value": round(done_bytes / t_cpu / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "layer-0 matrices %s at M=%d (%.1f s of CPU time, %.2f GB)" % (
+                ", ".join(used), M, t_cpu, done_bytes / 1e9),
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

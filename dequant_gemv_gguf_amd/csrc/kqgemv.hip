@@ -57,10 +57,10 @@ constexpr u32 OOB = 0x80000000u;  // an offset past every tile: loads return 0
 enum { T_Q8_0 = KQ_TYPE_Q8_0, T_Q2_K = KQ_TYPE_Q2_K, T_Q4_K = KQ_TYPE_Q4_K, T_Q6_K = KQ_TYPE_Q6_K };
 
 template <int T> struct Fmt;
-template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BYTES = 144, UPB = 4, KM = 1; };
-template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BYTES = 210, UPB = 4, KM = 32; };
-template <> struct Fmt<T_Q2_K> { static constexpr int QK = 256, BYTES = 84, UPB = 4, KM = 1; };
-template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BYTES = 34, UPB = 1, KM = 128; };
+template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BYTES = 144, UPB = 4; };
+template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BYTES = 210, UPB = 4; };
+template <> struct Fmt<T_Q2_K> { static constexpr int QK = 256, BYTES = 84, UPB = 4; };
+template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BYTES = 34, UPB = 1; };
 
 // ---------------------------------------------------------------------------
 // Small device helpers
@@ -109,33 +109,88 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
     v = dpp_add(v, 1);
     v = dpp_add(v, 2);
     v = dpp_add(v, 3);
-    if (lpr >= 32) v += __shfl_xor(v, 16);
-    if (lpr >= 64) v += __shfl_xor(v, 32);
+    if (lpr >= 32) {   // rows of 16 lanes pairwise: lane l gets v[l] + v[l ^ 16]
+        const u32 b = __builtin_bit_cast(u32, v);
+        const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        v = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+    }
+    if (lpr >= 64) {   // halves of 32 lanes: lane l gets v[l] + v[l ^ 32]
+        const u32 b = __builtin_bit_cast(u32, v);
+        const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        v = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+    }
     return v;
 }
 
 // ---------------------------------------------------------------------------
-// Per-format unit loaders and multiply-accumulate.
-//
-// A unit's raw registers are loaded for R rows at once; `xo` is the LDS
-// offset of the unit's first activation in row 0 of the staged chunk, `so`
-// the offset of its first 16-sum; rows of x are XS floats apart and rows of
-// sums SS floats apart.
+// Activation access.  A unit's activations are addressed by their offset from
+// the unit's first weight in the unit's own coordinates (Q4_K: 0..63, one
+// contiguous run; Q6_K and Q2_K: four runs of 16 at offsets 0, 32, 64, 96;
+// Q8_0: 0..31) and its sums of 16 activations by run index.  The two accessors
+// below return bit-identical values: the sums are formed by the same
+// expression (sum16) whether they are staged in LDS or kept in registers.
+
+__device__ __forceinline__ float sum16(f4 a, f4 b, f4 c, f4 d) {
+    return (((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w))) +
+           (((c.x + c.y) + (c.z + c.w)) + ((d.x + d.y) + (d.z + d.w)));
+}
+
+// Activations of a staged K chunk in LDS: row m at xs + m * XS (16 B of padding
+// every 64 floats, see xpad), 16-sums at ss + m * SS.  xo / so locate the unit.
+struct XLds {
+    const float *xs, *ss;
+    int XS, SS, xo, so, srun;
+    __device__ __forceinline__ f4 x4(int m, int off) const { return lds4(xs + m * XS + xo + xpad(off)); }
+    __device__ __forceinline__ float sum(int m, int run) const { return ss[m * SS + so + srun * run]; }
+};
+
+// One activation row of one unit held in registers (M = 1 kernels).
+template <int T> struct XReg {
+    static constexpr bool RUNS32 = (T == T_Q6_K || T == T_Q2_K);
+    static constexpr int NV = (T == T_Q8_0) ? 8 : 16, NS = NV / 4;
+    f4 v[NV];
+    float s[NS];
+    __device__ __forceinline__ f4 x4(int, int off) const {
+        return v[RUNS32 ? ((off >> 5) << 2) + ((off & 31) >> 2) : (off >> 2)];
+    }
+    __device__ __forceinline__ float sum(int, int run) const { return s[run]; }
+    // element offset of the unit's first activation and of run r
+    __device__ __forceinline__ void load(const float *x, int e0) {
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+            const f4 *p = reinterpret_cast<const f4 *>(x + e0 + (RUNS32 ? 32 : 16) * r);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * r + k] = p[k];
+        }
+#pragma unroll
+        for (int r = 0; r < NS; ++r) s[r] = sum16(v[4 * r], v[4 * r + 1], v[4 * r + 2], v[4 * r + 3]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Per-format units.  load_* reads one unit's raw bytes for one row at byte
+// offset `off` of a buffer; val_* turns R rows of raw units and M activation
+// rows into the unit's contribution v[r][m] to each output, always by the same
+// sequence of fp32 operations (so every kernel built on them rounds alike):
+//   aq = sum over sub-blocks of (scale * sum_i q_i x_i)     (units of 2^-24)
+//   am = sum over sub-blocks of (min   * sum_i x_i)
+//   v  = aq * 2^24 - KM * am
+// where KM folds a constant quant offset (Q6_K: 32; Q8_0: 128, from reading
+// the int8 quants as q + 128).
 
 // ---- Q4_K: unit (block b, group g) = quant bytes 32g..32g+31, i.e. weights
 // 64g..64g+31 (low nibbles, sub-block 2g) and 64g+32..64g+63 (high nibbles,
 // sub-block 2g+1); plus the 16-byte header.
 struct RawQ4K { u4 h, qa, qb; };
 
-__device__ __forceinline__ void load_q4k(RawQ4K &r, rsrc_t rs, u32 off, int g) {
+__device__ __forceinline__ void load_unit(RawQ4K &r, rsrc_t rs, u32 off, int g) {
     r.h = ld16(rs, off);
     r.qa = ld16(rs, off + 16 + 32 * g);
     r.qb = ld16(rs, off + 32 + 32 * g);
 }
 
-template <int M, int R>
-__device__ __forceinline__ void mac_q4k(const RawQ4K (&raw)[R], int g, const float *xs, int xo, int XS,
-                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+template <int M, int R, class XA>
+__device__ __forceinline__ void val_unit(const RawQ4K (&raw)[R], int g, const XA &xa, float (&v)[R][M]) {
     float dsc0[R], dsc1[R], dm0[R], dm1[R];
     const u32 sel = (u32)(2 * g) | ((u32)(2 * g + 1) << 8) | 0x0C0C0000u;
 #pragma unroll
@@ -162,8 +217,8 @@ __device__ __forceinline__ void mac_q4k(const RawQ4K (&raw)[R], int g, const flo
         f4 xl[M], xh[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            xl[m] = lds4(xs + m * XS + xo + xpad(4 * i) - xpad(0));
-            xh[m] = lds4(xs + m * XS + xo + xpad(32 + 4 * i) - xpad(0));
+            xl[m] = xa.x4(m, 4 * i);
+            xh[m] = xa.x4(m, 32 + 4 * i);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -190,14 +245,14 @@ __device__ __forceinline__ void mac_q4k(const RawQ4K (&raw)[R], int g, const flo
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        const f4 sx = lds4(ss + m * SS + so);
-        const float s_lo = sx.x + sx.y, s_hi = sx.z + sx.w;
+        const float s_lo = xa.sum(m, 0) + xa.sum(m, 1), s_hi = xa.sum(m, 2) + xa.sum(m, 3);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            aq[r][m] = __builtin_fmaf(dsc0[r], slo[r][m], aq[r][m]);
-            aq[r][m] = __builtin_fmaf(dsc1[r], shi[r][m], aq[r][m]);
-            am[r][m] = __builtin_fmaf(dm0[r], s_lo, am[r][m]);
-            am[r][m] = __builtin_fmaf(dm1[r], s_hi, am[r][m]);
+            float aq = dsc0[r] * slo[r][m];
+            aq = __builtin_fmaf(dsc1[r], shi[r][m], aq);
+            float am = dm0[r] * s_lo;
+            am = __builtin_fmaf(dm1[r], s_hi, am);
+            v[r][m] = __builtin_fmaf(aq, 16777216.0f, -am);
         }
     }
 }
@@ -205,30 +260,53 @@ __device__ __forceinline__ void mac_q4k(const RawQ4K (&raw)[R], int g, const flo
 // ---- Q6_K: unit (block b, half h, quarter q2) = the 64 weights
 // 128h + 32g + 16*q2 + i (g = 0..3, i = 0..15): low bits from bytes
 // 64h + 16*q2 + i (g = 0, 2) and 64h + 32 + 16*q2 + i (g = 1, 3), high bits
-// from byte 128 + 32h + 16*q2 + i, scales 8h + 2g + q2.
-struct RawQ6K { u32 a[4], b[4], hq[4], s0, s1; float d; };
+// from byte 128 + 32h + 16*q2 + i, scales 8h + 2g + q2.  Blocks may start
+// 2 bytes off a dword: fields are read dword-aligned and realigned.
+// The raw registers hold the dword-aligned loads as they arrive; the
+// realignment happens at use, so a prefetch never waits for its data.
+struct RawQ6K { u4 a, b, hq; u32 a4, b4, h4, s0, s1, s2, dw, sh; };
 
-__device__ __forceinline__ void load_q6k(RawQ6K &r, rsrc_t rs, u32 off, int h, int q2) {
+__device__ __forceinline__ void load_unit(RawQ6K &r, rsrc_t rs, u32 off, int sub) {
+    const int h = sub >> 1, q2 = sub & 1;
     const u32 sh = off & 3u, base = off - sh;
     const u32 oa = base + 64 * h + 16 * q2;
-    const u4 a = ld16(rs, oa), b = ld16(rs, oa + 32), hq = ld16(rs, base + 128 + 32 * h + 16 * q2);
-    const u32 a4 = ld4(rs, oa + 16), b4 = ld4(rs, oa + 48), h4 = ld4(rs, base + 144 + 32 * h + 16 * q2);
-    const u4 sc = ld16(rs, base + 192 + 8 * h);
-    const u32 dw = ld4(rs, base + 208);
-    r.a[0] = realign(a.y, a.x, sh); r.a[1] = realign(a.z, a.y, sh);
-    r.a[2] = realign(a.w, a.z, sh); r.a[3] = realign(a4, a.w, sh);
-    r.b[0] = realign(b.y, b.x, sh); r.b[1] = realign(b.z, b.y, sh);
-    r.b[2] = realign(b.w, b.z, sh); r.b[3] = realign(b4, b.w, sh);
-    r.hq[0] = realign(hq.y, hq.x, sh); r.hq[1] = realign(hq.z, hq.y, sh);
-    r.hq[2] = realign(hq.w, hq.z, sh); r.hq[3] = realign(h4, hq.w, sh);
-    r.s0 = realign(sc.y, sc.x, sh);
-    r.s1 = realign(sc.z, sc.y, sh);
-    r.d = half_lo(dw >> (8 * sh));
+    r.a = ld16(rs, oa);
+    r.a4 = ld4(rs, oa + 16);
+    r.b = ld16(rs, oa + 32);
+    r.b4 = ld4(rs, oa + 48);
+    r.hq = ld16(rs, base + 128 + 32 * h + 16 * q2);
+    r.h4 = ld4(rs, base + 144 + 32 * h + 16 * q2);
+    const u32 so = base + 192 + 8 * h;
+    r.s0 = ld4(rs, so);
+    r.s1 = ld4(rs, so + 4);
+    r.s2 = ld4(rs, so + 8);
+    r.dw = ld4(rs, base + 208);
+    r.sh = sh;
 }
 
-template <int M, int R>
-__device__ __forceinline__ void mac_q6k(const RawQ6K (&raw)[R], int q2, const float *xs, int xo, int XS,
-                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+struct Q6KFields { u32 a[4], b[4], hq[4], s0, s1; float d; };
+
+__device__ __forceinline__ Q6KFields fields(const RawQ6K &r) {
+    Q6KFields f;
+    const u32 sh = r.sh;
+    f.a[0] = realign(r.a.y, r.a.x, sh); f.a[1] = realign(r.a.z, r.a.y, sh);
+    f.a[2] = realign(r.a.w, r.a.z, sh); f.a[3] = realign(r.a4, r.a.w, sh);
+    f.b[0] = realign(r.b.y, r.b.x, sh); f.b[1] = realign(r.b.z, r.b.y, sh);
+    f.b[2] = realign(r.b.w, r.b.z, sh); f.b[3] = realign(r.b4, r.b.w, sh);
+    f.hq[0] = realign(r.hq.y, r.hq.x, sh); f.hq[1] = realign(r.hq.z, r.hq.y, sh);
+    f.hq[2] = realign(r.hq.w, r.hq.z, sh); f.hq[3] = realign(r.h4, r.hq.w, sh);
+    f.s0 = realign(r.s1, r.s0, sh);
+    f.s1 = realign(r.s2, r.s1, sh);
+    f.d = half_lo(r.dw >> (8 * sh));
+    return f;
+}
+
+template <int M, int R, class XA>
+__device__ __forceinline__ void val_unit(const RawQ6K (&rawu)[R], int sub, const XA &xa, float (&v)[R][M]) {
+    const int q2 = sub & 1;
+    Q6KFields raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[r] = fields(rawu[r]);
     float dsc[R][4];
     const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
 #pragma unroll
@@ -250,7 +328,7 @@ __device__ __forceinline__ void mac_q6k(const RawQ6K (&raw)[R], int q2, const fl
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) xv[m][g] = lds4(xs + m * XS + xo + xpad(32 * g + 4 * k) - xpad(0));
+            for (int g = 0; g < 4; ++g) xv[m][g] = xa.x4(m, 32 * g + 4 * k);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 A = raw[r].a[k], B = raw[r].b[k], H = raw[r].hq[k];
@@ -280,16 +358,17 @@ __device__ __forceinline__ void mac_q6k(const RawQ6K (&raw)[R], int q2, const fl
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        const float *sp = ss + m * SS + so;
-        const float sx[4] = {sp[0], sp[2], sp[4], sp[6]};
+        const float sx[4] = {xa.sum(m, 0), xa.sum(m, 1), xa.sum(m, 2), xa.sum(m, 3)};
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            aq[r][m] = __builtin_fmaf(dsc[r][0], acc[r][m][0], aq[r][m]);
-            aq[r][m] = __builtin_fmaf(dsc[r][1], acc[r][m][1], aq[r][m]);
-            aq[r][m] = __builtin_fmaf(dsc[r][2] * 0.0625f, acc[r][m][2], aq[r][m]);
-            aq[r][m] = __builtin_fmaf(dsc[r][3] * 0.0625f, acc[r][m][3], aq[r][m]);
+            float aq = dsc[r][0] * acc[r][m][0];
+            aq = __builtin_fmaf(dsc[r][1], acc[r][m][1], aq);
+            aq = __builtin_fmaf(dsc[r][2] * 0.0625f, acc[r][m][2], aq);
+            aq = __builtin_fmaf(dsc[r][3] * 0.0625f, acc[r][m][3], aq);
+            float am = dsc[r][0] * sx[0];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) am[r][m] = __builtin_fmaf(dsc[r][g], sx[g], am[r][m]);
+            for (int g = 1; g < 4; ++g) am = __builtin_fmaf(dsc[r][g], sx[g], am);
+            v[r][m] = __builtin_fmaf(aq, 16777216.0f, -32.0f * am);
         }
     }
 }
@@ -299,17 +378,18 @@ __device__ __forceinline__ void mac_q6k(const RawQ6K (&raw)[R], int q2, const fl
 // 32h + 16*q2 + i, scale/min byte 8h + 2s + q2.
 struct RawQ2K { u4 q; u32 s0, s1, dd; };
 
-__device__ __forceinline__ void load_q2k(RawQ2K &r, rsrc_t rs, u32 off, int h, int q2) {
+__device__ __forceinline__ void load_unit(RawQ2K &r, rsrc_t rs, u32 off, int sub) {
+    const int h = sub >> 1, q2 = sub & 1;
     r.q = ld16(rs, off + 16 + 32 * h + 16 * q2);
-    const u4 sc = ld16(rs, off + 8 * h);   // bytes 8h .. 8h+15 (only 8 used)
+    const u4 sc = ld16(rs, off + 8 * h);   // bytes 8h .. 8h+15 (the first 8 are used)
     r.s0 = sc.x;
     r.s1 = sc.y;
     r.dd = ld4(rs, off + 80);
 }
 
-template <int M, int R>
-__device__ __forceinline__ void mac_q2k(const RawQ2K (&raw)[R], int q2, const float *xs, int xo, int XS,
-                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+template <int M, int R, class XA>
+__device__ __forceinline__ void val_unit(const RawQ2K (&raw)[R], int sub, const XA &xa, float (&v)[R][M]) {
+    const int q2 = sub & 1;
     float dsc[R][4], dmm[R][4];
     const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
 #pragma unroll
@@ -336,7 +416,7 @@ __device__ __forceinline__ void mac_q2k(const RawQ2K (&raw)[R], int q2, const fl
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) xv[m][s] = lds4(xs + m * XS + xo + xpad(32 * s + 4 * k) - xpad(0));
+            for (int s = 0; s < 4; ++s) xv[m][s] = xa.x4(m, 32 * s + 4 * k);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 D = raw[r].q[k], D8 = D >> 8;
@@ -358,36 +438,51 @@ __device__ __forceinline__ void mac_q2k(const RawQ2K (&raw)[R], int q2, const fl
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        const float *sp = ss + m * SS + so;
-        const float sx[4] = {sp[0], sp[2], sp[4], sp[6]};
+        const float sx[4] = {xa.sum(m, 0), xa.sum(m, 1), xa.sum(m, 2), xa.sum(m, 3)};
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r) {
+            float aq = dsc[r][0] * acc[r][m][0];
+            float am = dmm[r][0] * sx[0];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                aq[r][m] = __builtin_fmaf(dsc[r][s], acc[r][m][s], aq[r][m]);
-                am[r][m] = __builtin_fmaf(dmm[r][s], sx[s], am[r][m]);
+            for (int s = 1; s < 4; ++s) {
+                aq = __builtin_fmaf(dsc[r][s], acc[r][m][s], aq);
+                am = __builtin_fmaf(dmm[r][s], sx[s], am);
             }
+            v[r][m] = __builtin_fmaf(aq, 16777216.0f, -am);
+        }
     }
 }
 
-// ---- Q8_0: unit = one block of 32 weights.
-struct RawQ80 { u32 q[8]; float d; };
+// ---- Q8_0: unit = one block of 32 weights; quants read as q + 128.
+struct RawQ80 { u4 a, b; u32 c, dw, off; };
 
-__device__ __forceinline__ void load_q80(RawQ80 &r, rsrc_t rs, u32 off) {
-    const u32 qo = off + 2, sh = qo & 3u, qb = qo - sh;
-    const u4 a = ld16(rs, qb), b = ld16(rs, qb + 16);
-    const u32 c = ld4(rs, qb + 32);
-    const u32 dw = ld4(rs, off & ~3u);
-    r.q[0] = realign(a.y, a.x, sh); r.q[1] = realign(a.z, a.y, sh);
-    r.q[2] = realign(a.w, a.z, sh); r.q[3] = realign(b.x, a.w, sh);
-    r.q[4] = realign(b.y, b.x, sh); r.q[5] = realign(b.z, b.y, sh);
-    r.q[6] = realign(b.w, b.z, sh); r.q[7] = realign(c, b.w, sh);
-    r.d = half_lo(dw >> (8 * (off & 3u)));
+__device__ __forceinline__ void load_unit(RawQ80 &r, rsrc_t rs, u32 off, int) {
+    const u32 qo = off + 2, qb = qo & ~3u;
+    r.a = ld16(rs, qb);
+    r.b = ld16(rs, qb + 16);
+    r.c = ld4(rs, qb + 32);
+    r.dw = ld4(rs, off & ~3u);
+    r.off = off;
 }
 
-template <int M, int R>
-__device__ __forceinline__ void mac_q80(const RawQ80 (&raw)[R], const float *xs, int xo, int XS,
-                                        const float *ss, int so, int SS, float (&aq)[R][M], float (&am)[R][M]) {
+struct Q80Fields { u32 q[8]; float d; };
+
+__device__ __forceinline__ Q80Fields fields(const RawQ80 &r) {
+    Q80Fields f;
+    const u32 sh = (r.off + 2) & 3u;
+    f.q[0] = realign(r.a.y, r.a.x, sh); f.q[1] = realign(r.a.z, r.a.y, sh);
+    f.q[2] = realign(r.a.w, r.a.z, sh); f.q[3] = realign(r.b.x, r.a.w, sh);
+    f.q[4] = realign(r.b.y, r.b.x, sh); f.q[5] = realign(r.b.z, r.b.y, sh);
+    f.q[6] = realign(r.b.w, r.b.z, sh); f.q[7] = realign(r.c, r.b.w, sh);
+    f.d = half_lo(r.dw >> (8 * (r.off & 3u)));
+    return f;
+}
+
+template <int M, int R, class XA>
+__device__ __forceinline__ void val_unit(const RawQ80 (&rawu)[R], int, const XA &xa, float (&v)[R][M]) {
+    Q80Fields raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[r] = fields(rawu[r]);
     float acc[R][M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -397,10 +492,10 @@ __device__ __forceinline__ void mac_q80(const RawQ80 (&raw)[R], const float *xs,
     for (int i = 0; i < 8; ++i) {
         f4 xv[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = lds4(xs + m * XS + xo + xpad(4 * i) - xpad(0));
+        for (int m = 0; m < M; ++m) xv[m] = xa.x4(m, 4 * i);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const u32 U = raw[r].q[i] ^ 0x80808080u;    // q + 128 as unsigned bytes
+            const u32 U = raw[r].q[i] ^ 0x80808080u;
             const hf2 we = as_h2(U & 0x00FF00FFu), wo = as_h2((U >> 8) & 0x00FF00FFu);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -415,25 +510,50 @@ __device__ __forceinline__ void mac_q80(const RawQ80 (&raw)[R], const float *xs,
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        const float sx = ss[m * SS + so] + ss[m * SS + so + 1];
+        const float sx = xa.sum(m, 0) + xa.sum(m, 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            aq[r][m] = __builtin_fmaf(raw[r].d, acc[r][m], aq[r][m]);
-            am[r][m] = __builtin_fmaf(raw[r].d, sx, am[r][m]);
+            const float aq = raw[r].d * acc[r][m];
+            const float am = raw[r].d * sx;
+            v[r][m] = __builtin_fmaf(aq, 16777216.0f, -128.0f * am);
         }
     }
 }
 
+template <int T> struct RawOf;
+template <> struct RawOf<T_Q4_K> { typedef RawQ4K type; };
+template <> struct RawOf<T_Q6_K> { typedef RawQ6K type; };
+template <> struct RawOf<T_Q2_K> { typedef RawQ2K type; };
+template <> struct RawOf<T_Q8_0> { typedef RawQ80 type; };
+
+// First weight (within its row) of unit u, and the spacing of its 16-sums.
+template <int T> __device__ __forceinline__ int unit_e0(int u) {
+    typedef Fmt<T> F;
+    const int b = u / F::UPB, sub = u - b * F::UPB;
+    if constexpr (T == T_Q4_K) return b * 256 + 64 * sub;
+    else if constexpr (T == T_Q8_0) return b * 32;
+    else return b * 256 + 128 * (sub >> 1) + 16 * (sub & 1);
+}
+template <int T> constexpr int sum_run_stride() { return (T == T_Q6_K || T == T_Q2_K) ? 2 : 1; }
+
 // ---------------------------------------------------------------------------
-// Activation staging: rows xr[0..M) of the chunk [c0, c0 + kc) go to LDS with
-// 16 B of padding every 64 floats; sums[m][j] = sum of x[c0 + 16j .. +16) in a
-// fixed order.  kc is a multiple of 32.
+// Row-sum structure shared by every kernel.  Units are numbered along the row;
+// "stripe" i is units [i*LPR, (i+1)*LPR) with unit i*LPR + l on lane l of a
+// lane group.  A row's result is
+//     y = ((0 + S_0) + S_1) + ... ,   S_i = group_sum over the stripe's lanes
+// of the per-unit values v, with a fixed binary tree (lanes paired by bit 0,
+// then bit 1, ... ).  Any kernel that follows it gives the same bits.
+
+// ---------------------------------------------------------------------------
+// Activation staging for the LDS kernels: rows xr[0..M) of the chunk
+// [c0, c0 + kc) go to LDS with 16 B of padding every 64 floats, and
+// ss[m][j] = sum16 of x[c0 + 16j .. +16).  kc is a multiple of 32.
 
 template <int M>
 __device__ __forceinline__ void stage_x(float *xs, float *ss, int XS, int SS, const float *const (&xr)[M],
-                                        int c0, int kc) {
+                                        int c0, int kc, int nthreads) {
     const int n16 = kc >> 4;
-    for (int idx = threadIdx.x; idx < M * n16; idx += WG_THREADS) {
+    for (int idx = threadIdx.x; idx < M * n16; idx += nthreads) {
         const int m = idx / n16, j = idx - m * n16;
         const f4 *src = reinterpret_cast<const f4 *>(xr[m] + c0 + 16 * j);
         const f4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
@@ -442,9 +562,7 @@ __device__ __forceinline__ void stage_x(float *xs, float *ss, int XS, int SS, co
         reinterpret_cast<f4 *>(dst)[1] = v1;
         reinterpret_cast<f4 *>(dst)[2] = v2;
         reinterpret_cast<f4 *>(dst)[3] = v3;
-        const float s = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
-                        (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
-        ss[m * SS + j] = s;
+        ss[m * SS + j] = sum16(v0, v1, v2, v3);
     }
 }
 
@@ -455,14 +573,17 @@ __host__ __device__ constexpr int s_stride(int kc) { return ((kc >> 4) + 3) & ~3
 __host__ __device__ constexpr int lds_floats(int M, int kc) { return M * (x_stride(kc) + s_stride(kc)); }
 
 // ---------------------------------------------------------------------------
-// One work-group computes `nrows` rows starting at `row0` of one matrix for M
-// activation rows xr[] and writes yr[m][row] for each of them.
+// LDS kernel body (any M; used for M >= 2, for the routed experts and for very
+// long rows).  One work-group of WG_THREADS computes `nrows` rows starting at
+// `row0` of one matrix for M activation rows xr[] and writes yr[m][row].
+// Each lane group of LPR lanes owns R rows; activations are staged per K chunk.
 
 template <int T, int M, int R>
 __device__ __forceinline__ void gemv_tile(float *smem, const uint8_t *W, int64_t row_bytes, int row0, int nrows,
                                           int K, int KC, int lpr, const float *const (&xr)[M],
                                           float *const (&yr)[M]) {
     typedef Fmt<T> F;
+    typedef typename RawOf<T>::type Raw;
     const int G = 64 / lpr;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int grp = lane / lpr, slot = lane - grp * lpr;
@@ -478,11 +599,11 @@ __device__ __forceinline__ void gemv_tile(float *smem, const uint8_t *W, int64_t
         roff[r] = rr < nrows ? delta + (u32)((int64_t)rr * row_bytes) : OOB;
     }
 
-    float aq[R][M], am[R][M];
+    float acc[R][M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) aq[r][m] = am[r][m] = 0.f;
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
     const int kcmax = KC < K ? KC : K;
     const int XS = x_stride(kcmax);
@@ -493,40 +614,29 @@ __device__ __forceinline__ void gemv_tile(float *smem, const uint8_t *W, int64_t
     for (int c0 = 0; c0 < K; c0 += KC) {
         const int kc = (K - c0) < KC ? (K - c0) : KC;
         if (c0) __syncthreads();
-        stage_x<M>(xs, ss, XS, SS, xr, c0, kc);
+        stage_x<M>(xs, ss, XS, SS, xr, c0, kc, WG_THREADS);
         __syncthreads();
         const int units = (kc / F::QK) * F::UPB;
-        const int b0 = c0 / F::QK;
-        for (int ul = slot; ul < units; ul += lpr) {
-            const int bl = ul / F::UPB, sub = ul - bl * F::UPB;
-            const u32 boff = (u32)(b0 + bl) * F::BYTES;
-            const int xe = bl * F::QK;              // chunk-relative first weight of the block
-            if constexpr (T == T_Q4_K) {
-                RawQ4K raw[R];
+        const int ub = (c0 / F::QK) * F::UPB;       // units before this chunk
+        const int nstripes = (units + lpr - 1) / lpr;
+        for (int i = 0; i < nstripes; ++i) {
+            const int ul = slot + lpr * i;
+            const bool act = ul < units;
+            const int uc = act ? ul : 0;
+            const int bl = uc / F::UPB, sub = uc - bl * F::UPB;
+            const u32 boff = (u32)((ub + uc) / F::UPB) * F::BYTES;
+            Raw raw[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) load_q4k(raw[r], rs, roff[r] + boff, sub);
-                const int e0 = xe + 64 * sub;
-                mac_q4k<M, R>(raw, sub, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
-            } else if constexpr (T == T_Q6_K) {
-                const int h = sub >> 1, q2 = sub & 1;
-                RawQ6K raw[R];
+            for (int r = 0; r < R; ++r) load_unit(raw[r], rs, act ? roff[r] + boff : OOB, sub);
+            const int e0 = unit_e0<T>(uc);
+            const XLds xa{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+            float v[R][M];
+            val_unit<M, R>(raw, sub, xa, v);
+            (void)bl;
 #pragma unroll
-                for (int r = 0; r < R; ++r) load_q6k(raw[r], rs, roff[r] + boff, h, q2);
-                const int e0 = xe + 128 * h + 16 * q2;
-                mac_q6k<M, R>(raw, q2, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
-            } else if constexpr (T == T_Q2_K) {
-                const int h = sub >> 1, q2 = sub & 1;
-                RawQ2K raw[R];
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int r = 0; r < R; ++r) load_q2k(raw[r], rs, roff[r] + boff, h, q2);
-                const int e0 = xe + 128 * h + 16 * q2;
-                mac_q2k<M, R>(raw, q2, xs, xpad(e0), XS, ss, e0 >> 4, SS, aq, am);
-            } else {
-                RawQ80 raw[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) load_q80(raw[r], rs, roff[r] + boff);
-                mac_q80<M, R>(raw, xs, xpad(xe), XS, ss, xe >> 4, SS, aq, am);
-            }
+                for (int m = 0; m < M; ++m) acc[r][m] += group_sum(act ? v[r][m] : 0.f, lpr);
         }
     }
 
@@ -534,10 +644,8 @@ __device__ __forceinline__ void gemv_tile(float *smem, const uint8_t *W, int64_t
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float v = __builtin_fmaf(aq[r][m], 16777216.0f, -(float)F::KM * am[r][m]);
-            const float tot = group_sum(v, lpr);
             const int rr = rfirst + r;
-            if (slot == 0 && rr < nrows) yr[m][row0 + rr] = tot;
+            if (slot == 0 && rr < nrows) yr[m][row0 + rr] = acc[r][m];
         }
 }
 
@@ -560,6 +668,164 @@ __global__ __launch_bounds__(WG_THREADS) void qgemv_kernel(const uint8_t *__rest
         yr[m] = y + (int64_t)m * N;
     }
     gemv_tile<T, M, R>(smem, W, row_bytes, row0, nrows, K, KC, lpr, xr, yr);
+}
+
+// Batch-1 kernel.  The row is cut into stripes of 64 units (fewer than 64:
+// one stripe of LPR lanes, 64 / LPR rows per wave); a work-group holds RS
+// row slots x NS stripes of waves (at most 16 waves), one work-group per
+// compute unit, persistent.  The work-group stages the activations and their
+// 16-sums once in LDS; every wave then copies the slice its lanes need into
+// registers, so the activations cross L2 once per compute unit.  Row slot rs
+// of work-group b takes the row steps b*RS + rs, + grid*RS, ... (interleaved,
+// every work-group gets the same share).  Each wave keeps the loads of the
+// next D steps in flight in a ring of registers; the loop body is
+// straight-line: a step's stripe sum is parked in one lane (lane = step mod
+// LPR) and every LPR steps the parked sums are flushed -- stored directly when
+// the row is one stripe, otherwise added across stripes in stripe order
+// through LDS.
+
+// Issue the loads of one row step.  Never conditional: a step past the last
+// row gets an empty buffer (its loads return zeros), so the loads of every
+// ring slot stay in flight in program order.
+template <int T>
+__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, const uint8_t *W, int64_t row_bytes,
+                                           int N, int G, int row0, int grp, bool act, u32 boff, int sub) {
+    const int left = N - row0;
+    const int nr = left < 0 ? 0 : (left < G ? left : G);
+    const int rr = nr ? row0 : 0;
+    const uintptr_t ta = (uintptr_t)(W + (int64_t)rr * row_bytes);
+    const u32 delta = (u32)(ta & 3u);
+    const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
+    load_unit(raw, rs, (act && grp < nr) ? delta + (u32)((int64_t)grp * row_bytes) + boff : OOB, sub);
+}
+
+// Registers <- LDS for one unit's activations (same values as XReg::load).
+template <int T>
+__device__ __forceinline__ void xreg_from_lds(XReg<T> &xr, const XLds &xa) {
+#pragma unroll
+    for (int r = 0; r < XReg<T>::NS; ++r) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xr.v[4 * r + k] = xa.x4(0, (XReg<T>::RUNS32 ? 32 : 16) * r + 4 * k);
+        xr.s[r] = xa.sum(0, r);
+    }
+}
+
+// Write the parked sums of steps [b0, b0 + LPR): one stripe -- store; several
+// stripes -- add them in stripe order through LDS (barriers: every wave of the
+// work-group calls this at the same steps).
+__device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first, int rstride, int N, int ns,
+                                       int wave, int lane, int rsl, int stripe, int grp, int slot,
+                                       float (*part)[64], float *__restrict__ y) {
+    if (ns > 1) {
+        part[wave][lane] = keep;
+        __syncthreads();
+        const int row = first + (b0 + lane) * rstride;
+        if (stripe == 0 && b0 + lane < wsteps && row < N) {
+            float s = 0.f;
+            for (int w = 0; w < ns; ++w) s += part[rsl * ns + w][lane];
+            y[row] = s;
+        }
+        __syncthreads();
+    } else {
+        const int row = first + (b0 + slot) * rstride + grp;
+        if (b0 + slot < wsteps && row < N) y[row] = 0.f + keep;
+    }
+}
+
+template <int T, int D>
+__global__ __launch_bounds__(1024) void qgemv1_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int N,
+                                                      int K, int lpr, int ns, const float *__restrict__ x,
+                                                      float *__restrict__ y) {
+    typedef Fmt<T> F;
+    typedef typename RawOf<T>::type Raw;
+    extern __shared__ float smem[];
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);       // [16][64]
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    float *ss = xs + XS;
+    const int nthreads = blockDim.x;
+    // wave index as a scalar: everything derived from it (the row of a step and
+    // the buffer descriptor of its loads) stays in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int RS = (nthreads >> 6) / ns;               // row slots
+    const int rsl = wave / ns, stripe = wave - rsl * ns;
+    const int G = 64 / lpr;
+    const int grp = lane / lpr, slot = lane - grp * lpr;
+    const int units = (K / F::QK) * F::UPB;
+    const int u = stripe * 64 + slot;
+    const bool act = u < units;
+    const int uc = act ? u : 0;
+    const int sub = uc % F::UPB;
+    const u32 boff = (u32)(uc / F::UPB) * F::BYTES;
+    const int rstride = gridDim.x * RS * G;
+    const int first = (blockIdx.x * RS + rsl) * G;
+    // steps of the work-group's first row slot; every row slot runs this many
+    // (uniform trip count: the flush below has barriers), later slots may run
+    // past N on empty buffers and store nothing
+    const int f0 = blockIdx.x * RS * G;
+    const int wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
+
+    // Prologue: activation loads first (at most two groups of 16 per thread),
+    // then the loads of the first D row steps, then the LDS writes -- waiting
+    // for the activations leaves the row loads in flight.
+    const int n16 = K >> 4;
+    f4 xg[2][4];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = threadIdx.x + it * nthreads;
+        const f4 *src = reinterpret_cast<const f4 *>(x + 16 * (idx < n16 ? idx : 0));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xg[it][k] = src[k];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every activation load ahead of the row loads
+    Raw ring[D][1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_step<T>(ring[d][0], W, row_bytes, N, G, first + d * rstride, grp, act, boff, sub);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        // unconditional, so the loads above are not sunk below the row loads:
+        // threads without a group write into the (not yet used) flush area
+        const int idx = threadIdx.x + it * nthreads;
+        const bool ok = idx < n16;
+        f4 *dst = reinterpret_cast<f4 *>(ok ? xs + xpad(16 * idx) : smem);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = xg[it][k];
+        (ok ? ss[idx] : smem[16]) = sum16(xg[it][0], xg[it][1], xg[it][2], xg[it][3]);
+    }
+    __syncthreads();
+    XReg<T> xa;
+    {
+        const int e0 = unit_e0<T>(uc);
+        const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+        xreg_from_lds<T>(xa, xl);
+    }
+
+    float keep = 0.f;
+    int j = 0;
+    for (; j + D <= wsteps; j += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            float v[1][1];
+            val_unit<1, 1>(ring[d], sub, xa, v);
+            issue_step<T>(ring[d][0], W, row_bytes, N, G, first + (j + d + D) * rstride, grp, act, boff, sub);
+            const float S = group_sum(act ? v[0][0] : 0.f, lpr);
+            keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+        }
+        if (((j + D) & (lpr - 1)) == 0)
+            flush1(keep, j + D - lpr, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, y);
+    }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        if (j + d < wsteps) {
+            float v[1][1];
+            val_unit<1, 1>(ring[d], sub, xa, v);
+            const float S = group_sum(act ? v[0][0] : 0.f, lpr);
+            keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+        }
+    }
+    if (wsteps & (lpr - 1))
+        flush1(keep, wsteps & ~(lpr - 1), wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, y);
 }
 
 // Routed experts: work-group (row tile, slot s).  Only the lowest slot that
@@ -660,7 +926,7 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__re
     float *out = dst + b * F::QK;
     if constexpr (T == T_Q4_K) {
         RawQ4K r;
-        load_q4k(r, rs, off, sub);
+        load_unit(r, rs, off, sub);
         const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
         const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
         const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
@@ -688,8 +954,9 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__re
         for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
     } else if constexpr (T == T_Q6_K) {
         const int h = sub >> 1, q2 = sub & 1;
-        RawQ6K r;
-        load_q6k(r, rs, off, h, q2);
+        RawQ6K ru;
+        load_unit(ru, rs, off, sub);
+        const Q6KFields r = fields(ru);
         const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
         const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
 #pragma unroll
@@ -711,7 +978,7 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__re
     } else if constexpr (T == T_Q2_K) {
         const int h = sub >> 1, q2 = sub & 1;
         RawQ2K r;
-        load_q2k(r, rs, off, h, q2);
+        load_unit(r, rs, off, sub);
         const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
         const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
         const float d = half_lo(r.dd), dmin = half_lo(r.dd >> 16);
@@ -730,8 +997,9 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__re
             for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
         }
     } else {
-        RawQ80 r;
-        load_q80(r, rs, off);
+        RawQ80 ru;
+        load_unit(ru, rs, off, 0);
+        const Q80Fields r = fields(ru);
         float w[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) w[i] = r.d * (float)(int)(signed char)(r.q[i >> 2] >> (8 * (i & 3))) + 0.0f;
@@ -761,7 +1029,8 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // 64 for every format).
 int chunk_for(int M) { return M == 1 ? 8192 : 4096; }
 
-int lanes_per_row(int units) { return units >= 64 ? 64 : (units > 16 ? 32 : 16); }
+// Lanes per row: enough that a row of fewer than 64 units fits one stripe.
+int lanes_per_row(int units) { return units > 32 ? 64 : (units > 16 ? 32 : 16); }
 
 template <typename Kern>
 hipError_t allow_lds(Kern k, size_t bytes) {
@@ -785,19 +1054,54 @@ int launch_qgemv_t(const void *W, int64_t row_bytes, int N, int K, const float *
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Row steps each wave of the batch-1 kernel keeps in flight.
+template <int T> constexpr int PREFETCH() { return T == T_Q8_0 ? 4 : (T == T_Q6_K ? 1 : 2); }
+
+// Batch-1 launch: one lane per unit of a row, stripes of 64 units, up to 16
+// waves per work-group, one work-group per compute unit (persistent).  Rows
+// whose activations do not fit in LDS go to the general kernel.
+template <int T>
+int launch_qgemv1(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int ns = units > 64 ? (units + 63) / 64 : 1;
+    const size_t lds = (size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float);
+    const int RS = 16 / (ns < 16 ? ns : 16);
+    // the prologue stages at most two groups of 16 activations per thread
+    if (ns > 8 || lds > 150 * 1024 || K / 16 > 2 * 64 * ns * RS)
+        return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    const int nt = 64 * ns * RS;
+    const int G = 64 / lpr;
+    auto kern = qgemv1_kernel<T, PREFETCH<T>()>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    const int64_t slots = ((int64_t)N + G - 1) / G;
+    const int64_t need = (slots + RS - 1) / RS;
+    const int64_t cap = cu_count();
+    const int grid = (int)(need < cap ? need : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, (const uint8_t *)W, row_bytes, N, K, lpr, ns, x, y);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
 template <int T>
 int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const float *x, float *y,
                    hipStream_t st) {
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);
-    const int G = 64 / lpr;
     switch (M) {
-    case 1: {
-        const int R = N >= 8192 * G ? 4 : (N >= 4096 * G ? 2 : 1);
-        if (R == 4) return launch_qgemv_t<T, 1, 4>(W, row_bytes, N, K, x, y, st, lpr);
-        if (R == 2) return launch_qgemv_t<T, 1, 2>(W, row_bytes, N, K, x, y, st, lpr);
-        return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    }
+    case 1: return launch_qgemv1<T>(W, row_bytes, N, K, x, y, st);
     case 2: return launch_qgemv_t<T, 2, 1>(W, row_bytes, N, K, x, y, st, lpr);
     case 3: return launch_qgemv_t<T, 3, 1>(W, row_bytes, N, K, x, y, st, lpr);
     case 4: return launch_qgemv_t<T, 4, 1>(W, row_bytes, N, K, x, y, st, lpr);
