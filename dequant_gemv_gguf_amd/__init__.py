@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     kq_block_info,
     kq_dequant,
     kq_qgemv,
+    kq_qgemv_multi,
     kq_qmoe_gemv,
     kq_qmoe_workspace_bytes,
     kq_row_bytes,

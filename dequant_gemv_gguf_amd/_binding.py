@@ -38,6 +38,7 @@ def lib():
         L.kq_row_bytes.restype = I64
         L.kq_dequant.argtypes = [I, P, I64, P, P]
         L.kq_qgemv.argtypes = [I, P, I64, I64, P, I, P, P]
+        L.kq_qgemv_multi.argtypes = [I, I, P, P, I64, P, I, P, P]
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
@@ -97,6 +98,26 @@ def kq_dequant(qtype, src, n_elems, dst, stream=None):
 def kq_qgemv(qtype, W, N, K, x, M, y, stream=None):
     _check("kq_qgemv", lib().kq_qgemv(int(qtype), _ptr(W), int(N), int(K), _ptr(x), int(M), _ptr(y),
                                       _stream(stream, y)))
+
+
+def _addr(t):
+    if t is None:
+        return 0
+    return t if isinstance(t, int) else t.data_ptr()
+
+
+def kq_qgemv_multi(qtype, Ws, Ns, K, x, M, ys, stream=None):
+    """Ws, Ns, ys: equal-length sequences (tensors or int addresses, row counts,
+    tensors or int addresses); marshalled into the host arrays the C call takes."""
+    count = len(Ws)
+    if len(Ns) != count or len(ys) != count:
+        raise ValueError("kq_qgemv_multi: Ws, Ns and ys must have the same length")
+    Wa = (ctypes.c_void_p * max(count, 1))(*[_addr(w) for w in Ws])
+    Na = (ctypes.c_int64 * max(count, 1))(*[int(n) for n in Ns])
+    Ya = (ctypes.c_void_p * max(count, 1))(*[_addr(y) for y in ys])
+    like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
+    _check("kq_qgemv_multi", lib().kq_qgemv_multi(int(qtype), count, Wa, Na, int(K), _ptr(x), int(M), Ya,
+                                                  _stream(stream, like)))
 
 
 def kq_qmoe_workspace_bytes(T, k, N):

@@ -684,19 +684,52 @@ __global__ __launch_bounds__(WG_THREADS) void qgemv_kernel(const uint8_t *__rest
 // the row is one stripe, otherwise added across stripes in stripe order
 // through LDS.
 
-// Issue the loads of one row step.  Never conditional: a step past the last
-// row gets an empty buffer (its loads return zeros), so the loads of every
-// ring slot stay in flight in program order.
-template <int T>
-__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, const uint8_t *W, int64_t row_bytes,
+// Several matrices with the same format and K that read the same
+// activations can be served by one launch: their rows are numbered one after
+// another, segment s holding rows [start[s], start[s] + rows[s]).  Starts are
+// multiples of the rows one step covers (G), so a step never spans two
+// segments; the numbers between a segment's last row and the next start are
+// padding that loads and stores nothing.
+constexpr int MAX_SEGS = 8;
+struct Segs {
+    const uint8_t *W[MAX_SEGS];
+    float *y[MAX_SEGS];
+    int start[MAX_SEGS + 1];
+    int rows[MAX_SEGS];
+    int n;
+};
+
+template <bool MS> __device__ __forceinline__ int seg_of(const Segs &sg, int row) {
+    if (!MS) return 0;
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && row >= sg.start[i]) ? 1 : 0;
+    return s;
+}
+
+// Issue the loads of one row step (rows row0 .. row0 + G - 1, one per lane
+// group).  Never conditional: a step past the last row gets an empty buffer
+// (its loads return zeros), so the loads of every ring slot stay in flight in
+// program order.
+template <int T, bool MS>
+__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, const Segs &sg, int64_t row_bytes,
                                            int N, int G, int row0, int grp, bool act, u32 boff, int sub) {
-    const int left = N - row0;
-    const int nr = left < 0 ? 0 : (left < G ? left : G);
-    const int rr = nr ? row0 : 0;
-    const uintptr_t ta = (uintptr_t)(W + (int64_t)rr * row_bytes);
+    const int sgi = seg_of<MS>(sg, row0 < N ? row0 : 0);
+    const int local = row0 - sg.start[sgi];
+    const int left = sg.rows[sgi] - local;
+    const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
+    const uintptr_t ta = (uintptr_t)(sg.W[sgi] + (int64_t)(nr ? local : 0) * row_bytes);
     const u32 delta = (u32)(ta & 3u);
     const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
     load_unit(raw, rs, (act && grp < nr) ? delta + (u32)((int64_t)grp * row_bytes) + boff : OOB, sub);
+}
+
+// Output slot of a row, or NULL for a padding row or a row past the end.
+template <bool MS> __device__ __forceinline__ float *out_of(const Segs &sg, int N, int row) {
+    if (row >= N) return nullptr;
+    const int s = seg_of<MS>(sg, row);
+    const int local = row - sg.start[s];
+    return local < sg.rows[s] ? sg.y[s] + local : nullptr;
 }
 
 // Registers <- LDS for one unit's activations (same values as XReg::load).
@@ -713,29 +746,30 @@ __device__ __forceinline__ void xreg_from_lds(XReg<T> &xr, const XLds &xa) {
 // Write the parked sums of steps [b0, b0 + LPR): one stripe -- store; several
 // stripes -- add them in stripe order through LDS (barriers: every wave of the
 // work-group calls this at the same steps).
+template <bool MS>
 __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first, int rstride, int N, int ns,
                                        int wave, int lane, int rsl, int stripe, int grp, int slot,
-                                       float (*part)[64], float *__restrict__ y) {
+                                       float (*part)[64], const Segs &sg) {
     if (ns > 1) {
         part[wave][lane] = keep;
         __syncthreads();
-        const int row = first + (b0 + lane) * rstride;
-        if (stripe == 0 && b0 + lane < wsteps && row < N) {
+        float *o = out_of<MS>(sg, N, first + (b0 + lane) * rstride);
+        if (stripe == 0 && b0 + lane < wsteps && o) {
             float s = 0.f;
             for (int w = 0; w < ns; ++w) s += part[rsl * ns + w][lane];
-            y[row] = s;
+            *o = s;
         }
         __syncthreads();
     } else {
-        const int row = first + (b0 + slot) * rstride + grp;
-        if (b0 + slot < wsteps && row < N) y[row] = 0.f + keep;
+        float *o = out_of<MS>(sg, N, first + (b0 + slot) * rstride + grp);
+        if (b0 + slot < wsteps && o) *o = 0.f + keep;
     }
 }
 
-template <int T, int D>
-__global__ __launch_bounds__(1024) void qgemv1_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int N,
-                                                      int K, int lpr, int ns, const float *__restrict__ x,
-                                                      float *__restrict__ y) {
+template <int T, int D, int LB, bool MS>
+__global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
+                                                    const float *__restrict__ x) {
+    const int N = sg.start[sg.n];
     typedef Fmt<T> F;
     typedef typename RawOf<T>::type Raw;
     extern __shared__ float smem[];
@@ -780,7 +814,7 @@ __global__ __launch_bounds__(1024) void qgemv1_kernel(const uint8_t *__restrict_
     __builtin_amdgcn_sched_barrier(0);   // keep every activation load ahead of the row loads
     Raw ring[D][1];
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue_step<T>(ring[d][0], W, row_bytes, N, G, first + d * rstride, grp, act, boff, sub);
+    for (int d = 0; d < D; ++d) issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + d * rstride, grp, act, boff, sub);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -808,12 +842,12 @@ __global__ __launch_bounds__(1024) void qgemv1_kernel(const uint8_t *__restrict_
         for (int d = 0; d < D; ++d) {
             float v[1][1];
             val_unit<1, 1>(ring[d], sub, xa, v);
-            issue_step<T>(ring[d][0], W, row_bytes, N, G, first + (j + d + D) * rstride, grp, act, boff, sub);
+            issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + (j + d + D) * rstride, grp, act, boff, sub);
             const float S = group_sum(act ? v[0][0] : 0.f, lpr);
             keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
         }
         if (((j + D) & (lpr - 1)) == 0)
-            flush1(keep, j + D - lpr, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, y);
+            flush1<MS>(keep, j + D - lpr, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
     }
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
@@ -825,7 +859,7 @@ __global__ __launch_bounds__(1024) void qgemv1_kernel(const uint8_t *__restrict_
         }
     }
     if (wsteps & (lpr - 1))
-        flush1(keep, wsteps & ~(lpr - 1), wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, y);
+        flush1<MS>(keep, wsteps & ~(lpr - 1), wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
 }
 
 // Routed experts: work-group (row tile, slot s).  Only the lowest slot that
@@ -1067,32 +1101,117 @@ int cu_count() {
     return cache[dev];
 }
 
-// Row steps each wave of the batch-1 kernel keeps in flight.
-template <int T> constexpr int PREFETCH() { return T == T_Q8_0 ? 4 : (T == T_Q6_K ? 1 : 2); }
+// Batch-1 configurations: a wide one (work-groups up to 16 waves, 4 per SIMD,
+// 128 VGPRs) and a narrow one (up to 8 waves, 2 per SIMD, 256 VGPRs) whose
+// larger register budget pays for a deeper prefetch ring.  Q6_K and Q8_0 units
+// carry the most raw registers per weight; they take the narrow one when it
+// still holds at least two row slots (Q8_0: one), which measured faster; with
+// long Q6_K rows the wide one's extra waves win.  PREFETCH is the number of
+// row steps each wave keeps in flight; it must divide every lanes-per-row
+// value (16, 32, 64).
+template <int T, bool WIDE> constexpr int PREFETCH() {
+    return WIDE ? (T == T_Q6_K ? 1 : 2) : (T == T_Q8_0 ? 4 : 2);
+}
+template <int T> constexpr int NARROW_MAX_STRIPES() { return T == T_Q6_K ? 4 : (T == T_Q8_0 ? 8 : 0); }
 
-// Batch-1 launch: one lane per unit of a row, stripes of 64 units, up to 16
-// waves per work-group, one work-group per compute unit (persistent).  Rows
-// whose activations do not fit in LDS go to the general kernel.
-template <int T>
-int launch_qgemv1(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
+struct B1Cfg {
+    int lpr, ns, rs;
+    size_t lds;
+    bool wide;
+};
+
+// Batch-1 configuration for rows of K columns; false: use the LDS kernel.
+template <int T> bool batch1_cfg(int K, B1Cfg *c) {
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
-    const int lpr = lanes_per_row(units);
-    const int ns = units > 64 ? (units + 63) / 64 : 1;
-    const size_t lds = (size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float);
-    const int RS = 16 / (ns < 16 ? ns : 16);
+    c->lpr = lanes_per_row(units);
+    c->ns = units > 64 ? (units + 63) / 64 : 1;
+    c->lds = (size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float);
+    c->wide = c->ns > NARROW_MAX_STRIPES<T>();
+    const int maxw = c->wide ? 16 : 8;
+    if (c->ns > maxw || c->lds > 150 * 1024) return false;
+    c->rs = maxw / c->ns;
     // the prologue stages at most two groups of 16 activations per thread
-    if (ns > 8 || lds > 150 * 1024 || K / 16 > 2 * 64 * ns * RS)
-        return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    const int nt = 64 * ns * RS;
-    const int G = 64 / lpr;
-    auto kern = qgemv1_kernel<T, PREFETCH<T>()>;
-    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    const int64_t slots = ((int64_t)N + G - 1) / G;
-    const int64_t need = (slots + RS - 1) / RS;
+    if (K / 16 > 2 * 64 * c->ns * c->rs) return false;
+    return true;
+}
+
+template <int T, bool WIDE>
+int launch_qgemv1_cfg(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    const int nt = 64 * c.ns * c.rs;
+    const int G = 64 / c.lpr;
+    auto kern = sg.n > 1 ? qgemv1_kernel<T, PREFETCH<T, WIDE>(), WIDE ? 1024 : 512, true>
+                         : qgemv1_kernel<T, PREFETCH<T, WIDE>(), WIDE ? 1024 : 512, false>;
+    if (allow_lds(kern, c.lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
+    const int64_t need = (slots + c.rs - 1) / c.rs;
     const int64_t cap = cu_count();
     const int grid = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, (const uint8_t *)W, row_bytes, N, K, lpr, ns, x, y);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), c.lds, st, sg, row_bytes, K, c.lpr, c.ns, x);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+// Batch-1 launch over one or more segments (same format and K): one lane per
+// unit, stripes of 64 units, one work-group per compute unit (persistent).
+template <int T>
+int launch_qgemv1(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    if constexpr (NARROW_MAX_STRIPES<T>() > 0) {
+        if (!c.wide) return launch_qgemv1_cfg<T, false>(c, sg, row_bytes, K, x, st);
+    }
+    return launch_qgemv1_cfg<T, true>(c, sg, row_bytes, K, x, st);
+}
+
+template <int T>
+int launch_qgemv1_single(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
+    B1Cfg c;
+    if (!batch1_cfg<T>(K, &c))
+        return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB));
+    Segs sg = {};
+    sg.W[0] = (const uint8_t *)W;
+    sg.y[0] = y;
+    sg.start[0] = 0;
+    sg.start[1] = N;
+    sg.rows[0] = N;
+    sg.n = 1;
+    return launch_qgemv1<T>(c, sg, row_bytes, K, x, st);
+}
+
+// Batch-1 products of several matrices (same format and K) with the same
+// activations: up to MAX_SEGS matrices per launch.
+template <int T>
+int launch_qgemv1_multi(int count, const void *const *W, const int64_t *N, int64_t row_bytes, int K,
+                        const float *x, float *const *y, hipStream_t st) {
+    B1Cfg c;
+    if (!batch1_cfg<T>(K, &c)) {
+        for (int i = 0; i < count; ++i) {
+            if (N[i] == 0) continue;
+            const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, c.lpr);
+            if (r) return r;
+        }
+        return KQ_OK;
+    }
+    const int64_t G = 64 / c.lpr;
+    int i = 0;
+    while (i < count) {
+        Segs sg = {};
+        int64_t at = 0;
+        while (i < count && sg.n < MAX_SEGS) {
+            if (N[i] == 0) { ++i; continue; }
+            const int64_t next = at + (N[i] + G - 1) / G * G;
+            if (next >= ((int64_t)1 << 31)) break;
+            sg.W[sg.n] = (const uint8_t *)W[i];
+            sg.y[sg.n] = y[i];
+            sg.start[sg.n] = (int)at;
+            sg.rows[sg.n] = (int)N[i];
+            ++sg.n;
+            at = next;
+            ++i;
+        }
+        if (sg.n == 0) break;
+        sg.start[sg.n] = (int)at;
+        const int r = launch_qgemv1<T>(c, sg, row_bytes, K, x, st);
+        if (r) return r;
+    }
+    return KQ_OK;
 }
 
 template <int T>
@@ -1101,7 +1220,7 @@ int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const 
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);
     switch (M) {
-    case 1: return launch_qgemv1<T>(W, row_bytes, N, K, x, y, st);
+    case 1: return launch_qgemv1_single<T>(W, row_bytes, N, K, x, y, st);
     case 2: return launch_qgemv_t<T, 2, 1>(W, row_bytes, N, K, x, y, st, lpr);
     case 3: return launch_qgemv_t<T, 3, 1>(W, row_bytes, N, K, x, y, st, lpr);
     case 4: return launch_qgemv_t<T, 4, 1>(W, row_bytes, N, K, x, y, st, lpr);
@@ -1230,6 +1349,44 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K, const float *x, int 
     case KQ_TYPE_Q6_K: return launch_qgemv_m<T_Q6_K>(M, W, row_bytes, (int)N, (int)K, x, y, st);
     case KQ_TYPE_Q2_K: return launch_qgemv_m<T_Q2_K>(M, W, row_bytes, (int)N, (int)K, x, y, st);
     default: return launch_qgemv_m<T_Q8_0>(M, W, row_bytes, (int)N, (int)K, x, y, st);
+    }
+}
+
+int kq_qgemv_multi(int type, int count, const void *const *W, const int64_t *N, int64_t K, const float *x, int M,
+                   float *const *y, void *stream) {
+    if (count < 0) return KQ_ERR_ARG;
+    if (count == 0) return KQ_OK;
+    if (!W || !N || !y) return KQ_ERR_NULL;
+    int64_t row_bytes;
+    for (int i = 0; i < count; ++i) {
+        const int r = check_gemv_shape(type, N[i], K, &row_bytes);
+        if (r) return r;
+    }
+    if (M < 1 || M > 8) return KQ_ERR_M;
+    bool any = false;
+    for (int i = 0; i < count; ++i) {
+        if (N[i] == 0) continue;
+        any = true;
+        if (!W[i] || !y[i]) return KQ_ERR_NULL;
+        if (!aligned(W[i], 16) || !aligned(y[i], 16)) return KQ_ERR_ALIGN;
+    }
+    if (!any) return KQ_OK;
+    if (!x) return KQ_ERR_NULL;
+    if (!aligned(x, 16)) return KQ_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (M > 1) {
+        for (int i = 0; i < count; ++i) {
+            if (N[i] == 0) continue;
+            const int r = kq_qgemv(type, W[i], N[i], K, x, M, y[i], stream);
+            if (r) return r;
+        }
+        return KQ_OK;
+    }
+    switch (type) {
+    case KQ_TYPE_Q4_K: return launch_qgemv1_multi<T_Q4_K>(count, W, N, row_bytes, (int)K, x, y, st);
+    case KQ_TYPE_Q6_K: return launch_qgemv1_multi<T_Q6_K>(count, W, N, row_bytes, (int)K, x, y, st);
+    case KQ_TYPE_Q2_K: return launch_qgemv1_multi<T_Q2_K>(count, W, N, row_bytes, (int)K, x, y, st);
+    default: return launch_qgemv1_multi<T_Q8_0>(count, W, N, row_bytes, (int)K, x, y, st);
     }
 }
 

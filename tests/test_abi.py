@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
-                            "kq_dequant", "kq_qgemv", "kq_qmoe_workspace_bytes", "kq_qmoe_gemv"])
+                            "kq_dequant", "kq_qgemv", "kq_qgemv_multi", "kq_qmoe_workspace_bytes",
+                            "kq_qmoe_gemv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -84,6 +85,22 @@ def test_qgemv_argument_errors():
     assert _status(g, Q4, FAKE, 4, 256, ODD, 1, FAKE) == -5
     assert _status(g, Q4, FAKE, 4, 256, FAKE, 1, ODD) == -5
     assert _status(g, Q4, None, 0, 256, None, 1, None) == 0             # N == 0: nothing to do
+
+
+def test_qgemv_multi_argument_errors():
+    def g(qtype=Q4, Ws=(FAKE, FAKE), Ns=(4, 8), K=256, x=FAKE, M=1, ys=(FAKE, FAKE)):
+        return _status(kq.kq_qgemv_multi, qtype, list(Ws), list(Ns), K, x, M, list(ys))
+    assert g(qtype=99) == -1
+    assert g(K=100) == -2 and g(Ns=(4, -1)) == -2 and g(K=1 << 21) == -2
+    assert g(M=0) == -3 and g(M=9) == -3
+    assert g(Ws=(FAKE, None)) == -4 and g(ys=(None, FAKE)) == -4 and g(x=None) == -4
+    assert g(Ws=(FAKE, ODD)) == -5 and g(ys=(ODD, FAKE)) == -5 and g(x=ODD) == -5
+    assert g(Ws=(), Ns=(), ys=()) == 0                                  # count == 0
+    assert g(Ws=(None, None), Ns=(0, 0), ys=(None, None), x=None) == 0   # every matrix empty
+    assert g(Ws=(None, FAKE), Ns=(0, 8), ys=(None, ODD)) == -5          # empty ones are skipped
+    L = kq.lib()
+    assert L.kq_qgemv_multi(Q4, -1, None, None, 256, None, 1, None, None) == -6
+    assert L.kq_qgemv_multi(Q4, 2, None, None, 256, None, 1, None, None) == -4
 
 
 def test_dequant_argument_errors():

@@ -161,6 +161,62 @@ def test_qgemv_zero_weights_and_large_activations():
     assert np.all(y == 0)
 
 
+# ---- grouped launch: several matrices sharing x ------------------------------------
+
+MULTI = [
+    # (type, K, row counts): small K packs several rows per step (segment
+    # starts padded), more than 8 matrices take several launches, N = 0 is
+    # skipped, 2-byte-aligned Q6_K/Q8_0 rows
+    (kqsynth.Q4_K, 256, [7, 1, 5, 0, 13]),
+    (kqsynth.Q4_K, 1280, [3, 64, 9]),
+    (kqsynth.Q4_K, 4096, [37, 1, 130, 2, 5, 8, 3, 11, 4, 19]),
+    (kqsynth.Q6_K, 768, [9, 70, 1]),
+    (kqsynth.Q6_K, 12544, [30, 7, 12]),
+    (kqsynth.Q2_K, 2048, [33, 300, 1]),
+    (kqsynth.Q8_0, 1184, [9, 17, 4]),
+    (kqsynth.Q8_0, 4096, [37, 5]),
+]
+
+
+@pytest.mark.parametrize("case", MULTI, ids=lambda c: "%s-K%d-%d" % (kqsynth.TYPE_NAMES[c[0]], c[1], len(c[2])))
+@pytest.mark.parametrize("M", [1, 3])
+def test_qgemv_multi_equals_separate_calls(case, M):
+    qtype, K, Ns = case
+    say("qgemv_multi", kqsynth.TYPE_NAMES[qtype], "K", K, "Ns", Ns, "M", M)
+    Ws = [qmat(qtype, max(n, 1), K, 40 + i)[:n] for i, n in enumerate(Ns)]
+    x = kqsynth.activations(M, K, kqsynth.rng_for(41, M, K))
+    Wd = [dev(w) if n else None for w, n in zip(Ws, Ns)]
+    ys = [torch.full((M, n), float("nan"), device="cuda") if n else None for n in Ns]
+    kq.kq_qgemv_multi(qtype, Wd, Ns, K, dev(x), M, ys)
+    torch.cuda.synchronize()
+    for i, n in enumerate(Ns):
+        if n == 0:
+            continue
+        got = ys[i].cpu().numpy()
+        one = gpu_gemv(qtype, Wd[i], n, K, x)
+        assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), i
+        yo, S = oracle.gemv(qtype, Ws[i], n, K, x)
+        check_close(got, yo, S, "matrix %d" % i)
+
+
+def test_qgemv_multi_full_size_projections():
+    # a 70B layer's k and q projections (Q4_K, K = 8192) in one launch
+    K = 8192
+    Ns = [1024, 8192]
+    Ws = [kqsynth.device_matrix(kqsynth.Q4_K, n, K, seed=60 + i, device="cuda") for i, n in enumerate(Ns)]
+    x = kqsynth.activations(1, K, kqsynth.rng_for(61))
+    ys = [torch.empty((1, n), device="cuda") for n in Ns]
+    kq.kq_qgemv_multi(kqsynth.Q4_K, Ws, Ns, K, dev(x), 1, ys)
+    torch.cuda.synchronize()
+    for i, n in enumerate(Ns):
+        one = gpu_gemv(kqsynth.Q4_K, Ws[i], n, K, x)
+        assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), one.view(np.uint32)), i
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).integers(0, n, 30)]))
+        Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(kqsynth.Q4_K, Wr, len(rows), K, x)
+        check_close(ys[i].cpu().numpy()[:, rows], yo, S, "matrix %d" % i)
+
+
 # ---- full-size shapes, sampled rows -----------------------------------------------
 
 FULL = [
@@ -169,6 +225,7 @@ FULL = [
     ("70B wk", kqsynth.Q4_K, 1024, 8192),
     ("70B w1 Q2_K", kqsynth.Q2_K, 28672, 8192),
     ("70B w2 Q8_0", kqsynth.Q8_0, 8192, 28672),
+    ("Q6_K K=40960", kqsynth.Q6_K, 3000, 40960),
 ]
 
 
