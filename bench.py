@@ -50,6 +50,13 @@ def parse():
     ap.add_argument("--no-group", action="store_true",
                     help="one launch per matrix (no grouped calls for matrices sharing an input)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the warmup (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter_collection.csv files of a FETCH_SIZE pass and a "
+                         "WRITE_SIZE pass (both run with --copy-calibration) into profiles/traffic_<workload>.json")
+    ap.add_argument("--pmc-command", default="", help="with --summarize-pmc: the command the passes ran")
     return ap.parse_args()
 
 
@@ -67,8 +74,61 @@ def source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+CALIB_BYTES = 1 << 30
+DOMINANT_KERNEL = "qgemv1_kernel<12,"      # Q4_K batch-1 instantiations
+
+
+def pmc_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, value)} for one counter of a counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(args):
+    """Traffic of the dominant kernel from a FETCH_SIZE and a WRITE_SIZE pass.
+    Each counter is calibrated on the 1 GiB copy the passes ran first: the
+    factor is 1 GiB over what the counter read for it."""
+    result = {"kernel": "qgemv1_kernel Q4_K (M=1)", "kernel_source_sha256_16": source_hash(),
+              "workload": args.workload, "command": args.pmc_command}
+    per = {}
+    for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),
+                               ("write", args.summarize_pmc[1], "WRITE_SIZE")):
+        d = pmc_per_dispatch(path, counter)
+        copies = [v for (n, v) in d.values() if "copy" in n]
+        if not copies:
+            raise SystemExit("no copy kernel in %s: run the pass with --copy-calibration" % path)
+        ref = max(copies)                              # the 1 GiB copy is the largest one
+        factor = CALIB_BYTES / (ref * 1024.0)
+        dom = [v for (n, v) in d.values() if DOMINANT_KERNEL in n.replace(" ", "")]
+        if not dom:
+            raise SystemExit("no dominant-kernel dispatch in %s" % path)
+        per[key] = sum(dom) / len(dom) * 1024.0 * factor
+        result["%s_kib_copy_1gib" % key] = round(ref, 1)
+        result["%s_factor" % key] = round(factor, 4)
+        result["%s_bytes_per_launch" % key] = int(per[key])
+        result["%s_dispatches" % key] = len(dom)
+    result["bytes_per_launch"] = int(per["fetch"] + per["write"])
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "traffic_%s.json" % args.workload)
+    with open(out, "w") as f:
+        json.dump(result, f, indent=1)
+        f.write("\n")
+    print(json.dumps(result))
+    return 0
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on exactly one GPU (no collectives, no sharding); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -207,40 +267,33 @@ def main():
     torch.cuda.synchronize()
     step_bytes = sum(b for (_, b, _) in launches)
 
-    # Events bracket each contiguous run of dominant launches.  An event
-    # record between two launches costs the stream a few microseconds, so the
-    # headline value comes from a pass with events only at its ends, and the
-    # dominant kernel's duration from a second pass of the same steps with
-    # the bracketing events (created before that pass starts).
-    runs = []
-    cur = None
-    for i, (_, _, dom) in enumerate(launches):
-        if dom and cur is None:
-            cur = [i, i]
-        if dom:
-            cur[1] = i + 1
-        if not dom and cur is not None:
-            runs.append(tuple(cur))
-            cur = None
-    if cur is not None:
-        runs.append(tuple(cur))
-    run_at = {a: b for (a, b) in runs}
+    def run_step():
+        for (fn, _, _) in launches:
+            fn()
 
-    def run_step(ev=None):
-        i = 0
-        while i < len(launches):
-            if ev is not None and i in run_at:
-                a, b = next(ev)
-                a.record(stream)
-                for (fn, _, _) in launches[i:run_at[i]]:
-                    fn()
-                b.record(stream)
-                i = run_at[i]
-                continue
+    # The dominant kernel's duration comes from a second pass of the same
+    # steps in which each step issues its dominant launches first, as one
+    # contiguous run between two events, and then the others: an event record
+    # costs the stream a few microseconds, which one bracket per step spreads
+    # over all of the step's dominant launches.
+    dominant_idx = [i for i, (_, _, d) in enumerate(launches) if d]
+    other_idx = [i for i, (_, _, d) in enumerate(launches) if not d]
+
+    def run_step_bracketed(a, b):
+        a.record(stream)
+        for i in dominant_idx:
             launches[i][0]()
-            i += 1
+        b.record(stream)
+        for i in other_idx:
+            launches[i][0]()
 
     log("inputs resident: %.2f GB of packed weights per step, %d launches" % (step_bytes / 1e9, len(launches)))
+    if args.copy_calibration:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -261,13 +314,12 @@ def main():
     ms_per_step = ms_total / args.steps
     gbs = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
 
-    # ---- roofline pass: the same steps, events around each dominant run
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), b - a)
-             for _ in range(args.steps) for (a, b) in runs]
-    ev = iter([(a, b) for (a, b, _) in pairs])
+    # ---- roofline pass: the same steps, dominant launches bracketed
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), len(dominant_idx))
+             for _ in range(args.steps)]
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        run_step(ev)
+    for (a, b, _) in pairs:
+        run_step_bracketed(a, b)
     torch.cuda.synchronize()
     dom_ms = sum(a.elapsed_time(b) for (a, b, _) in pairs)
     dom_n = sum(n for (_, _, n) in pairs)
@@ -314,7 +366,7 @@ def main():
             "avg_launch_us": round(dom_avg_us, 3),
             "algorithmic_bytes_per_launch": int(dom_bytes_per_launch),
             "launches_timed": dom_n,
-            "timing": "HIP events around each run of dominant launches, in a second pass of the same steps",
+            "timing": "HIP events around each step's dominant launches, issued as one run in a second pass of the same steps",
         },
     }
 
