@@ -122,6 +122,101 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
     return v;
 }
 
+// group_sum of N values at once, level by level, so that no DPP read waits on
+// the instruction just before it; each value gets exactly group_sum's tree.
+template <int N> __device__ __forceinline__ void group_sum_n(float (&v)[N], int lpr) {
+#pragma unroll
+    for (int lv = 0; lv < 4; ++lv)
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = dpp_add(v[i], lv);
+    if (lpr >= 32) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32 b = __builtin_bit_cast(u32, v[i]);
+            const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+            v[i] = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+        }
+    }
+    if (lpr >= 64) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32 b = __builtin_bit_cast(u32, v[i]);
+            const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+            v[i] = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+        }
+    }
+}
+
+// group_sum of NV values (a power of two, at most 16) in one pass: a
+// butterfly that at each of the first log2(NV) levels halves the values a lane
+// holds -- it keeps one half, hands the other to its partner and adds the
+// partner's copy of the half it kept -- then sums the last value like
+// group_sum.  Every lane ends with the total of value scatter_idx(lane); the
+// pairs added at every level are those of group_sum's tree, so each total has
+// group_sum's bits.  Lane l keeps the upper half at level k iff bit k of
+//   (bit0^bit2, bit1^bit2, bit2^bit3, bit3)
+// is set: partners at each level differ in that bit and agree in the earlier
+// ones (the partners are l^1, l^2, then the mirrors 7-j and 15-j in 8- and
+// 16-lane rows).
+__device__ __forceinline__ int scatter_bit(int lane, int k) {
+    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+    return k == 0 ? (b0 ^ b2) : k == 1 ? (b1 ^ b2) : k == 2 ? (b2 ^ b3) : b3;
+}
+template <int NV> __device__ __forceinline__ int scatter_idx(int lane) {
+    int idx = 0, h = NV;
+#pragma unroll
+    for (int k = 0; (1 << k) < NV; ++k) {
+        h >>= 1;
+        idx += scatter_bit(lane, k) * h;
+    }
+    return idx;
+}
+__device__ __forceinline__ float dpp_get(float v, int lvl) {
+    const int iv = __builtin_bit_cast(int, v);
+    int t;
+    switch (lvl) {
+    case 0: t = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false); break;
+    case 1: t = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false); break;
+    case 2: t = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xF, 0xF, false); break;
+    default: t = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(float, t);
+}
+template <int NV> __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int lane, int lpr) {
+    static_assert(NV >= 1 && NV <= 16 && (NV & (NV - 1)) == 0, "NV: power of two <= 16");
+    int n = NV;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (n > 1) {
+            const bool up = scatter_bit(lane, k);
+            const int h = n >> 1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < h) {
+                    const float keep = up ? v[j + h] : v[j];
+                    const float send = up ? v[j] : v[j + h];
+                    v[j] = keep + dpp_get(send, k);
+                }
+            }
+            n = h;
+        } else {
+            v[0] = dpp_add(v[0], k);
+        }
+    }
+    float r = v[0];
+    if (lpr >= 32) {
+        const u32 b = __builtin_bit_cast(u32, r);
+        const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        r = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+    }
+    if (lpr >= 64) {
+        const u32 b = __builtin_bit_cast(u32, r);
+        const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        r = __builtin_bit_cast(float, (u32)p[0]) + __builtin_bit_cast(float, (u32)p[1]);
+    }
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // Activation access.  A unit's activations are addressed by their offset from
 // the unit's first weight in the unit's own coordinates (Q4_K: 0..63, one
@@ -138,6 +233,7 @@ __device__ __forceinline__ float sum16(f4 a, f4 b, f4 c, f4 d) {
 // Activations of a staged K chunk in LDS: row m at xs + m * XS (16 B of padding
 // every 64 floats, see xpad), 16-sums at ss + m * SS.  xo / so locate the unit.
 struct XLds {
+    static constexpr bool FENCE = true;
     const float *xs, *ss;
     int XS, SS, xo, so, srun;
     __device__ __forceinline__ f4 x4(int m, int off) const { return lds4(xs + m * XS + xo + xpad(off)); }
@@ -146,6 +242,7 @@ struct XLds {
 
 // One activation row of one unit held in registers (M = 1 kernels).
 template <int T> struct XReg {
+    static constexpr bool FENCE = false;
     static constexpr bool RUNS32 = (T == T_Q6_K || T == T_Q2_K);
     static constexpr int NV = (T == T_Q8_0) ? 8 : 16, NS = NV / 4;
     f4 v[NV];
@@ -177,6 +274,30 @@ template <int T> struct XReg {
 //   v  = aq * 2^24 - KM * am
 // where KM folds a constant quant offset (Q6_K: 32; Q8_0: 128, from reading
 // the int8 quants as q + 128).
+
+// With activations in LDS and several activation rows, the compiler would
+// otherwise read every row's activations of a unit up front and run out of
+// registers: the val_* loops below read one activation row at a time, one step
+// ahead of its use, and pin each step's accumulators with an empty asm
+// statement that also orders memory accesses, which keeps the step's
+// arithmetic and reads in program order.  Register-resident activations need
+// no pinning.
+template <class XA, int M> __device__ __forceinline__ void pin(float &v) {
+    if constexpr (XA::FENCE && M > 1) asm volatile("" : "+v"(v) : : "memory");
+}
+
+// acc + w * x for one fp16 half of w (HI: the upper one), widened exactly
+// (one rounding: the compiler emits v_fma_mix_f32, or converts the half once
+// and reuses it with v_fmac_f32 across activation rows).
+template <class XA, int M, bool HI> __device__ __forceinline__ float fmx(hf2 w, float x, float acc) {
+    return __builtin_fmaf((float)(HI ? w.y : w.x), x, acc);
+}
+
+// Reads of the activations of step t (NV float4 each) kept XP steps ahead of
+// their use in a small register ring; register-resident activations are read
+// at their use (XP = 0).
+constexpr int XPREF = 2;
+template <class XA, int M> constexpr int xpref() { return (XA::FENCE && M > 1) ? XPREF : 0; }
 
 // ---- Q4_K: unit (block b, group g) = quant bytes 32g..32g+31, i.e. weights
 // 64g..64g+31 (low nibbles, sub-block 2g) and 64g+32..64g+63 (high nibbles,
@@ -212,34 +333,60 @@ __device__ __forceinline__ void val_unit(const RawQ4K (&raw)[R], int g, const XA
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) slo[r][m] = shi[r][m] = 0.f;
+    // step t = (i, m) reads x[4i .. 4i+3] and x[32+4i .. 32+4i+3] of row m
+    constexpr int XP = xpref<XA, M>(), NT = 8 * M;
+    f4 xb[XP + 1][2];
+    auto fetch = [&](int t) {
+        const int i = t / M, m = t % M;
+        xb[t % (XP + 1)][0] = xa.x4(m, 4 * i);
+        xb[t % (XP + 1)][1] = xa.x4(m, 32 + 4 * i);
+    };
+#pragma unroll
+    for (int t = 0; t < XP; ++t)
+        if (t < NT) fetch(t);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        f4 xl[M], xh[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            xl[m] = xa.x4(m, 4 * i);
-            xh[m] = xa.x4(m, 32 + 4 * i);
-        }
+        hf2 a[R], b[R], c[R], e[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 D = i < 4 ? raw[r].qa[i & 3] : raw[r].qb[i & 3];
             const u32 D8 = D >> 8;
-            const hf2 a = as_h2(D & 0x000F000Fu), b = as_h2(D8 & 0x000F000Fu);
-            const hf2 c = as_h2(D & 0x00F000F0u), e = as_h2(D8 & 0x00F000F0u);
+            a[r] = as_h2(D & 0x000F000Fu);
+            b[r] = as_h2(D8 & 0x000F000Fu);
+            c[r] = as_h2(D & 0x00F000F0u);
+            e[r] = as_h2(D8 & 0x00F000F0u);
+        }
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s = slo[r][m];
-                s = __builtin_fmaf((float)a.x, xl[m].x, s);
-                s = __builtin_fmaf((float)b.x, xl[m].y, s);
-                s = __builtin_fmaf((float)a.y, xl[m].z, s);
-                s = __builtin_fmaf((float)b.y, xl[m].w, s);
-                slo[r][m] = s;
-                float t = shi[r][m];
-                t = __builtin_fmaf((float)c.x, xh[m].x, t);
-                t = __builtin_fmaf((float)e.x, xh[m].y, t);
-                t = __builtin_fmaf((float)c.y, xh[m].z, t);
-                t = __builtin_fmaf((float)e.y, xh[m].w, t);
-                shi[r][m] = t;
+        for (int m = 0; m < M; ++m) {
+            const int t = i * M + m;
+            if (t + XP < NT) fetch(t + XP);
+            const f4 cl = xb[t % (XP + 1)][0], ch = xb[t % (XP + 1)][1];
+            // the 2R chains of the step advance together (independent FMAs
+            // back to back); each chain keeps its own order
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                slo[r][m] = fmx<XA, M, false>(a[r], cl.x, slo[r][m]);
+                shi[r][m] = fmx<XA, M, false>(c[r], ch.x, shi[r][m]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                slo[r][m] = fmx<XA, M, false>(b[r], cl.y, slo[r][m]);
+                shi[r][m] = fmx<XA, M, false>(e[r], ch.y, shi[r][m]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                slo[r][m] = fmx<XA, M, true>(a[r], cl.z, slo[r][m]);
+                shi[r][m] = fmx<XA, M, true>(c[r], ch.z, shi[r][m]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                slo[r][m] = fmx<XA, M, true>(b[r], cl.w, slo[r][m]);
+                shi[r][m] = fmx<XA, M, true>(e[r], ch.w, shi[r][m]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                pin<XA, M>(slo[r][m]);
+                pin<XA, M>(shi[r][m]);
             }
         }
     }
@@ -322,38 +469,59 @@ __device__ __forceinline__ void val_unit(const RawQ6K (&rawu)[R], int sub, const
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int g = 0; g < 4; ++g) acc[r][m][g] = 0.f;
+    // step t = (k, m) reads run g at x[32g + 4k .. 32g + 4k + 3] of row m
+    constexpr int XP = xpref<XA, M>(), NT = 4 * M;
+    f4 xb[XP + 1][4];
+    auto fetch = [&](int t) {
+        const int k = t / M, m = t % M;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) xb[t % (XP + 1)][g] = xa.x4(m, 32 * g + 4 * k);
+    };
+#pragma unroll
+    for (int t = 0; t < XP; ++t)
+        if (t < NT) fetch(t);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        f4 xv[M][4];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) xv[m][g] = xa.x4(m, 32 * g + 4 * k);
+        hf2 w[R][4][2];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 A = raw[r].a[k], B = raw[r].b[k], H = raw[r].hq[k];
             const u32 A8 = A >> 8, B8 = B >> 8;
             const u32 H4l = H << 4, H4r = H >> 4, H2l = H << 2, H6r = H >> 6;
-            hf2 w[4][2];
-            w[0][0] = as_h2((A & 0x000F000Fu) | (H4l & 0x00300030u));
-            w[0][1] = as_h2((A8 & 0x000F000Fu) | (H4r & 0x00300030u));
-            w[1][0] = as_h2((B & 0x000F000Fu) | (H2l & 0x00300030u));
-            w[1][1] = as_h2((B8 & 0x000F000Fu) | (H6r & 0x00300030u));
-            w[2][0] = as_h2((A & 0x00F000F0u) | (H4l & 0x03000300u));
-            w[2][1] = as_h2((A8 & 0x00F000F0u) | (H4r & 0x03000300u));
-            w[3][0] = as_h2((B & 0x00F000F0u) | (H2l & 0x03000300u));
-            w[3][1] = as_h2((B8 & 0x00F000F0u) | (H6r & 0x03000300u));
+            w[r][0][0] = as_h2((A & 0x000F000Fu) | (H4l & 0x00300030u));
+            w[r][0][1] = as_h2((A8 & 0x000F000Fu) | (H4r & 0x00300030u));
+            w[r][1][0] = as_h2((B & 0x000F000Fu) | (H2l & 0x00300030u));
+            w[r][1][1] = as_h2((B8 & 0x000F000Fu) | (H6r & 0x00300030u));
+            w[r][2][0] = as_h2((A & 0x00F000F0u) | (H4l & 0x03000300u));
+            w[r][2][1] = as_h2((A8 & 0x00F000F0u) | (H4r & 0x03000300u));
+            w[r][3][0] = as_h2((B & 0x00F000F0u) | (H2l & 0x03000300u));
+            w[r][3][1] = as_h2((B8 & 0x00F000F0u) | (H6r & 0x03000300u));
+        }
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m) {
+            const int t = k * M + m;
+            if (t + XP < NT) fetch(t + XP);
+            const f4 *xv = xb[t % (XP + 1)];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float s = acc[r][m][g];
-                    s = __builtin_fmaf((float)w[g][0].x, xv[m][g].x, s);
-                    s = __builtin_fmaf((float)w[g][1].x, xv[m][g].y, s);
-                    s = __builtin_fmaf((float)w[g][0].y, xv[m][g].z, s);
-                    s = __builtin_fmaf((float)w[g][1].y, xv[m][g].w, s);
-                    acc[r][m][g] = s;
-                }
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[r][m][g] = fmx<XA, M, false>(w[r][g][0], xv[g].x, acc[r][m][g]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[r][m][g] = fmx<XA, M, false>(w[r][g][1], xv[g].y, acc[r][m][g]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[r][m][g] = fmx<XA, M, true>(w[r][g][0], xv[g].z, acc[r][m][g]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[r][m][g] = fmx<XA, M, true>(w[r][g][1], xv[g].w, acc[r][m][g]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) pin<XA, M>(acc[r][m][g]);
         }
     }
 #pragma unroll
@@ -410,30 +578,55 @@ __device__ __forceinline__ void val_unit(const RawQ2K (&raw)[R], int sub, const 
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc[r][m][s] = 0.f;
+    // step t = (k, m) reads run s at x[32s + 4k .. 32s + 4k + 3] of row m
+    constexpr int XP = xpref<XA, M>(), NT = 4 * M;
+    f4 xb[XP + 1][4];
+    auto fetch = [&](int t) {
+        const int k = t / M, m = t % M;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xb[t % (XP + 1)][s] = xa.x4(m, 32 * s + 4 * k);
+    };
+#pragma unroll
+    for (int t = 0; t < XP; ++t)
+        if (t < NT) fetch(t);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        f4 xv[M][4];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xv[m][s] = xa.x4(m, 32 * s + 4 * k);
+        hf2 we[R][4], wo[R][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 D = raw[r].q[k], D8 = D >> 8;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32 mask = 0x00030003u << (2 * s);
-                const hf2 we = as_h2(D & mask), wo = as_h2(D8 & mask);
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float t = acc[r][m][s];
-                    t = __builtin_fmaf((float)we.x, xv[m][s].x, t);
-                    t = __builtin_fmaf((float)wo.x, xv[m][s].y, t);
-                    t = __builtin_fmaf((float)we.y, xv[m][s].z, t);
-                    t = __builtin_fmaf((float)wo.y, xv[m][s].w, t);
-                    acc[r][m][s] = t;
-                }
+                we[r][s] = as_h2(D & mask);
+                wo[r][s] = as_h2(D8 & mask);
             }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int t = k * M + m;
+            if (t + XP < NT) fetch(t + XP);
+            const f4 *xv = xb[t % (XP + 1)];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[r][m][s] = fmx<XA, M, false>(we[r][s], xv[s].x, acc[r][m][s]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[r][m][s] = fmx<XA, M, false>(wo[r][s], xv[s].y, acc[r][m][s]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[r][m][s] = fmx<XA, M, true>(we[r][s], xv[s].z, acc[r][m][s]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[r][m][s] = fmx<XA, M, true>(wo[r][s], xv[s].w, acc[r][m][s]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) pin<XA, M>(acc[r][m][s]);
         }
     }
 #pragma unroll
@@ -488,24 +681,37 @@ __device__ __forceinline__ void val_unit(const RawQ80 (&rawu)[R], int, const XA 
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+    // step t = (i, m) reads x[4i .. 4i+3] of row m
+    constexpr int XP = xpref<XA, M>(), NT = 8 * M;
+    f4 xb[XP + 1];
+    auto fetch = [&](int t) { xb[t % (XP + 1)] = xa.x4(t % M, 4 * (t / M)); };
+#pragma unroll
+    for (int t = 0; t < XP; ++t)
+        if (t < NT) fetch(t);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        f4 xv[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = xa.x4(m, 4 * i);
+        hf2 we[R], wo[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const u32 U = raw[r].q[i] ^ 0x80808080u;
-            const hf2 we = as_h2(U & 0x00FF00FFu), wo = as_h2((U >> 8) & 0x00FF00FFu);
+            we[r] = as_h2(U & 0x00FF00FFu);
+            wo[r] = as_h2((U >> 8) & 0x00FF00FFu);
+        }
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float t = acc[r][m];
-                t = __builtin_fmaf((float)we.x, xv[m].x, t);
-                t = __builtin_fmaf((float)wo.x, xv[m].y, t);
-                t = __builtin_fmaf((float)we.y, xv[m].z, t);
-                t = __builtin_fmaf((float)wo.y, xv[m].w, t);
-                acc[r][m] = t;
-            }
+        for (int m = 0; m < M; ++m) {
+            const int t = i * M + m;
+            if (t + XP < NT) fetch(t + XP);
+            const f4 cx = xb[t % (XP + 1)];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = fmx<XA, M, false>(we[r], cx.x, acc[r][m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = fmx<XA, M, false>(wo[r], cx.y, acc[r][m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = fmx<XA, M, true>(we[r], cx.z, acc[r][m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = fmx<XA, M, true>(wo[r], cx.w, acc[r][m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) pin<XA, M>(acc[r][m]);
         }
     }
 #pragma unroll
@@ -862,6 +1068,163 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
         flush1<MS>(keep, wsteps & ~(lpr - 1), wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
 }
 
+// Batch-M kernel (2 <= M <= 8).  Persistent work-groups of NW waves, one per
+// compute unit.  Rows are dealt out in row steps of RG = R * G rows (G lane
+// groups of LPR lanes per wave, R rows per group, so one read of a unit's
+// activations from LDS serves R rows).  The activations of M rows are staged
+// per K chunk (a multiple of 4096 columns, so stripes never straddle chunks);
+// for each chunk a wave walks its row steps and, within a step, the chunk's
+// stripes in order.  The running row sums live in LDS across chunks and take
+// the stripe sums in ascending order, so every output gets the M = 1 bits.
+// The weight loads run D items ahead through a register ring that does not
+// stop at chunk boundaries (the loads do not depend on the activations).
+template <bool MS> __device__ __forceinline__ float *out_m(const Segs &sg, int N, int row, int m) {
+    if (row >= N) return nullptr;
+    const int s = seg_of<MS>(sg, row);
+    const int local = row - sg.start[s];
+    return local < sg.rows[s] ? sg.y[s] + (int64_t)m * sg.rows[s] + local : nullptr;
+}
+
+template <int T, int R, bool MS>
+__device__ __forceinline__ void issue_rows(typename RawOf<T>::type (&raw)[R], const Segs &sg, int64_t row_bytes,
+                                           int N, int RG, int row0, bool live, int grp, bool act, u32 boff,
+                                           int sub) {
+    const int sgi = seg_of<MS>(sg, row0 < N ? row0 : 0);
+    const int local = row0 - sg.start[sgi];
+    const int left = sg.rows[sgi] - local;
+    const int nr = (!live || row0 >= N || left <= 0) ? 0 : (left < RG ? left : RG);
+    const uintptr_t ta = (uintptr_t)(sg.W[sgi] + (int64_t)(nr ? local : 0) * row_bytes);
+    const u32 delta = (u32)(ta & 3u);
+    const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int rr = grp * R + r;
+        load_unit(raw[r], rs, (act && rr < nr) ? delta + (u32)((int64_t)rr * row_bytes) + boff : OOB, sub);
+    }
+}
+
+template <int T, int M, int R, int D, bool MS>
+__global__ __launch_bounds__(512) void qgemvm_kernel(const Segs sg, int64_t row_bytes, int K, int KC, int lpr,
+                                                     const float *__restrict__ x) {
+    typedef Fmt<T> F;
+    typedef typename RawOf<T>::type Raw;
+    const int N = sg.start[sg.n];
+    extern __shared__ float smem[];
+    const int NW = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int G = 64 / lpr, grp = lane / lpr, slot = lane - grp * lpr;
+    const int RG = R * G;
+    const int XS = x_stride(KC), SS = s_stride(KC);
+    float *xs = smem, *ss = smem + M * XS, *accl = ss + M * SS;
+    const int nsteps = (N + RG - 1) / RG;
+    const int per_round = gridDim.x * NW;
+    const int f0 = blockIdx.x * NW;
+    const int wsteps = f0 < nsteps ? (nsteps - f0 + per_round - 1) / per_round : 0;
+    if (wsteps == 0) return;                       // uniform over the work-group
+    const int nchunks = (K + KC - 1) / KC;
+    const int ub_chunk = (KC / F::QK) * F::UPB;    // units per full chunk
+    const int units_last = ((K - (nchunks - 1) * KC) / F::QK) * F::UPB;
+    const int ns_full = (ub_chunk + lpr - 1) / lpr, ns_last = (units_last + lpr - 1) / lpr;
+    const int total = wsteps * (ns_full * (nchunks - 1) + ns_last);
+    const int sub = slot % F::UPB;
+    const int accn = wsteps * NW * RG * M;
+    for (int i = threadIdx.x; i < accn; i += blockDim.x) accl[i] = 0.f;
+    const float *xr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xr[m] = x + (int64_t)m * K;
+
+    // item cursors (chunk c, row step j, stripe s): one for issue, one for use
+    int ic = 0, ij = 0, is = 0, ins = nchunks > 1 ? ns_full : ns_last;
+    int cc = 0, cj = 0, cs = 0, cns = ins;
+    auto step = [&](int &c, int &j, int &st, int &ns) {
+        if (++st == ns) {
+            st = 0;
+            if (++j == wsteps) {
+                j = 0;
+                ++c;
+                ns = c < nchunks - 1 ? ns_full : ns_last;
+            }
+        }
+    };
+    auto issue = [&](Raw (&raw)[R], int c, int j, int st) {
+        const int ul = st * lpr + slot;
+        const int uc_n = c < nchunks - 1 ? ub_chunk : units_last;
+        const bool act = ul < uc_n;
+        const int ug = c * ub_chunk + (act ? ul : 0);
+        const u32 boff = (u32)(ug / F::UPB) * F::BYTES;
+        const int row0 = ((j * gridDim.x + blockIdx.x) * NW + wave) * RG;
+        issue_rows<T, R, MS>(raw, sg, row_bytes, N, RG, row0, c < nchunks, grp, act, boff, sub);
+    };
+
+    Raw ring[D][R];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        issue(ring[d], ic, ij, is);
+        step(ic, ij, is, ins);
+    }
+
+    // row sums: each lane carries the running sum of index idx = r * M + m
+    // (the butterfly's output slot), for rows grp * R + r of the step
+    constexpr int RM = R * M, NV = RM <= 4 ? 4 : (RM <= 8 ? 8 : 16);
+    static_assert(RM <= 16, "butterfly row sums hold at most 16 values");
+    const int idx = scatter_idx<NV>(lane);
+    float t = 0.f;
+    auto use = [&](const Raw (&raw)[R]) {
+        if (cj == 0 && cs == 0) {                  // first item of chunk cc: stage its activations
+            if (cc) __syncthreads();
+            const int kc = cc < nchunks - 1 ? KC : K - cc * KC;
+            stage_x<M>(xs, ss, XS, SS, xr, cc * KC, kc, blockDim.x);
+            __syncthreads();
+        }
+        float *acc = accl + ((cj * NW + wave) * RG + grp * R) * M;
+        if (cs == 0) t = idx < RM ? acc[idx] : 0.f;
+        const int ul = cs * lpr + slot;
+        const bool act = ul < (cc < nchunks - 1 ? ub_chunk : units_last);
+        const int e0 = unit_e0<T>(act ? ul : 0);
+        const XLds xa{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+        float v[R][M], g[NV];
+        val_unit<M, R>(raw, sub, xa, v);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) g[i] = (i < RM && act) ? v[i / M][i % M] : 0.f;
+        float S;
+        if constexpr (NV <= 8) {
+            // up to 8 values: plain sums side by side (measured faster than
+            // the butterfly there), then this lane's index
+            group_sum_n<NV>(g, lpr);
+            S = g[0];
+#pragma unroll
+            for (int i = 1; i < NV; ++i) S = idx == i ? g[i] : S;
+        } else {
+            S = reduce_scatter<NV>(g, lane, lpr);
+        }
+        t = t + S;
+        if (cs == cns - 1 && idx < RM) acc[idx] = t;   // lanes holding one index store the same value
+        step(cc, cj, cs, cns);
+    };
+
+    int it = 0;
+    for (; it + D <= total; it += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            use(ring[d]);
+            issue(ring[d], ic, ij, is);
+            step(ic, ij, is, ins);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (it + d < total) use(ring[d]);
+
+    __syncthreads();
+    for (int i = threadIdx.x; i < accn; i += blockDim.x) {
+        const int m = i % M, rest = i / M;
+        const int tt = rest % RG, q = rest / RG;
+        const int w = q % NW, j = q / NW;
+        float *o = out_m<MS>(sg, N, ((j * gridDim.x + blockIdx.x) * NW + w) * RG + tt, m);
+        if (o) *o = accl[i];
+    }
+}
+
 // Routed experts: work-group (row tile, slot s).  Only the lowest slot that
 // routes to an expert does the work; it collects every slot that routes to the
 // same expert and serves them in batches of up to MAXM activation rows with one
@@ -1214,20 +1577,73 @@ int launch_qgemv1_multi(int count, const void *const *W, const int64_t *N, int64
     return KQ_OK;
 }
 
+// Batch-M configuration: rows per lane group (R: each activation read from
+// LDS serves R rows) and ring depth (D) per format and M, chosen by
+// measurement among the settings that fit the 256-VGPR budget of 8-wave
+// work-groups without spilling.  R = 2 keeps R * M <= 16 for the butterfly
+// row sums.
+template <int T, int M> constexpr int MROWS() { return 2; }
+template <int T, int M> constexpr int MRING() { return (T == T_Q6_K && M > 4) ? 1 : 2; }
+constexpr size_t LDS_MAX = 160 * 1024;
+
+// Batch-M launch over one or more segments (starts padded to the row step).
+// Returns KQ_ERR_ARG when the activations of one 4096-column chunk do not fit
+// in LDS next to the row sums (then the caller uses the LDS kernel).
+template <int T, int M>
+int launch_qgemvm(const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    constexpr int R = MROWS<T, M>(), D = MRING<T, M>(), NW = 8;
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int RG = R * (64 / lpr);
+    const int N = sg.start[sg.n];
+    const int64_t nsteps = ((int64_t)N + RG - 1) / RG;
+    const int64_t need = (nsteps + NW - 1) / NW;
+    const int64_t cap = cu_count();
+    const int grid = (int)(need < cap ? need : cap);
+    if (grid == 0) return KQ_OK;
+    const int64_t wsteps = (nsteps + (int64_t)grid * NW - 1) / ((int64_t)grid * NW);
+    const size_t acc = (size_t)wsteps * NW * RG * M * sizeof(float);
+    auto bytes = [&](int kc) { return (size_t)M * (x_stride(kc) + s_stride(kc)) * sizeof(float) + acc; };
+    int KC = K;
+    if (bytes(K) > LDS_MAX) {
+        KC = (K / 4096) * 4096;
+        while (KC > 4096 && bytes(KC) > LDS_MAX) KC -= 4096;
+        if (KC < 4096 || bytes(KC) > LDS_MAX) return KQ_ERR_ARG;
+    }
+    const size_t lds = bytes(KC);
+    auto kern = sg.n > 1 ? qgemvm_kernel<T, M, R, D, true> : qgemvm_kernel<T, M, R, D, false>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, sg, row_bytes, K, KC, lpr, x);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+template <int T, int M>
+int launch_qgemvm_single(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
+    Segs sg = {};
+    sg.W[0] = (const uint8_t *)W;
+    sg.y[0] = y;
+    sg.start[0] = 0;
+    sg.start[1] = N;
+    sg.rows[0] = N;
+    sg.n = 1;
+    const int r = launch_qgemvm<T, M>(sg, row_bytes, K, x, st);
+    if (r != KQ_ERR_ARG) return r;
+    const int lpr = lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB);
+    return launch_qgemv_t<T, M, 1>(W, row_bytes, N, K, x, y, st, lpr);
+}
+
 template <int T>
 int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const float *x, float *y,
                    hipStream_t st) {
-    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
-    const int lpr = lanes_per_row(units);
     switch (M) {
     case 1: return launch_qgemv1_single<T>(W, row_bytes, N, K, x, y, st);
-    case 2: return launch_qgemv_t<T, 2, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    case 3: return launch_qgemv_t<T, 3, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    case 4: return launch_qgemv_t<T, 4, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    case 5: return launch_qgemv_t<T, 5, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    case 6: return launch_qgemv_t<T, 6, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    case 7: return launch_qgemv_t<T, 7, 1>(W, row_bytes, N, K, x, y, st, lpr);
-    default: return launch_qgemv_t<T, 8, 1>(W, row_bytes, N, K, x, y, st, lpr);
+    case 2: return launch_qgemvm_single<T, 2>(W, row_bytes, N, K, x, y, st);
+    case 3: return launch_qgemvm_single<T, 3>(W, row_bytes, N, K, x, y, st);
+    case 4: return launch_qgemvm_single<T, 4>(W, row_bytes, N, K, x, y, st);
+    case 5: return launch_qgemvm_single<T, 5>(W, row_bytes, N, K, x, y, st);
+    case 6: return launch_qgemvm_single<T, 6>(W, row_bytes, N, K, x, y, st);
+    case 7: return launch_qgemvm_single<T, 7>(W, row_bytes, N, K, x, y, st);
+    default: return launch_qgemvm_single<T, 8>(W, row_bytes, N, K, x, y, st);
     }
 }
 
