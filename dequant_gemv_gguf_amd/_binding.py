@@ -38,7 +38,7 @@ def lib():
         L.kq_row_bytes.restype = I64
         L.kq_dequant.argtypes = [I, P, I64, P, P]
         L.kq_qgemv.argtypes = [I, P, I64, I64, P, I, P, P]
-        L.kq_qgemv_multi.argtypes = [I, I, P, P, I64, P, I, P, P]
+        L.kq_qgemv_multi.argtypes = [I, P, P, P, I64, P, I, P, P]
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
@@ -106,17 +106,22 @@ def _addr(t):
     return t if isinstance(t, int) else t.data_ptr()
 
 
-def kq_qgemv_multi(qtype, Ws, Ns, K, x, M, ys, stream=None):
-    """Ws, Ns, ys: equal-length sequences (tensors or int addresses, row counts,
-    tensors or int addresses); marshalled into the host arrays the C call takes."""
+def kq_qgemv_multi(types, Ws, Ns, K, x, M, ys, stream=None):
+    """types: one kq_type for every matrix, or a sequence of them; Ws, Ns, ys:
+    equal-length sequences (tensors or int addresses, row counts, tensors or
+    int addresses), marshalled into the host arrays the C call takes."""
     count = len(Ws)
-    if len(Ns) != count or len(ys) != count:
-        raise ValueError("kq_qgemv_multi: Ws, Ns and ys must have the same length")
-    Wa = (ctypes.c_void_p * max(count, 1))(*[_addr(w) for w in Ws])
-    Na = (ctypes.c_int64 * max(count, 1))(*[int(n) for n in Ns])
-    Ya = (ctypes.c_void_p * max(count, 1))(*[_addr(y) for y in ys])
+    if isinstance(types, int):
+        types = [types] * count
+    if len(types) != count or len(Ns) != count or len(ys) != count:
+        raise ValueError("kq_qgemv_multi: types, Ws, Ns and ys must have the same length")
+    n = max(count, 1)
+    Ta = (ctypes.c_int * n)(*[int(t) for t in types])
+    Wa = (ctypes.c_void_p * n)(*[_addr(w) for w in Ws])
+    Na = (ctypes.c_int64 * n)(*[int(v) for v in Ns])
+    Ya = (ctypes.c_void_p * n)(*[_addr(y) for y in ys])
     like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
-    _check("kq_qgemv_multi", lib().kq_qgemv_multi(int(qtype), count, Wa, Na, int(K), _ptr(x), int(M), Ya,
+    _check("kq_qgemv_multi", lib().kq_qgemv_multi(count, Ta, Wa, Na, int(K), _ptr(x), int(M), Ya,
                                                   _stream(stream, like)))
 
 

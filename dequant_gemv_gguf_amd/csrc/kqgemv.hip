@@ -37,6 +37,8 @@
 
 #include "kqgemv.h"
 
+#include <vector>
+
 #define KQ_VERSION 10000
 
 namespace {
@@ -972,42 +974,100 @@ __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first
     }
 }
 
-template <int T, int D, int LB, bool MS>
-__global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
-                                                    const float *__restrict__ x) {
-    const int N = sg.start[sg.n];
+// One batch-1 pass over a set of segments of one format (rows of one or more
+// matrices with the same K) on activations already staged in LDS.  Each wave
+// owns one stripe of one row slot: its lane's unit never changes, so the
+// unit's activations are read from LDS into registers once, and every step
+// only streams weights.
+template <int T, int D, bool MS> struct B1Pass {
     typedef Fmt<T> F;
     typedef typename RawOf<T>::type Raw;
-    extern __shared__ float smem[];
-    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);       // [16][64]
-    float *xs = smem + 16 * 64;
-    const int XS = x_stride(K), SS = s_stride(K);
-    float *ss = xs + XS;
-    const int nthreads = blockDim.x;
-    // wave index as a scalar: everything derived from it (the row of a step and
-    // the buffer descriptor of its loads) stays in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int RS = (nthreads >> 6) / ns;               // row slots
-    const int rsl = wave / ns, stripe = wave - rsl * ns;
-    const int G = 64 / lpr;
-    const int grp = lane / lpr, slot = lane - grp * lpr;
-    const int units = (K / F::QK) * F::UPB;
-    const int u = stripe * 64 + slot;
-    const bool act = u < units;
-    const int uc = act ? u : 0;
-    const int sub = uc % F::UPB;
-    const u32 boff = (u32)(uc / F::UPB) * F::BYTES;
-    const int rstride = gridDim.x * RS * G;
-    const int first = (blockIdx.x * RS + rsl) * G;
-    // steps of the work-group's first row slot; every row slot runs this many
-    // (uniform trip count: the flush below has barriers), later slots may run
-    // past N on empty buffers and store nothing
-    const int f0 = blockIdx.x * RS * G;
-    const int wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
+    const Segs &sg;
+    int64_t row_bytes;
+    int N, lpr, ns, wave, lane, rsl, stripe, G, grp, slot, sub, rstride, first, wsteps, uc;
+    bool act;
+    u32 boff;
+    Raw ring[D][1];
 
-    // Prologue: activation loads first (at most two groups of 16 per thread),
-    // then the loads of the first D row steps, then the LDS writes -- waiting
-    // for the activations leaves the row loads in flight.
+    __device__ __forceinline__ B1Pass(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_)
+        : sg(s), row_bytes(rb), lpr(lpr_), ns(ns_), wave(wave_), lane(lane_) {
+        N = sg.start[sg.n];
+        const int RS = (blockDim.x >> 6) / ns;          // row slots
+        rsl = wave / ns;
+        stripe = wave - rsl * ns;
+        G = 64 / lpr;
+        grp = lane / lpr;
+        slot = lane - grp * lpr;
+        const int units = (K / F::QK) * F::UPB;
+        const int u = stripe * 64 + slot;
+        act = u < units;
+        uc = act ? u : 0;
+        sub = uc % F::UPB;
+        boff = (u32)(uc / F::UPB) * F::BYTES;
+        rstride = gridDim.x * RS * G;
+        first = (blockIdx.x * RS + rsl) * G;
+        // steps of the work-group's first row slot; every row slot runs this
+        // many (uniform trip count: the loop has barriers), later slots may
+        // run past N on empty buffers and store nothing
+        const int f0 = blockIdx.x * RS * G;
+        wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
+    }
+    __device__ __forceinline__ void issue(int d, int step) {
+        issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + step * rstride, grp, act, boff, sub);
+    }
+    __device__ __forceinline__ void issue_first() {
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(d, d);
+    }
+    __device__ __forceinline__ void flush(float keep, int b0, float (*part)[64]) {
+        flush1<MS>(keep, b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
+    }
+    // the loads of the first D steps must have been issued (issue_first)
+    __device__ __forceinline__ void run(const float *xs, const float *ss, int XS, int SS, float (*part)[64]) {
+        XReg<T> xa;
+        {
+            const int e0 = unit_e0<T>(uc);
+            const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+            xreg_from_lds<T>(xa, xl);
+        }
+        float keep = 0.f;
+        int j = 0;
+        for (; j + D <= wsteps; j += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                float v[1][1];
+                val_unit<1, 1>(ring[d], sub, xa, v);
+                issue(d, j + d + D);
+                const float S = group_sum(act ? v[0][0] : 0.f, lpr);
+                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+            }
+            if (((j + D) & (lpr - 1)) == 0) flush(keep, j + D - lpr, part);
+            // keep the waves of the work-group in step: otherwise the oldest
+            // waves race ahead and the work-group ends on a few slow waves
+            // with too few loads in flight
+            __syncthreads();
+        }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            if (j + d < wsteps) {
+                float v[1][1];
+                val_unit<1, 1>(ring[d], sub, xa, v);
+                const float S = group_sum(act ? v[0][0] : 0.f, lpr);
+                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+            }
+        }
+        if (wsteps & (lpr - 1)) flush(keep, wsteps & ~(lpr - 1), part);
+    }
+};
+
+// Prologue of the batch-1 kernels: the activation loads (at most two groups
+// of 16 per thread), then `issue` (the first row loads), then the LDS writes
+// of the activations and their 16-sums -- waiting for the activations leaves
+// the row loads in flight.
+template <class Issue>
+__device__ __forceinline__ void stage_x1(const float *__restrict__ x, int K, float *smem, float *xs, float *ss,
+                                         Issue issue) {
+    const int nthreads = blockDim.x;
     const int n16 = K >> 4;
     f4 xg[2][4];
 #pragma unroll
@@ -1018,9 +1078,7 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
         for (int k = 0; k < 4; ++k) xg[it][k] = src[k];
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every activation load ahead of the row loads
-    Raw ring[D][1];
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + d * rstride, grp, act, boff, sub);
+    issue();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -1034,38 +1092,48 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
         (ok ? ss[idx] : smem[16]) = sum16(xg[it][0], xg[it][1], xg[it][2], xg[it][3]);
     }
     __syncthreads();
-    XReg<T> xa;
-    {
-        const int e0 = unit_e0<T>(uc);
-        const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
-        xreg_from_lds<T>(xa, xl);
-    }
+}
 
-    float keep = 0.f;
-    int j = 0;
-    for (; j + D <= wsteps; j += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            float v[1][1];
-            val_unit<1, 1>(ring[d], sub, xa, v);
-            issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + (j + d + D) * rstride, grp, act, boff, sub);
-            const float S = group_sum(act ? v[0][0] : 0.f, lpr);
-            keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
-        }
-        if (((j + D) & (lpr - 1)) == 0)
-            flush1<MS>(keep, j + D - lpr, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
+// Batch-1 kernel: one persistent work-group per compute unit, RS row slots of
+// ns stripe waves.  LDS: [16][64] flush area, then the staged activations.
+template <int T, int D, int LB, bool MS>
+__global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
+                                                    const float *__restrict__ x) {
+    extern __shared__ float smem[];
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    float *ss = xs + XS;
+    // wave index as a scalar: everything derived from it (the row of a step and
+    // the buffer descriptor of its loads) stays in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    B1Pass<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane);
+    stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
+    p.run(xs, ss, XS, SS, part);
+}
+
+// Two formats with the same K and work-group shape (the K-quants: same units
+// per row) and the same activations in one launch: the activations are staged
+// once, then the work-group makes a pass over the rows of format TA and one
+// over those of format TB.
+template <int TA, int DA, int TB, int DB>
+__global__ __launch_bounds__(1024) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
+                                                           int K, int lpr, int ns, const float *__restrict__ x) {
+    extern __shared__ float smem[];
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    float *ss = xs + XS;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    {
+        B1Pass<TA, DA, true> pa(sa, rba, K, lpr, ns, wave, lane);
+        stage_x1(x, K, smem, xs, ss, [&] { pa.issue_first(); });
+        pa.run(xs, ss, XS, SS, part);
     }
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) {
-        if (j + d < wsteps) {
-            float v[1][1];
-            val_unit<1, 1>(ring[d], sub, xa, v);
-            const float S = group_sum(act ? v[0][0] : 0.f, lpr);
-            keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
-        }
-    }
-    if (wsteps & (lpr - 1))
-        flush1<MS>(keep, wsteps & ~(lpr - 1), wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
+    __syncthreads();
+    B1Pass<TB, DB, true> pb(sb, rbb, K, lpr, ns, wave, lane);
+    pb.issue_first();
+    pb.run(xs, ss, XS, SS, part);
 }
 
 // Batch-M kernel (2 <= M <= 8).  Persistent work-groups of NW waves, one per
@@ -1421,6 +1489,13 @@ int fmt_of(int type, int *qk, int *bytes, int *upb) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Bytes per row of K weights of a valid type (K a multiple of the block).
+int64_t kq_row_bytes_(int type, int64_t K) {
+    int qk, nb, upb;
+    fmt_of(type, &qk, &nb, &upb);
+    return (K / qk) * nb;
+}
+
 // K chunk staged in LDS per M: a multiple of 4096 so that the lane owning a
 // unit never depends on the chunking (units per 4096 columns are a multiple of
 // 64 for every format).
@@ -1538,45 +1613,6 @@ int launch_qgemv1_single(const void *W, int64_t row_bytes, int N, int K, const f
     return launch_qgemv1<T>(c, sg, row_bytes, K, x, st);
 }
 
-// Batch-1 products of several matrices (same format and K) with the same
-// activations: up to MAX_SEGS matrices per launch.
-template <int T>
-int launch_qgemv1_multi(int count, const void *const *W, const int64_t *N, int64_t row_bytes, int K,
-                        const float *x, float *const *y, hipStream_t st) {
-    B1Cfg c;
-    if (!batch1_cfg<T>(K, &c)) {
-        for (int i = 0; i < count; ++i) {
-            if (N[i] == 0) continue;
-            const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, c.lpr);
-            if (r) return r;
-        }
-        return KQ_OK;
-    }
-    const int64_t G = 64 / c.lpr;
-    int i = 0;
-    while (i < count) {
-        Segs sg = {};
-        int64_t at = 0;
-        while (i < count && sg.n < MAX_SEGS) {
-            if (N[i] == 0) { ++i; continue; }
-            const int64_t next = at + (N[i] + G - 1) / G * G;
-            if (next >= ((int64_t)1 << 31)) break;
-            sg.W[sg.n] = (const uint8_t *)W[i];
-            sg.y[sg.n] = y[i];
-            sg.start[sg.n] = (int)at;
-            sg.rows[sg.n] = (int)N[i];
-            ++sg.n;
-            at = next;
-            ++i;
-        }
-        if (sg.n == 0) break;
-        sg.start[sg.n] = (int)at;
-        const int r = launch_qgemv1<T>(c, sg, row_bytes, K, x, st);
-        if (r) return r;
-    }
-    return KQ_OK;
-}
-
 // Batch-M configuration: rows per lane group (R: each activation read from
 // LDS serves R rows) and ring depth (D) per format and M, chosen by
 // measurement among the settings that fit the 256-VGPR budget of 8-wave
@@ -1646,6 +1682,131 @@ int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const 
     default: return launch_qgemvm_single<T, 8>(W, row_bytes, N, K, x, y, st);
     }
 }
+
+// Segments for the matrices ids[*pos ..] (their rows numbered one after the
+// other, each start padded to a multiple of `pad` rows): at most MAX_SEGS, and
+// fewer than 2^31 numbered rows.  Advances *pos; false when none is left.
+static bool next_segs(const std::vector<int> &ids, size_t *pos, const void *const *W, const int64_t *N,
+                      float *const *y, int64_t pad, Segs *sg) {
+    *sg = Segs{};
+    int64_t at = 0;
+    while (*pos < ids.size() && sg->n < MAX_SEGS) {
+        const int i = ids[*pos];
+        const int64_t next = at + (N[i] + pad - 1) / pad * pad;
+        if (next >= ((int64_t)1 << 31)) break;
+        sg->W[sg->n] = (const uint8_t *)W[i];
+        sg->y[sg->n] = y[i];
+        sg->start[sg->n] = (int)at;
+        sg->rows[sg->n] = (int)N[i];
+        ++sg->n;
+        at = next;
+        ++*pos;
+    }
+    sg->start[sg->n] = (int)at;
+    return sg->n > 0;
+}
+
+// Products y[i] = W[i] . x of one format and K for the matrices ids, M rows.
+template <int T>
+int launch_group(int M, const std::vector<int> &ids, const void *const *W, const int64_t *N, int64_t row_bytes,
+                 int K, const float *x, float *const *y, hipStream_t st) {
+    size_t pos = 0;
+    Segs sg;
+    if (M == 1) {
+        B1Cfg c;
+        if (!batch1_cfg<T>(K, &c)) {
+            for (int i : ids) {
+                const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, c.lpr);
+                if (r) return r;
+            }
+            return KQ_OK;
+        }
+        while (next_segs(ids, &pos, W, N, y, 64 / c.lpr, &sg)) {
+            const int r = launch_qgemv1<T>(c, sg, row_bytes, K, x, st);
+            if (r) return r;
+        }
+        return KQ_OK;
+    }
+    const int lpr = lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB);
+    const int64_t pad = 2 * (64 / lpr);          // the batch-M row step (MROWS = 2)
+    while (next_segs(ids, &pos, W, N, y, pad, &sg)) {
+        int r;
+        switch (M) {
+        case 2: r = launch_qgemvm<T, 2>(sg, row_bytes, K, x, st); break;
+        case 3: r = launch_qgemvm<T, 3>(sg, row_bytes, K, x, st); break;
+        case 4: r = launch_qgemvm<T, 4>(sg, row_bytes, K, x, st); break;
+        case 5: r = launch_qgemvm<T, 5>(sg, row_bytes, K, x, st); break;
+        case 6: r = launch_qgemvm<T, 6>(sg, row_bytes, K, x, st); break;
+        case 7: r = launch_qgemvm<T, 7>(sg, row_bytes, K, x, st); break;
+        default: r = launch_qgemvm<T, 8>(sg, row_bytes, K, x, st); break;
+        }
+        if (r == KQ_ERR_ARG) {                     // activations too large for LDS: one call each
+            for (int s = 0; s < sg.n; ++s) {
+                r = launch_qgemv_m<T>(M, sg.W[s], row_bytes, sg.rows[s], K, x, sg.y[s], st);
+                if (r) return r;
+            }
+        } else if (r) {
+            return r;
+        }
+    }
+    return KQ_OK;
+}
+
+int launch_group_t(int type, int M, const std::vector<int> &ids, const void *const *W, const int64_t *N, int K,
+                   const float *x, float *const *y, hipStream_t st) {
+    const int64_t rb = kq_row_bytes_(type, K);
+    switch (type) {
+    case KQ_TYPE_Q4_K: return launch_group<T_Q4_K>(M, ids, W, N, rb, K, x, y, st);
+    case KQ_TYPE_Q6_K: return launch_group<T_Q6_K>(M, ids, W, N, rb, K, x, y, st);
+    case KQ_TYPE_Q2_K: return launch_group<T_Q2_K>(M, ids, W, N, rb, K, x, y, st);
+    default: return launch_group<T_Q8_0>(M, ids, W, N, rb, K, x, y, st);
+    }
+}
+
+// Batch-1 configuration of the 16-wave kernel whatever the format prefers
+// (the two passes of a mixed launch share the work-group shape).
+template <int T> bool batch1_wide_cfg(int K, B1Cfg *c) {
+    if (!batch1_cfg<T>(K, c)) return false;
+    if (c->wide) return true;
+    c->wide = true;
+    if (c->ns > 16) return false;
+    c->rs = 16 / c->ns;
+    return K / 16 <= 2 * 64 * c->ns * c->rs;
+}
+
+// Two K-quant formats (type ids TA < TB) with the same K in one launch: up to
+// MAX_SEGS matrices of each; returns how many of each it served.
+template <int TA, int TB>
+int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> &ib, size_t *pb,
+                 const void *const *W, const int64_t *N, int K, const float *x, float *const *y, hipStream_t st) {
+    B1Cfg ca, cb;
+    if (!batch1_wide_cfg<TA>(K, &ca) || !batch1_wide_cfg<TB>(K, &cb) || ca.lpr != cb.lpr || ca.ns != cb.ns ||
+        ca.rs != cb.rs)
+        return KQ_ERR_ARG;
+    const int G = 64 / ca.lpr;
+    Segs sa, sb;
+    next_segs(ia, pa, W, N, y, G, &sa);
+    next_segs(ib, pb, W, N, y, G, &sb);
+    const int64_t slots = ((int64_t)(sa.start[sa.n] > sb.start[sb.n] ? sa.start[sa.n] : sb.start[sb.n]) + G - 1) / G;
+    const int64_t need = (slots + ca.rs - 1) / ca.rs;
+    const int64_t cap = cu_count();
+    const int grid = (int)(need < cap ? need : cap);
+    const size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
+    auto kern = qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>()>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK),
+                       sb, Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK), K, ca.lpr, ca.ns, x);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+int launch_mixed_t(int ta, int tb, const std::vector<int> &ia, size_t *pa, const std::vector<int> &ib, size_t *pb,
+                   const void *const *W, const int64_t *N, int K, const float *x, float *const *y, hipStream_t st) {
+    if (ta == KQ_TYPE_Q2_K && tb == KQ_TYPE_Q4_K) return launch_mixed<T_Q2_K, T_Q4_K>(ia, pa, ib, pb, W, N, K, x, y, st);
+    if (ta == KQ_TYPE_Q2_K && tb == KQ_TYPE_Q6_K) return launch_mixed<T_Q2_K, T_Q6_K>(ia, pa, ib, pb, W, N, K, x, y, st);
+    if (ta == KQ_TYPE_Q4_K && tb == KQ_TYPE_Q6_K) return launch_mixed<T_Q4_K, T_Q6_K>(ia, pa, ib, pb, W, N, K, x, y, st);
+    return KQ_ERR_ARG;
+}
+
 
 template <int T, int MAXM>
 int launch_qmoe_t(const void *W, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_, int k,
@@ -1768,42 +1929,56 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K, const float *x, int 
     }
 }
 
-int kq_qgemv_multi(int type, int count, const void *const *W, const int64_t *N, int64_t K, const float *x, int M,
-                   float *const *y, void *stream) {
+int kq_qgemv_multi(int count, const int *types, const void *const *W, const int64_t *N, int64_t K, const float *x,
+                   int M, float *const *y, void *stream) {
     if (count < 0) return KQ_ERR_ARG;
     if (count == 0) return KQ_OK;
-    if (!W || !N || !y) return KQ_ERR_NULL;
-    int64_t row_bytes;
+    if (!types || !W || !N || !y) return KQ_ERR_NULL;
     for (int i = 0; i < count; ++i) {
-        const int r = check_gemv_shape(type, N[i], K, &row_bytes);
+        int64_t rb;
+        const int r = check_gemv_shape(types[i], N[i], K, &rb);
         if (r) return r;
     }
     if (M < 1 || M > 8) return KQ_ERR_M;
-    bool any = false;
+    // the matrices to compute, by format, in the caller's order
+    const int tids[4] = {KQ_TYPE_Q4_K, KQ_TYPE_Q6_K, KQ_TYPE_Q2_K, KQ_TYPE_Q8_0};
+    std::vector<int> by[4];
     for (int i = 0; i < count; ++i) {
         if (N[i] == 0) continue;
-        any = true;
         if (!W[i] || !y[i]) return KQ_ERR_NULL;
         if (!aligned(W[i], 16) || !aligned(y[i], 16)) return KQ_ERR_ALIGN;
+        for (int t = 0; t < 4; ++t)
+            if (types[i] == tids[t]) by[t].push_back(i);
     }
-    if (!any) return KQ_OK;
+    if (by[0].empty() && by[1].empty() && by[2].empty() && by[3].empty()) return KQ_OK;
     if (!x) return KQ_ERR_NULL;
     if (!aligned(x, 16)) return KQ_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
-    if (M > 1) {
-        for (int i = 0; i < count; ++i) {
-            if (N[i] == 0) continue;
-            const int r = kq_qgemv(type, W[i], N[i], K, x, M, y[i], stream);
-            if (r) return r;
+    size_t pos[4] = {0, 0, 0, 0};
+    if (M == 1) {
+        // two K-quant formats: pair them up in mixed launches while both last
+        int a = -1, b = -1;
+        for (int t = 0; t < 3; ++t) {
+            if (by[t].empty()) continue;
+            if (a < 0) a = t; else if (b < 0) b = t;
         }
-        return KQ_OK;
+        if (a >= 0 && b >= 0) {
+            const int lo = tids[a] < tids[b] ? a : b, hi = lo == a ? b : a;
+            while (pos[lo] < by[lo].size() && pos[hi] < by[hi].size()) {
+                const int r = launch_mixed_t(tids[lo], tids[hi], by[lo], &pos[lo], by[hi], &pos[hi], W, N, (int)K, x,
+                                             y, st);
+                if (r == KQ_ERR_ARG) break;              // shapes do not pair: separate launches
+                if (r) return r;
+            }
+        }
     }
-    switch (type) {
-    case KQ_TYPE_Q4_K: return launch_qgemv1_multi<T_Q4_K>(count, W, N, row_bytes, (int)K, x, y, st);
-    case KQ_TYPE_Q6_K: return launch_qgemv1_multi<T_Q6_K>(count, W, N, row_bytes, (int)K, x, y, st);
-    case KQ_TYPE_Q2_K: return launch_qgemv1_multi<T_Q2_K>(count, W, N, row_bytes, (int)K, x, y, st);
-    default: return launch_qgemv1_multi<T_Q8_0>(count, W, N, row_bytes, (int)K, x, y, st);
+    for (int t = 0; t < 4; ++t) {
+        if (pos[t] >= by[t].size()) continue;
+        const std::vector<int> rest(by[t].begin() + (long)pos[t], by[t].end());
+        const int r = launch_group_t(tids[t], M, rest, W, N, (int)K, x, y, st);
+        if (r) return r;
     }
+    return KQ_OK;
 }
 
 size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N) {

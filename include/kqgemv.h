@@ -104,24 +104,28 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K,
              const float *x, int M, float *y, void *stream);
 
 /* Grouped fused dequant-GEMV: the `count` products y[i] = W[i] . x of
- * matrices that share K, the block format and the activations (a layer's
- * q/k/v projections, or its gate and up projections), served by as few
- * launches as possible (at M == 1, up to 8 matrices per launch).  The fused
- * kernels of the Kortex pages ("Out-of-core LLM inference engine written from
- * scratch in Rust", section Approach) run one layer's projections in one pass;
- * this is that grouping for matrices with the same input.
- *   W  host array of `count` device pointers, matrix i has N[i] rows of
- *      `type` blocks (layout and alignment as for kq_qgemv).
- *   N  host array of `count` row counts (0 allowed: that matrix is skipped).
- *   x  M rows of K fp32 shared by every matrix.
- *   y  host array of `count` device pointers, y[i] is M rows of N[i] fp32.
+ * matrices that share K and the activations (a layer's q, k and v
+ * projections, or its gate and up projections), served by as few launches as
+ * possible: at M == 1, up to 8 matrices of one format per launch, and two
+ * K-quant formats (Q2_K, Q4_K, Q6_K) together in one launch (their rows have
+ * the same number of units); at M > 1, up to 8 matrices of one format per
+ * launch.  The fused kernels of the Kortex pages ("Out-of-core LLM inference
+ * engine written from scratch in Rust", section Approach) run one layer's
+ * projections in one pass; this is that grouping for matrices with the same
+ * input.
+ *   types  host array of `count` kq_type values, one per matrix.
+ *   W      host array of `count` device pointers; matrix i has N[i] rows of
+ *          types[i] blocks (layout and alignment as for kq_qgemv).
+ *   N      host array of `count` row counts (0 allowed: that matrix is skipped).
+ *   x      M rows of K fp32 shared by every matrix.
+ *   y      host array of `count` device pointers, y[i] is M rows of N[i] fp32.
  * count >= 0 (0 launches nothing).  Every argument is checked before anything
- * is launched; the limits are those of kq_qgemv.  Each y[i] is bit-identical
- * to kq_qgemv(type, W[i], N[i], K, x, M, y[i], stream).  The y[i] must not
- * overlap each other or any W[i] or x. */
-int kq_qgemv_multi(int type, int count, const void *const *W, const int64_t *N,
-                   int64_t K, const float *x, int M, float *const *y,
-                   void *stream);
+ * is launched; the limits are those of kq_qgemv (K must suit every type).
+ * Each y[i] is bit-identical to kq_qgemv(types[i], W[i], N[i], K, x, M, y[i],
+ * stream).  The y[i] must not overlap each other or any W[i] or x. */
+int kq_qgemv_multi(int count, const int *types, const void *const *W,
+                   const int64_t *N, int64_t K, const float *x, int M,
+                   float *const *y, void *stream);
 
 /* Workspace bytes kq_qmoe_gemv needs for T tokens, k slots and N rows when a
  * routing-weighted combine is requested (T*k*N*4); 0 on invalid sizes. */

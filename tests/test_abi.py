@@ -88,10 +88,11 @@ def test_qgemv_argument_errors():
 
 
 def test_qgemv_multi_argument_errors():
-    def g(qtype=Q4, Ws=(FAKE, FAKE), Ns=(4, 8), K=256, x=FAKE, M=1, ys=(FAKE, FAKE)):
-        return _status(kq.kq_qgemv_multi, qtype, list(Ws), list(Ns), K, x, M, list(ys))
-    assert g(qtype=99) == -1
+    def g(types=Q4, Ws=(FAKE, FAKE), Ns=(4, 8), K=256, x=FAKE, M=1, ys=(FAKE, FAKE)):
+        return _status(kq.kq_qgemv_multi, types, list(Ws), list(Ns), K, x, M, list(ys))
+    assert g(types=99) == -1 and g(types=[Q4, 99]) == -1
     assert g(K=100) == -2 and g(Ns=(4, -1)) == -2 and g(K=1 << 21) == -2
+    assert g(types=[Q4, Q8], K=32) == -2                               # K must suit every type
     assert g(M=0) == -3 and g(M=9) == -3
     assert g(Ws=(FAKE, None)) == -4 and g(ys=(None, FAKE)) == -4 and g(x=None) == -4
     assert g(Ws=(FAKE, ODD)) == -5 and g(ys=(ODD, FAKE)) == -5 and g(x=ODD) == -5
@@ -99,8 +100,8 @@ def test_qgemv_multi_argument_errors():
     assert g(Ws=(None, None), Ns=(0, 0), ys=(None, None), x=None) == 0   # every matrix empty
     assert g(Ws=(None, FAKE), Ns=(0, 8), ys=(None, ODD)) == -5          # empty ones are skipped
     L = kq.lib()
-    assert L.kq_qgemv_multi(Q4, -1, None, None, 256, None, 1, None, None) == -6
-    assert L.kq_qgemv_multi(Q4, 2, None, None, 256, None, 1, None, None) == -4
+    assert L.kq_qgemv_multi(-1, None, None, None, 256, None, 1, None, None) == -6
+    assert L.kq_qgemv_multi(2, None, None, None, 256, None, 1, None, None) == -4
 
 
 def test_dequant_argument_errors():

@@ -199,6 +199,59 @@ def test_qgemv_multi_equals_separate_calls(case, M):
         check_close(got, yo, S, "matrix %d" % i)
 
 
+MIXED = [
+    # (K, [(type, N), ...]): two K-quant formats share one launch at M = 1;
+    # a third format, or Q8_0, goes through its own launches
+    (4096, [(kqsynth.Q4_K, 37), (kqsynth.Q6_K, 9), (kqsynth.Q4_K, 130)]),
+    (2048, [(kqsynth.Q6_K, 33), (kqsynth.Q2_K, 300), (kqsynth.Q4_K, 5), (kqsynth.Q6_K, 1)]),
+    (1280, [(kqsynth.Q2_K, 7), (kqsynth.Q4_K, 64), (kqsynth.Q4_K, 3)]),
+    (4096, [(kqsynth.Q8_0, 17), (kqsynth.Q4_K, 20), (kqsynth.Q6_K, 0)]),
+    (768, [(kqsynth.Q6_K, 70), (kqsynth.Q2_K, 0), (kqsynth.Q4_K, 0)]),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=lambda c: "K%d-" % c[0] + "+".join(
+    "%s%d" % (kqsynth.TYPE_NAMES[t], n) for t, n in c[1]))
+@pytest.mark.parametrize("M", [1, 2])
+def test_qgemv_multi_mixed_formats(case, M):
+    K, mats = case
+    say("qgemv_multi mixed K", K, mats, "M", M)
+    if any(K % kqsynth.BLOCK[t][0] for t, _ in mats):
+        pytest.skip("K does not suit every format")
+    Ws = [qmat(t, max(n, 1), K, 50 + i)[:n] for i, (t, n) in enumerate(mats)]
+    x = kqsynth.activations(M, K, kqsynth.rng_for(51, M, K))
+    Wd = [dev(w) if n else None for w, (t, n) in zip(Ws, mats)]
+    ys = [torch.full((M, n), float("nan"), device="cuda") if n else None for t, n in mats]
+    kq.kq_qgemv_multi([t for t, _ in mats], Wd, [n for _, n in mats], K, dev(x), M, ys)
+    torch.cuda.synchronize()
+    for i, (t, n) in enumerate(mats):
+        if n == 0:
+            continue
+        got = ys[i].cpu().numpy()
+        one = gpu_gemv(t, Wd[i], n, K, x)
+        assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), i
+        yo, S = oracle.gemv(t, Ws[i], n, K, x)
+        check_close(got, yo, S, "matrix %d" % i)
+
+
+def test_qgemv_multi_mixed_full_size_attention_input():
+    # a 70B layer's k, v and q projections in one launch (Q4_K, Q6_K, Q4_K)
+    K = 8192
+    mats = [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)]
+    Ws = [kqsynth.device_matrix(t, n, K, seed=70 + i, device="cuda") for i, (t, n) in enumerate(mats)]
+    x = kqsynth.activations(1, K, kqsynth.rng_for(71))
+    ys = [torch.empty((1, n), device="cuda") for _, n in mats]
+    kq.kq_qgemv_multi([t for t, _ in mats], Ws, [n for _, n in mats], K, dev(x), 1, ys)
+    torch.cuda.synchronize()
+    for i, (t, n) in enumerate(mats):
+        one = gpu_gemv(t, Ws[i], n, K, x)
+        assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), one.view(np.uint32)), i
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n + i).integers(0, n, 30)]))
+        Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(t, Wr, len(rows), K, x)
+        check_close(ys[i].cpu().numpy()[:, rows], yo, S, "matrix %d" % i)
+
+
 def test_qgemv_multi_full_size_projections():
     # a 70B layer's k and q projections (Q4_K, K = 8192) in one launch
     K = 8192
