@@ -64,6 +64,17 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def check(status):
     if status != 0:
         raise RuntimeError("kq_qgemv_multi failed with status %d" % status)
@@ -301,19 +312,23 @@ def main():
     log("warmup done")
 
     # ---- timed region: exactly `steps` steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # (one event at every step boundary, for the median / p10 / p90 of a step)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0.record(stream)
+    marks[0].record(stream)
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         run_step()
-    t1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
-    ms_total = t0.elapsed_time(t1)
+    ms_total = marks[0].elapsed_time(marks[-1])
     ms_per_step = ms_total / args.steps
     gbs = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        return step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
 
     # ---- roofline pass: the same steps, dominant launches bracketed
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), len(dominant_idx))
@@ -352,6 +367,7 @@ def main():
         "config": config,
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tok_per_s_equiv": round(1e3 / ms_per_step, 2),
+        "step_ms_median_p10_p90": [round(pct(0.5), 4), round(pct(0.1), 4), round(pct(0.9), 4)],
         "weight_bytes_per_step": step_bytes,
         "wall_s_timed": round(wall1 - wall0, 3),
         "roofline": {
@@ -371,6 +387,9 @@ def main():
         },
     }
 
+    if args.workload == "verify":
+        out["positions_per_s"] = round(M * 1e3 / ms_per_step, 2)
+
     # ---- CPU baseline: the oracle on a bounded sample, host cores
     log("timed %d steps: %.3f ms/step, %.1f GB/s" % (args.steps, ms_per_step, gbs))
     if not args.no_cpu_baseline and host_sample:
@@ -383,14 +402,22 @@ def main():
             rb = kq.kq_row_bytes(qt, K)
             xh = np.random.default_rng(0).standard_normal((M, K)).astype(np.float32)
             hosts.append((qt, N, K, rb, W.view(N, rb).cpu().numpy(), xh))
-        # repeat the layer-0 matrices until the sample holds enough CPU time
-        while t_cpu < args.cpu_seconds:
-            for (qt, N, K, rb, Wh, xh) in hosts:
-                s = time.perf_counter()
-                oracle.gemv(qt, Wh, N, K, xh)
-                t_cpu += time.perf_counter() - s
-                done_bytes += N * rb
-            passes += 1
+        # repeat the layer-0 matrices until the sample holds enough CPU time;
+        # all host threads, then one thread on a quarter of that time
+        def sample(seconds):
+            done, t, n = 0, 0.0, 0
+            while t < seconds:
+                for (qt, N, K, rb, Wh, xh) in hosts:
+                    s = time.perf_counter()
+                    oracle.gemv(qt, Wh, N, K, xh)
+                    t += time.perf_counter() - s
+                    done += N * rb
+                n += 1
+            return done, t, n
+        done_bytes, t_cpu, passes = sample(args.cpu_seconds)
+        oracle.set_threads(1)
+        done1, t1c, passes1 = sample(args.cpu_seconds / 4)
+        oracle.set_threads(threads)
         used = ["%s %dx%d" % (kqsynth.TYPE_NAMES[qt], N, K) for (qt, N, K, _, _, _) in hosts]
         out["cpu_baseline"] = {
             "value": round(done_bytes / t_cpu / 1e9, 3),
@@ -399,6 +426,9 @@ def main():
             "kind": "oracle",
             "sample": "layer-0 matrices %s at M=%d, %d passes (%.1f s of CPU time, %.2f GB)" % (
                 ", ".join(used), M, passes, t_cpu, done_bytes / 1e9),
+            "value_1_thread": round(done1 / t1c / 1e9, 3),
+            "sample_1_thread": "the same matrices, %d passes on one thread (%.1f s)" % (passes1, t1c),
+            "host_cpu": cpu_model(),
         }
     print(json.dumps(out), flush=True)
     return 0
