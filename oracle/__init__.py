@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kq_oracle.c")
 _LIB = os.path.join(_HERE, "libkq_oracle.so")
+# The pin tests can be pointed at another build of the oracle (a copy with a
+# planted mistake, which they must reject); it is loaded as given, not built.
+_LIB_OVERRIDE = os.environ.get("KQ_ORACLE_LIB")
 
 Q8_0, Q2_K, Q4_K, Q6_K = 8, 10, 12, 14
 
@@ -39,8 +42,11 @@ def build(force=False):
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_block_shape.argtypes = [ctypes.c_int, P, P]
