@@ -14,6 +14,9 @@ Recipe (every draw seeded; numpy ``default_rng(SeedSequence([seed, *path]))``):
     mins uniform 0..63 and quants 0..15; Q6_K quants 0..63 and int8 scales
     -128..127; Q2_K scale and min nibbles 0..15 and quants 0..3.
   * Q8_0 quants are int8 uniform in -127..127.
+  * Q4_0 quants uniform 0..15; Q5_K quants 0..31 with Q4_K's scale fields;
+    Q3_K quants -4..3 and stored 6-bit scales 0..63 (uniform bytes give all
+    of these exactly).
   * Activations are fp32 N(0,1).
   * MoE routing: per token, k distinct expert ids uniform without replacement;
     routing weights are the softmax (fp64, then fp32) of k N(0,1) logits.
@@ -24,8 +27,8 @@ convention (a reading; the pages name the formats but print no layout).
 """
 import numpy as np
 
-Q8_0, Q2_K, Q4_K, Q6_K = 8, 10, 12, 14
-TYPE_NAMES = {Q8_0: "Q8_0", Q2_K: "Q2_K", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K = 2, 8, 10, 11, 12, 13, 14
+TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q2_K: "Q2_K", Q3_K: "Q3_K", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
 
 # weights per block, bytes per block, byte offsets of the fp16 d / dmin fields
 BLOCK = {
@@ -33,6 +36,9 @@ BLOCK = {
     Q6_K: (256, 210, 208, None),
     Q2_K: (256, 84, 80, 82),
     Q8_0: (32, 34, 0, None),
+    Q4_0: (32, 18, 0, None),
+    Q5_K: (256, 176, 0, 2),
+    Q3_K: (256, 110, 108, None),
 }
 
 

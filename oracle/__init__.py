@@ -24,7 +24,7 @@ _LIB = os.path.join(_HERE, "libkq_oracle.so")
 # planted mistake, which they must reject); it is loaded as given, not built.
 _LIB_OVERRIDE = os.environ.get("KQ_ORACLE_LIB")
 
-Q8_0, Q2_K, Q4_K, Q6_K = 8, 10, 12, 14
+Q4_0, Q8_0, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K = 2, 8, 10, 11, 12, 13, 14
 
 _lib = None
 

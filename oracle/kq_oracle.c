@@ -11,8 +11,8 @@
  *    values only inside the matmul (Kortex, "Out-of-core LLM inference engine
  *    written from scratch in Rust", section Approach; "Kortex: Streaming 70B
  *    Models on Consumer GPUs", section Key components, item 3) and list native
- *    kernels for the GGUF K-quants Q2_K..Q6_K and Q8_0 ("RunNburn - Run a 295B
- *    Moe from a 98GB GGUF on a 64GB RAM Desktop", the post).  Because the
+ *    kernels for the GGUF K-quants Q2_K..Q6_K, Q4_0 and Q8_0 ("RunNburn - Run
+ *    a 295B Moe from a 98GB GGUF on a 64GB RAM Desktop", the post).  Because the
  *    expansion happens only in registers, the fused result equals the plain
  *    definition written out here: expand every weight, then take the dot.
  *  - The pages give no byte layout.  The block layouts below follow the GGUF
@@ -21,6 +21,10 @@
  *      Q6_K: 256 weights in 210 B, w = d*sc*(q - 32), int8 sc per 16.
  *      Q2_K: 256 weights in  84 B, w = d*sc*q - dmin*m, 4-bit sc/m per 16.
  *      Q8_0:  32 weights in  34 B, w = d*q.
+ *      Q4_0:  32 weights in  18 B, w = d*(q - 8), 4-bit q.
+ *      Q5_K: 256 weights in 176 B, w = d*sc*q - dmin*m, 5-bit q, Q4_K scales.
+ *      Q3_K: 256 weights in 110 B, w = d*(sc - 32)*q, q in -4..3, 6-bit sc
+ *            per 16.
  *  - Several positions per pass (the speculative-verify pass of the Kortex
  *    page, section Approach) are M independent activation rows.
  *  - The MoE variant gathers the experts each token selected (the RunNburn
@@ -43,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { OT_Q8_0 = 8, OT_Q2_K = 10, OT_Q4_K = 12, OT_Q6_K = 14 };
+enum { OT_Q4_0 = 2, OT_Q8_0 = 8, OT_Q2_K = 10, OT_Q3_K = 11, OT_Q4_K = 12, OT_Q5_K = 13, OT_Q6_K = 14 };
 
 /* ---- fp16 ------------------------------------------------------------ */
 
@@ -160,9 +164,64 @@ static float q80_element(const uint8_t *b, int e)
     return weight_from_numerator(D * q);
 }
 
+/* Q4_0, 18 B: [0,2) d, [2,18) 4-bit quants; weight e < 16 is the low nibble
+ * of quant byte e, weight e >= 16 the high nibble of byte e - 16; d*(q-8). */
+static float q40_element(const uint8_t *b, int e)
+{
+    int q = (e < 16) ? (b[2 + e] & 15) : (b[2 + e - 16] >> 4);
+    int64_t D;
+    if (!f16_times_2p24(b, &D)) return (float)(f16_double(b) * (q - 8));
+    return weight_from_numerator(D * (q - 8));
+}
+
+/* Q5_K, 176 B: [0,2) d, [2,4) dmin, [4,16) scales and mins packed as in
+ * Q4_K, [16,48) high bits, [48,176) low 4 bits laid out as Q4_K's quants.
+ * Element e: sub-block j = e/32; low 4 bits as Q4_K's element e; bit 4 is
+ * bit j of byte 16 + e%32. */
+static float q5k_element(const uint8_t *b, int e)
+{
+    int j = e / 32, sc, m, low, q;
+    int64_t D, Dmin;
+    uint8_t byte = b[48 + 32 * (e / 64) + e % 32];
+    q4k_scale_min(b + 4, j, &sc, &m);
+    low = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+    q = low | (((b[16 + e % 32] >> j) & 1) << 4);
+    if (!f16_times_2p24(b, &D) || !f16_times_2p24(b + 2, &Dmin))
+        return (float)(f16_double(b) * sc * q - f16_double(b + 2) * m);
+    return weight_from_numerator(D * sc * q - Dmin * m);
+}
+
+/* Q3_K, 110 B: [0,32) high-bit mask, [32,96) 2-bit quants, [96,108) sixteen
+ * 6-bit scales, [108,110) d.  Element e: h = e/128, j = (e%128)/32, l = e%32;
+ * two low bits are bits 2j..2j+1 of byte 32 + 32h + l; the mask bit is bit
+ * e/32 of byte l; q = low - 4 when the mask bit is clear, low when set.
+ * Scale i (one per 16 weights): its low 4 bits are the low nibble of byte
+ * 96 + i (i < 8) or the high nibble of byte 96 + i - 8 (i >= 8); its top 2
+ * bits are bits 2*(i/4)..2*(i/4)+1 of byte 104 + i%4; weight d*(sc-32)*q. */
+static int q3k_scale(const uint8_t *s, int i)
+{
+    int low = (i < 8) ? (s[i] & 15) : (s[i - 8] >> 4);
+    int top = (s[8 + i % 4] >> (2 * (i / 4))) & 3;
+    return low | (top << 4);
+}
+
+static float q3k_element(const uint8_t *b, int e)
+{
+    int h = e / 128, j = (e % 128) / 32, l = e % 32;
+    int low = (b[32 + 32 * h + l] >> (2 * j)) & 3;
+    int q = ((b[l] >> (e / 32)) & 1) ? low : low - 4;
+    int sc = q3k_scale(b + 96, e / 16) - 32;
+    int64_t D;
+    if (!f16_times_2p24(b + 108, &D)) return (float)(f16_double(b + 108) * sc * q);
+    return weight_from_numerator(D * sc * q);
+}
+
 static int block_shape(int type, int *qk, int *bytes)
 {
     switch (type) {
+    case OT_Q4_0: *qk = 32; *bytes = 18; return 0;
+    case OT_Q5_K: *qk = 256; *bytes = 176; return 0;
+    case OT_Q3_K: *qk = 256; *bytes = 110; return 0;
     case OT_Q4_K: *qk = 256; *bytes = 144; return 0;
     case OT_Q6_K: *qk = 256; *bytes = 210; return 0;
     case OT_Q2_K: *qk = 256; *bytes = 84; return 0;
@@ -177,6 +236,9 @@ static float element(int type, const uint8_t *block, int e)
     case OT_Q4_K: return q4k_element(block, e);
     case OT_Q6_K: return q6k_element(block, e);
     case OT_Q2_K: return q2k_element(block, e);
+    case OT_Q4_0: return q40_element(block, e);
+    case OT_Q5_K: return q5k_element(block, e);
+    case OT_Q3_K: return q3k_element(block, e);
     default: return q80_element(block, e);
     }
 }

@@ -330,6 +330,10 @@ MOE_CASES = [
     (kqsynth.Q6_K, 128, 2048, 768, 8, 8, 1),
     (kqsynth.Q2_K, 16, 100, 512, 5, 4, 0),
     (kqsynth.Q8_0, 12, 70, 96, 3, 5, 1),
+    # one token: the split-grid path, more slots than segments of a launch
+    (kqsynth.Q2_K, 40, 300, 4096, 1, 16, 1),
+    (kqsynth.Q8_0, 20, 33, 1184, 1, 3, 0),
+    (kqsynth.Q6_K, 6, 5, 256, 1, 6, 0),
 ]
 
 
@@ -377,6 +381,34 @@ def test_qmoe_shared_expert_groups_and_bad_ids():
     yc, flag = gpu_moe(qtype, W, E, N, K, ids, p, x, 1)
     yoc, Sc, _ = oracle.moe(qtype, W, E, N, K, ids, p, x, 1)
     check_close(yc, yoc, Sc, "bad ids combined")
+
+
+@pytest.mark.parametrize("x_mode", [0, 1])
+def test_qmoe_one_token_bad_ids_and_bits(x_mode):
+    # one token: each slot equals a batch-1 product on its expert bit for bit;
+    # out-of-range ids give zeros and the flag
+    qtype, E, N, K, k = kqsynth.Q6_K, 10, 2048, 768, 8
+    W, ids, p, x = moe_inputs(qtype, E, N, K, 1, k, 12, x_mode)
+    Wd = dev(W.reshape(-1))
+    ids[0, 2] = E + 3
+    ids[0, 5] = -1
+    y, flag = gpu_moe(qtype, Wd, E, N, K, ids, None, x, x_mode)
+    assert flag == 1
+    per = N * kqsynth.row_bytes(qtype, K)
+    for j in range(k):
+        e = ids[0, j]
+        if e < 0 or e >= E:
+            assert np.all(y[0, j] == 0)
+            continue
+        xr = x[j:j + 1] if x_mode else x[0:1]
+        yg = gpu_gemv(qtype, Wd[e * per:(e + 1) * per], N, K, xr)
+        assert np.array_equal(y[0, j].view(np.uint32), yg[0].view(np.uint32)), j
+    yo, S, oflag = oracle.moe(qtype, W, E, N, K, ids, None, x, x_mode)
+    assert oflag == 1
+    check_close(y, yo, S, "one token")
+    yc, _ = gpu_moe(qtype, Wd, E, N, K, ids, p, x, x_mode)
+    yoc, Sc, _ = oracle.moe(qtype, W, E, N, K, ids, p, x, x_mode)
+    check_close(yc, yoc, Sc, "one token combined")
 
 
 def test_qmoe_slot_rows_do_not_depend_on_grouping():

@@ -12,7 +12,7 @@ import kq_fields as F
 import kqsynth
 import oracle
 
-TYPES = [F.Q4_K, F.Q6_K, F.Q2_K, F.Q8_0]
+TYPES = [F.Q4_K, F.Q6_K, F.Q2_K, F.Q8_0, F.Q4_0, F.Q5_K, F.Q3_K]
 
 
 def deq(qtype, raw, n):
@@ -37,6 +37,9 @@ def test_encoder_max_fields_fill_block(qtype):
         F.Q6_K: dict(d=0xFFFF, sc=[-1] * 16, q=[63] * 256),
         F.Q2_K: dict(d=0xFFFF, dmin=0xFFFF, sc=[15] * 16, m=[15] * 16, q=[3] * 256),
         F.Q8_0: dict(d=0xFFFF, q=[-1] * 32),
+        F.Q4_0: dict(d=0xFFFF, q=[15] * 32),
+        F.Q5_K: dict(d=0xFFFF, dmin=0xFFFF, sc=[63] * 8, m=[63] * 8, q=[31] * 256),
+        F.Q3_K: dict(d=0xFFFF, sc=[63] * 16, q=[3] * 256),
     }[qtype]
     assert F.encode(qtype, full) == b"\xff" * F.NBYTES[qtype]
 
@@ -151,6 +154,40 @@ def test_q80_special_cases():
     w = deq(F.Q8_0, F.encode_q80(d, q), 32)
     dv = float(np.float16(0.001))
     assert w[0] == np.float32(-127 * dv) and w[1] == np.float32(127 * dv) and w[2] == 0
+
+
+def test_q40_special_cases():
+    one = F.f16_bits(1.0)
+    q = [e % 16 for e in range(32)]
+    w = deq(F.Q4_0, F.encode_q40(one, q), 32)
+    assert list(w) == [float(v - 8) for v in q]
+    w = deq(F.Q4_0, F.encode_q40(F.f16_bits(-0.5), [8] * 32), 32)
+    assert np.all(w.view(np.uint32) == 0)                # q = 8 -> +0 for either sign of d
+
+
+def test_q5k_special_cases():
+    one, half = F.f16_bits(1.0), F.f16_bits(0.5)
+    sc = [1, 2, 3, 4, 5, 6, 7, 63]
+    m = [0, 1, 2, 3, 62, 63, 5, 9]
+    q = [(e * 7) % 32 for e in range(256)]
+    w = deq(F.Q5_K, F.encode_q5k(one, half, sc, m, q), 256)
+    for e in range(256):
+        assert w[e] == sc[e // 32] * q[e] - 0.5 * m[e // 32]
+    w = deq(F.Q5_K, F.encode_q5k(one, half, [1] * 8, [0] * 8, [16] * 256), 256)
+    assert np.all(w == 16)                               # the high bit alone
+
+
+def test_q3k_special_cases():
+    one = F.f16_bits(1.0)
+    sc = list(range(0, 64, 4))
+    q = [(e % 8) - 4 for e in range(256)]
+    w = deq(F.Q3_K, F.encode_q3k(one, sc, q), 256)
+    for e in range(256):
+        assert w[e] == (sc[e // 16] - 32) * q[e]
+    w = deq(F.Q3_K, F.encode_q3k(F.f16_bits(-2.0), [32] * 16, q), 256)
+    assert np.all(w.view(np.uint32) == 0)                # sc = 32 -> +0
+    w = deq(F.Q3_K, F.encode_q3k(one, [0] * 16, [-4] * 256), 256)
+    assert np.all(w == 128)                              # (0 - 32) * (-4)
 
 
 @pytest.mark.parametrize("qtype", TYPES)

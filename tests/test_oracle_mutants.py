@@ -44,6 +44,17 @@ MUTANTS = [
     ("Q2_K min dropped", "return weight_from_numerator(D * sc * q - Dmin * m);",
      "return weight_from_numerator(D * sc * q);", 1),
     ("Q8_0 unsigned quants", "int q = (int8_t)b[2 + e];", "int q = b[2 + e];", 0),
+    ("Q4_0 offset dropped", "return weight_from_numerator(D * (q - 8));", "return weight_from_numerator(D * q);", 0),
+    ("Q4_0 nibbles interleaved", "int q = (e < 16) ? (b[2 + e] & 15) : (b[2 + e - 16] >> 4);",
+     "int q = (e % 2 == 0) ? (b[2 + e / 2] & 15) : (b[2 + e / 2] >> 4);", 0),
+    ("Q5_K high bit from the wrong position", "q = low | (((b[16 + e % 32] >> j) & 1) << 4);",
+     "q = low | (((b[16 + e % 32] >> (j / 2)) & 1) << 4);", 0),
+    ("Q5_K high bit dropped", "q = low | (((b[16 + e % 32] >> j) & 1) << 4);", "q = low;", 0),
+    ("Q3_K mask sense inverted", "int q = ((b[l] >> (e / 32)) & 1) ? low : low - 4;",
+     "int q = ((b[l] >> (e / 32)) & 1) ? low - 4 : low;", 0),
+    ("Q3_K scale offset dropped", "int sc = q3k_scale(b + 96, e / 16) - 32;", "int sc = q3k_scale(b + 96, e / 16);", 0),
+    ("Q3_K scale top bits transposed", "int top = (s[8 + i % 4] >> (2 * (i / 4))) & 3;",
+     "int top = (s[8 + i / 4] >> (2 * (i % 4))) & 3;", 0),
     ("GEMV drops the last column", "for (i = 0; i < K; ++i) {", "for (i = 0; i < K - 1; ++i) {", 0),
     ("GEMV activation row stride", "const float *xm = x + (int64_t)m * K;", "const float *xm = x + (int64_t)m;", 0),
     ("GEMV output transposed", "y[(int64_t)m * N + o] = acc;", "y[(int64_t)o * M + m] = acc;", 0),
