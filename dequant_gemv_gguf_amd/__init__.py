@@ -9,7 +9,10 @@ no fallback: if the shared library is missing, loading it raises.
 from ._binding import (  # noqa: F401
     KQError,
     KQ_TYPE_Q2_K,
+    KQ_TYPE_Q3_K,
+    KQ_TYPE_Q4_0,
     KQ_TYPE_Q4_K,
+    KQ_TYPE_Q5_K,
     KQ_TYPE_Q6_K,
     KQ_TYPE_Q8_0,
     STATUS,

@@ -2,7 +2,8 @@
 import ctypes
 import os
 
-KQ_TYPE_Q8_0, KQ_TYPE_Q2_K, KQ_TYPE_Q4_K, KQ_TYPE_Q6_K = 8, 10, 12, 14
+KQ_TYPE_Q4_0, KQ_TYPE_Q8_0, KQ_TYPE_Q2_K, KQ_TYPE_Q3_K = 2, 8, 10, 11
+KQ_TYPE_Q4_K, KQ_TYPE_Q5_K, KQ_TYPE_Q6_K = 12, 13, 14
 
 STATUS = {
     0: "KQ_OK", -1: "KQ_ERR_TYPE", -2: "KQ_ERR_SHAPE", -3: "KQ_ERR_M", -4: "KQ_ERR_NULL",

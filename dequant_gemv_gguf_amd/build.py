@@ -1,30 +1,84 @@
 """Build the gfx950 shared library libkqgemv.so in-tree with hipcc.
 
+The library is several objects compiled in parallel: the C ABI
+(csrc/kqgemv.hip), and csrc/kq_inst.hip once per block format and once per
+pair of K-quant formats served by one mixed launch (each instantiates the
+launchers and kernels of its format or pair).  They are linked with
+--no-undefined, so an instantiation missing from the lists below fails the
+build.
+
 All HIP code is compiled with packed fp32 instructions disabled: hipcc would
 otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code."""
+import concurrent.futures
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "kqgemv.hip")
+CSRC = os.path.join(HERE, "csrc")
 INC = os.path.join(ROOT, "include")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkqgemv.so")
 ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 
-FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+
+# GGUF type ids of the formats, and the K-quant pairs (lower id first) that
+# kq_impl.h declares mixed launchers for.
+TYPES = (2, 8, 10, 11, 12, 13, 14)
+PAIRS = ((10, 11), (10, 12), (10, 13), (10, 14), (11, 12), (11, 13), (11, 14),
+         (12, 13), (12, 14), (13, 14))
+
+
+def units():
+    """(object name, source, defines) of every object of the library."""
+    out = [("kqgemv", "kqgemv.hip", [])]
+    out += [("kq_type%d" % t, "kq_inst.hip", ["-DKQ_INST_TYPE=%d" % t]) for t in TYPES]
+    out += [("kq_mixed%d_%d" % p, "kq_inst.hip", ["-DKQ_INST_A=%d" % p[0], "-DKQ_INST_B=%d" % p[1]])
+            for p in PAIRS]
+    return out
+
+
+def _jobs():
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        v = os.environ.get(var, "")
+        if v.isdigit() and int(v) > 0:
+            return min(int(v), 16)
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 def build(verbose=False, extra=()):
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    os.makedirs(OBJ, exist_ok=True)
+    cmds, objs = [], []
+    for name, src, defs in units():
+        o = os.path.join(OBJ, name + ".o")
+        objs.append(o)
+        cmds.append([hipcc] + FLAGS + list(extra) + defs + ["-I", INC, "-c", os.path.join(CSRC, src), "-o", o])
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        return cmd, r.returncode, r.stdout
+
+    failed = []
+    with concurrent.futures.ThreadPoolExecutor(_jobs()) as pool:
+        for cmd, rc, out in pool.map(run, cmds):
+            if out.strip() and (verbose or rc):
+                print(out, end="" if out.endswith("\n") else "\n", flush=True)
+            if rc:
+                failed.append(cmd)
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + FLAGS + list(extra) + ["-I", INC, SRC, "-o", tmp]
+    link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined"] + objs + ["-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+        print(" ".join(link), flush=True)
+    subprocess.check_call(link)
     os.replace(tmp, LIB)
     return LIB
 

@@ -9,7 +9,8 @@
  * section Approach, and "Kortex: Streaming 70B Models on Consumer GPUs",
  * section Key components, item 3).  The block formats are the GGUF K-quants
  * the RunNburn post lists native kernels for ("RunNburn - Run a 295B Moe from
- * a 98GB GGUF on a 64GB RAM Desktop"): Q2_K, Q4_K, Q6_K and Q8_0.  A
+ * a 98GB GGUF on a 64GB RAM Desktop"): Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, Q4_0 and
+ * Q8_0.  A
  * speculative-verify pass runs several positions through one pass of the
  * weights (Kortex summary, section Approach): here M <= 8 activation rows.  The
  * MoE variant applies the experts each token selected (the RunNburn post).
@@ -20,6 +21,9 @@
  *   Q6_K  256 weights / 210 B   w = d*sc*(q - 32)     (int8 sc per 16)
  *   Q2_K  256 weights /  84 B   w = d*sc*q - dmin*m   (4-bit sc, m per 16)
  *   Q8_0   32 weights /  34 B   w = d*q
+ *   Q4_0   32 weights /  18 B   w = d*(q - 8)        (4-bit q)
+ *   Q5_K  256 weights / 176 B   w = d*sc*q - dmin*m   (5-bit q, Q4_K's scales)
+ *   Q3_K  256 weights / 110 B   w = d*(sc - 32)*q     (q in -4..3, 6-bit sc per 16)
  * d and dmin are IEEE fp16 (subnormals honoured).  A weight matrix W of N rows
  * and K columns is N consecutive rows of K/QK blocks each (K fastest).  MoE
  * expert tensors are E such matrices back to back.
@@ -35,8 +39,9 @@
  *    a kernel surface at the caller's next synchronisation.
  *  - The library holds no state; calls are reentrant and thread-safe.
  *  - Alignment: W, W_exps and src 16 B; x, y, dst, workspace 16 B; ids,
- *    route_w, err_flag 4 B.  Rows of Q6_K and Q8_0 matrices may start at any
- *    even byte offset (e.g. 630-byte rows); that is handled inside.
+ *    route_w, err_flag 4 B.  Rows of Q6_K, Q3_K, Q8_0 and Q4_0 matrices may
+ *    start at any even byte offset (e.g. 630-byte rows); that is handled
+ *    inside.
  */
 #ifndef KQGEMV_H
 #define KQGEMV_H
@@ -50,9 +55,12 @@ extern "C" {
 
 /* GGUF tensor type ids of the supported block formats. */
 typedef enum kq_type {
+    KQ_TYPE_Q4_0 = 2,
     KQ_TYPE_Q8_0 = 8,
     KQ_TYPE_Q2_K = 10,
+    KQ_TYPE_Q3_K = 11,
     KQ_TYPE_Q4_K = 12,
+    KQ_TYPE_Q5_K = 13,
     KQ_TYPE_Q6_K = 14
 } kq_type;
 
@@ -107,7 +115,7 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K,
  * matrices that share K and the activations (a layer's q, k and v
  * projections, or its gate and up projections), served by as few launches as
  * possible: at M == 1, up to 8 matrices of one format per launch, and two
- * K-quant formats (Q2_K, Q4_K, Q6_K) together in one launch (their rows have
+ * K-quant formats (Q2_K..Q6_K) together in one launch (their rows have
  * the same number of units); at M > 1, up to 8 matrices of one format per
  * launch.  The fused kernels of the Kortex pages ("Out-of-core LLM inference
  * engine written from scratch in Rust", section Approach) run one layer's

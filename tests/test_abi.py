@@ -45,7 +45,8 @@ def test_version_and_status_strings():
     assert kq.kq_status_string(12345) == "unknown status"
 
 
-@pytest.mark.parametrize("qtype,qk,nb", [(Q4, 256, 144), (Q6, 256, 210), (Q2, 256, 84), (Q8, 32, 34)])
+@pytest.mark.parametrize("qtype,qk,nb", [(Q4, 256, 144), (Q6, 256, 210), (Q2, 256, 84), (Q8, 32, 34),
+                                         (2, 32, 18), (13, 256, 176), (11, 256, 110)])
 def test_block_info_and_row_bytes(qtype, qk, nb):
     assert kq.kq_block_info(qtype) == (qk, nb)
     assert kq.kq_row_bytes(qtype, 8 * qk) == 8 * nb
@@ -59,6 +60,9 @@ def test_unknown_type():
     with pytest.raises(kq.KQError) as e:
         kq.kq_block_info(3)
     assert e.value.status == -1
+    for t in (0, 1, 6, 7, 9, 15, 16, -1):
+        with pytest.raises(kq.KQError):
+            kq.kq_block_info(t)
 
 
 def _status(fn, *args):

@@ -17,7 +17,7 @@ import dequant_gemv_gguf_amd as kq  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [kqsynth.Q4_K, kqsynth.Q6_K, kqsynth.Q2_K, kqsynth.Q8_0]
+TYPES = [kqsynth.Q4_K, kqsynth.Q6_K, kqsynth.Q2_K, kqsynth.Q8_0, kqsynth.Q4_0, kqsynth.Q5_K, kqsynth.Q3_K]
 TOL_REL, TOL_ABS = 1e-4, 1e-6
 
 
@@ -87,6 +87,9 @@ SHAPES = {
     kqsynth.Q6_K: [(1, 256), (9, 768), (37, 4096), (130, 12544), (70, 1280)],
     kqsynth.Q2_K: [(1, 256), (7, 1280), (37, 4096), (130, 12544), (300, 2048)],
     kqsynth.Q8_0: [(1, 32), (9, 1184), (37, 4096), (130, 12544), (70, 96)],
+    kqsynth.Q4_0: [(1, 32), (9, 1184), (37, 4096), (130, 12544), (70, 96)],
+    kqsynth.Q5_K: [(1, 256), (7, 1280), (37, 4096), (130, 12544), (300, 2048)],
+    kqsynth.Q3_K: [(1, 256), (9, 768), (37, 4096), (130, 12544), (70, 1280)],
 }
 
 
@@ -175,6 +178,10 @@ MULTI = [
     (kqsynth.Q2_K, 2048, [33, 300, 1]),
     (kqsynth.Q8_0, 1184, [9, 17, 4]),
     (kqsynth.Q8_0, 4096, [37, 5]),
+    (kqsynth.Q4_0, 1184, [9, 17, 4]),
+    (kqsynth.Q5_K, 4096, [37, 1, 130, 2, 5, 8, 3, 11, 4, 19]),
+    (kqsynth.Q3_K, 768, [9, 70, 1]),
+    (kqsynth.Q3_K, 12544, [30, 7, 12]),
 ]
 
 
@@ -207,6 +214,11 @@ MIXED = [
     (1280, [(kqsynth.Q2_K, 7), (kqsynth.Q4_K, 64), (kqsynth.Q4_K, 3)]),
     (4096, [(kqsynth.Q8_0, 17), (kqsynth.Q4_K, 20), (kqsynth.Q6_K, 0)]),
     (768, [(kqsynth.Q6_K, 70), (kqsynth.Q2_K, 0), (kqsynth.Q4_K, 0)]),
+    (4096, [(kqsynth.Q5_K, 37), (kqsynth.Q3_K, 9), (kqsynth.Q5_K, 130)]),
+    (2048, [(kqsynth.Q3_K, 33), (kqsynth.Q6_K, 300), (kqsynth.Q5_K, 5), (kqsynth.Q2_K, 40),
+            (kqsynth.Q4_K, 7)]),
+    (1280, [(kqsynth.Q4_0, 7), (kqsynth.Q5_K, 64), (kqsynth.Q4_K, 3), (kqsynth.Q8_0, 5)]),
+    (768, [(kqsynth.Q3_K, 70), (kqsynth.Q4_K, 9)]),
 ]
 
 
@@ -279,6 +291,9 @@ FULL = [
     ("70B w1 Q2_K", kqsynth.Q2_K, 28672, 8192),
     ("70B w2 Q8_0", kqsynth.Q8_0, 8192, 28672),
     ("Q6_K K=40960", kqsynth.Q6_K, 3000, 40960),
+    ("70B w1 Q5_K", kqsynth.Q5_K, 28672, 8192),
+    ("70B w2 Q3_K", kqsynth.Q3_K, 8192, 28672),
+    ("70B w1 Q4_0", kqsynth.Q4_0, 28672, 8192),
 ]
 
 
@@ -334,6 +349,9 @@ MOE_CASES = [
     (kqsynth.Q2_K, 40, 300, 4096, 1, 16, 1),
     (kqsynth.Q8_0, 20, 33, 1184, 1, 3, 0),
     (kqsynth.Q6_K, 6, 5, 256, 1, 6, 0),
+    (kqsynth.Q5_K, 24, 96, 2048, 4, 6, 0),
+    (kqsynth.Q3_K, 24, 200, 768, 2, 8, 1),
+    (kqsynth.Q4_0, 10, 40, 1184, 1, 4, 1),
 ]
 
 
