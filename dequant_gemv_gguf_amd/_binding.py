@@ -8,12 +8,20 @@ KQ_TYPE_Q4_K, KQ_TYPE_Q5_K, KQ_TYPE_Q6_K = 12, 13, 14
 STATUS = {
     0: "KQ_OK", -1: "KQ_ERR_TYPE", -2: "KQ_ERR_SHAPE", -3: "KQ_ERR_M", -4: "KQ_ERR_NULL",
     -5: "KQ_ERR_ALIGN", -6: "KQ_ERR_ARG", -7: "KQ_ERR_LAUNCH", -8: "KQ_ERR_DEVICE",
+    -9: "KQ_ERR_IO", -10: "KQ_ERR_FORMAT",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libkqgemv.so")
 
 _lib = None
+
+
+class GGUFTensor(ctypes.Structure):
+    """struct kq_gguf_tensor (include/kqgguf.h)."""
+    _fields_ = [("name", ctypes.c_char_p), ("type", ctypes.c_int), ("n_dims", ctypes.c_int),
+                ("dims", ctypes.c_int64 * 4), ("offset", ctypes.c_uint64), ("nbytes", ctypes.c_uint64),
+                ("data", ctypes.c_void_p)]
 
 
 class KQError(RuntimeError):
@@ -43,6 +51,27 @@ def lib():
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
+        U64, CP = ctypes.c_uint64, ctypes.c_char_p
+        L.kq_gguf_open.argtypes = [CP, ctypes.POINTER(P)]
+        L.kq_gguf_close.argtypes = [P]
+        L.kq_gguf_close.restype = None
+        L.kq_gguf_version.argtypes = [P]
+        L.kq_gguf_alignment.argtypes = [P]
+        L.kq_gguf_alignment.restype = I64
+        L.kq_gguf_tensor_count.argtypes = [P]
+        L.kq_gguf_tensor_count.restype = I64
+        L.kq_gguf_find_tensor.argtypes = [P, CP]
+        L.kq_gguf_find_tensor.restype = I64
+        L.kq_gguf_tensor_info.argtypes = [P, I64, ctypes.POINTER(GGUFTensor)]
+        L.kq_gguf_upload.argtypes = [P, I64, P, P]
+        L.kq_gguf_meta_count.argtypes = [P]
+        L.kq_gguf_meta_count.restype = I64
+        L.kq_gguf_meta_key.argtypes = [P, I64, ctypes.POINTER(CP), ctypes.POINTER(I)]
+        L.kq_gguf_meta_int.argtypes = [P, CP, ctypes.POINTER(I64)]
+        L.kq_gguf_meta_float.argtypes = [P, CP, ctypes.POINTER(ctypes.c_double)]
+        L.kq_gguf_meta_string.argtypes = [P, CP, ctypes.POINTER(P), ctypes.POINTER(U64)]
+        L.kq_gguf_meta_array.argtypes = [P, CP, ctypes.POINTER(I), ctypes.POINTER(U64), ctypes.POINTER(P)]
+        L.kq_gguf_meta_array_string.argtypes = [P, CP, U64, ctypes.POINTER(P), ctypes.POINTER(U64)]
         _lib = L
     return _lib
 
@@ -135,3 +164,89 @@ def kq_qmoe_gemv(qtype, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, works
     _check("kq_qmoe_gemv", lib().kq_qmoe_gemv(int(qtype), _ptr(W_exps), int(E), int(N), int(K), _ptr(ids),
                                               _ptr(route_w), int(T), int(k), _ptr(x), int(x_mode), _ptr(y),
                                               _ptr(workspace), _ptr(err_flag), _stream(stream, y)))
+
+
+# ---- GGUF reader (include/kqgguf.h) ------------------------------------------
+# A handle is the opaque kq_gguf* as an int.
+
+def kq_gguf_open(path):
+    h = ctypes.c_void_p()
+    _check("kq_gguf_open", lib().kq_gguf_open(os.fsencode(path), ctypes.byref(h)))
+    return h.value
+
+
+def kq_gguf_close(h):
+    lib().kq_gguf_close(h)
+
+
+def kq_gguf_version(h):
+    return int(lib().kq_gguf_version(h))
+
+
+def kq_gguf_alignment(h):
+    return int(lib().kq_gguf_alignment(h))
+
+
+def kq_gguf_tensor_count(h):
+    return int(lib().kq_gguf_tensor_count(h))
+
+
+def kq_gguf_find_tensor(h, name):
+    r = int(lib().kq_gguf_find_tensor(h, name.encode()))
+    if r < 0:
+        raise KQError("kq_gguf_find_tensor", r)
+    return r
+
+
+def kq_gguf_tensor_info(h, i):
+    t = GGUFTensor()
+    _check("kq_gguf_tensor_info", lib().kq_gguf_tensor_info(h, int(i), ctypes.byref(t)))
+    return {"name": t.name.decode(), "type": t.type, "n_dims": t.n_dims, "dims": tuple(t.dims[:t.n_dims]),
+            "offset": int(t.offset), "nbytes": int(t.nbytes), "data": t.data}
+
+
+def kq_gguf_upload(h, i, dst, stream=None):
+    _check("kq_gguf_upload", lib().kq_gguf_upload(h, int(i), _ptr(dst), _stream(stream, dst)))
+
+
+def kq_gguf_meta_count(h):
+    return int(lib().kq_gguf_meta_count(h))
+
+
+def kq_gguf_meta_key(h, i):
+    k, t = ctypes.c_char_p(), ctypes.c_int()
+    _check("kq_gguf_meta_key", lib().kq_gguf_meta_key(h, int(i), ctypes.byref(k), ctypes.byref(t)))
+    return k.value.decode(), t.value
+
+
+def kq_gguf_meta_int(h, key):
+    v = ctypes.c_int64()
+    _check("kq_gguf_meta_int", lib().kq_gguf_meta_int(h, key.encode(), ctypes.byref(v)))
+    return v.value
+
+
+def kq_gguf_meta_float(h, key):
+    v = ctypes.c_double()
+    _check("kq_gguf_meta_float", lib().kq_gguf_meta_float(h, key.encode(), ctypes.byref(v)))
+    return v.value
+
+
+def kq_gguf_meta_string(h, key):
+    p, n = ctypes.c_void_p(), ctypes.c_uint64()
+    _check("kq_gguf_meta_string", lib().kq_gguf_meta_string(h, key.encode(), ctypes.byref(p), ctypes.byref(n)))
+    return ctypes.string_at(p.value, n.value) if n.value else b""
+
+
+def kq_gguf_meta_array(h, key):
+    """(element type, count, host address of the packed elements or None)."""
+    t, n, p = ctypes.c_int(), ctypes.c_uint64(), ctypes.c_void_p()
+    _check("kq_gguf_meta_array", lib().kq_gguf_meta_array(h, key.encode(), ctypes.byref(t), ctypes.byref(n),
+                                                          ctypes.byref(p)))
+    return t.value, n.value, p.value
+
+
+def kq_gguf_meta_array_string(h, key, j):
+    p, n = ctypes.c_void_p(), ctypes.c_uint64()
+    _check("kq_gguf_meta_array_string", lib().kq_gguf_meta_array_string(h, key.encode(), int(j), ctypes.byref(p),
+                                                                        ctypes.byref(n)))
+    return ctypes.string_at(p.value, n.value) if n.value else b""

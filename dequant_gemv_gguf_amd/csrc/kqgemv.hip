@@ -60,6 +60,8 @@ const char *kq_status_string(int status) {
     case KQ_ERR_ARG: return "invalid argument";
     case KQ_ERR_LAUNCH: return "kernel launch failed";
     case KQ_ERR_DEVICE: return "no usable device";
+    case KQ_ERR_IO: return "file could not be opened or mapped";
+    case KQ_ERR_FORMAT: return "malformed or unsupported file";
     default: return "unknown status";
     }
 }

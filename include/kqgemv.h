@@ -74,7 +74,9 @@ typedef enum kq_status {
     KQ_ERR_ALIGN = -5,    /* a pointer violates its alignment requirement   */
     KQ_ERR_ARG = -6,      /* any other invalid argument (x_mode, k, E)      */
     KQ_ERR_LAUNCH = -7,   /* the HIP launch itself failed                   */
-    KQ_ERR_DEVICE = -8    /* no usable gfx950 device                        */
+    KQ_ERR_DEVICE = -8,   /* no usable gfx950 device                        */
+    KQ_ERR_IO = -9,       /* a file could not be opened or mapped (kqgguf.h) */
+    KQ_ERR_FORMAT = -10   /* a malformed or unsupported file (kqgguf.h)     */
 } kq_status;
 
 /* Library version, major*10000 + minor*100 + patch. */

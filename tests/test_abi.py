@@ -10,7 +10,8 @@ import pytest
 import dequant_gemv_gguf_amd as kq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kqgemv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 Q4, Q6, Q2, Q8 = kq.KQ_TYPE_Q4_K, kq.KQ_TYPE_Q6_K, kq.KQ_TYPE_Q2_K, kq.KQ_TYPE_Q8_0
 FAKE = 0x10000          # a 16-B aligned non-NULL address that is never dereferenced
@@ -18,16 +19,23 @@ ODD = 0x10002           # 2-B aligned only
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
                             "kq_dequant", "kq_qgemv", "kq_qgemv_multi", "kq_qmoe_workspace_bytes",
-                            "kq_qmoe_gemv"])
+                            "kq_qmoe_gemv",
+                            "kq_gguf_open", "kq_gguf_close", "kq_gguf_version", "kq_gguf_alignment",
+                            "kq_gguf_tensor_count", "kq_gguf_find_tensor", "kq_gguf_tensor_info",
+                            "kq_gguf_upload", "kq_gguf_meta_count", "kq_gguf_meta_key", "kq_gguf_meta_int",
+                            "kq_gguf_meta_float", "kq_gguf_meta_string", "kq_gguf_meta_array",
+                            "kq_gguf_meta_array_string"])
 
 
 def test_library_exports_every_declared_symbol():
