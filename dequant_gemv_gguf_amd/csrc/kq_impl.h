@@ -1347,7 +1347,9 @@ template <int T, int D, bool MS> struct B1Pass {
     u32 boff;
     Raw ring[D][1];
 
-    __device__ __forceinline__ B1Pass(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_)
+    // wg / nwg: this work-group's index among the nwg that share the rows
+    __device__ __forceinline__ B1Pass(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_,
+                                      int wg, int nwg)
         : sg(s), row_bytes(rb), lpr(lpr_), ns(ns_), wave(wave_), lane(lane_) {
         N = sg.start[sg.n];
         const int RS = (blockDim.x >> 6) / ns;          // row slots
@@ -1362,12 +1364,12 @@ template <int T, int D, bool MS> struct B1Pass {
         uc = act ? u : 0;
         sub = uc % F::UPB;
         boff = (u32)(uc / F::UPB) * F::BYTES;
-        rstride = gridDim.x * RS * G;
-        first = (blockIdx.x * RS + rsl) * G;
+        rstride = nwg * RS * G;
+        first = (wg * RS + rsl) * G;
         // steps of the work-group's first row slot; every row slot runs this
         // many (uniform trip count: the loop has barriers), later slots may
         // run past N on empty buffers and store nothing
-        const int f0 = blockIdx.x * RS * G;
+        const int f0 = wg * RS * G;
         wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
     }
     __device__ __forceinline__ void issue(int d, int step) {
@@ -1465,33 +1467,35 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     // wave index as a scalar: everything derived from it (the row of a step and
     // the buffer descriptor of its loads) stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    B1Pass<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane);
+    B1Pass<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
     stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
     p.run(xs, ss, XS, SS, part);
 }
 
 // Two formats with the same K and work-group shape (the K-quants: same units
-// per row) and the same activations in one launch: the activations are staged
-// once, then the work-group makes a pass over the rows of format TA and one
-// over those of format TB.
+// per row) and the same activations in one launch: the first `gb` work-groups
+// serve the rows of format TB, the others those of format TA, side by side
+// (the host splits the grid in proportion to the bytes of each); each stages
+// the activations and makes one pass.
 template <int TA, int DA, int TB, int DB>
 __global__ __launch_bounds__(1024) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
-                                                           int K, int lpr, int ns, const float *__restrict__ x) {
+                                                           int gb, int K, int lpr, int ns,
+                                                           const float *__restrict__ x) {
     extern __shared__ float smem[];
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
     const int XS = x_stride(K), SS = s_stride(K);
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    {
-        B1Pass<TA, DA, true> pa(sa, rba, K, lpr, ns, wave, lane);
+    if ((int)blockIdx.x < gb) {
+        B1Pass<TB, DB, true> pb(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb);
+        stage_x1(x, K, smem, xs, ss, [&] { pb.issue_first(); });
+        pb.run(xs, ss, XS, SS, part);
+    } else {
+        B1Pass<TA, DA, true> pa(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb);
         stage_x1(x, K, smem, xs, ss, [&] { pa.issue_first(); });
         pa.run(xs, ss, XS, SS, part);
     }
-    __syncthreads();
-    B1Pass<TB, DB, true> pb(sb, rbb, K, lpr, ns, wave, lane);
-    pb.issue_first();
-    pb.run(xs, ss, XS, SS, part);
 }
 
 // Batch-M kernel (2 <= M <= 8).  Persistent work-groups of NW waves, one per
@@ -1973,14 +1977,22 @@ inline int cu_count() {
 // weight) and the 32-weight formats (Q8_0, Q4_0: a scale per 32) take the
 // narrow one when it still holds at least two row slots (32-weight formats:
 // one), which measured faster for Q6_K and Q8_0; with long rows the wide
-// one's extra waves win.  PREFETCH is the number of
+// one's extra waves win.  Q4_K takes the narrow one (ring of 4) only for
+// launches of at most 8 row steps per wide row slot (a 8192 x 8192 matrix, an
+// 8B model's projections), where having every step's loads in flight early
+// matters more than the wide one's extra waves.  PREFETCH is the number of
 // row steps each wave keeps in flight; it must divide every lanes-per-row
 // value (16, 32, 64).
 template <int T> constexpr bool BIG_UNIT() { return T == T_Q6_K || T == T_Q5_K || T == T_Q3_K; }
 template <int T, bool WIDE> constexpr int PREFETCH() {
-    return WIDE ? (BIG_UNIT<T>() ? 1 : 2) : (Fmt<T>::QK == 32 ? 4 : 2);
+    return WIDE ? (BIG_UNIT<T>() ? 1 : 2) : (Fmt<T>::QK == 32 || T == T_Q4_K ? 4 : 2);
 }
-template <int T> constexpr int NARROW_MAX_STRIPES() { return BIG_UNIT<T>() ? 4 : (Fmt<T>::QK == 32 ? 8 : 0); }
+template <int T> constexpr int NARROW_MAX_STRIPES() {
+    return BIG_UNIT<T>() ? 4 : (Fmt<T>::QK == 32 ? 8 : (T == T_Q4_K ? 2 : 0));
+}
+// formats that take the narrow configuration only for short launches
+template <int T> constexpr bool NARROW_SHORT_ONLY() { return T == T_Q4_K; }
+constexpr int64_t SHORT_LAUNCH_STEPS = 8;
 
 struct B1Cfg {
     int lpr, ns, rs;
@@ -1988,13 +2000,20 @@ struct B1Cfg {
     bool wide;
 };
 
-// Batch-1 configuration for rows of K columns; false: use the LDS kernel.
-template <int T> bool batch1_cfg(int K, B1Cfg *c) {
+// Batch-1 configuration for a launch over `rows` rows of K columns; false:
+// use the LDS kernel.
+template <int T> bool batch1_cfg(int K, int64_t rows, B1Cfg *c) {
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     c->lpr = lanes_per_row(units);
     c->ns = units > 64 ? (units + 63) / 64 : 1;
     c->lds = (size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float);
     c->wide = c->ns > NARROW_MAX_STRIPES<T>();
+    if (NARROW_SHORT_ONLY<T>() && !c->wide) {
+        // row steps per row slot of the wide configuration
+        const int64_t slots = (rows + 64 / c->lpr - 1) / (64 / c->lpr);
+        const int64_t per_round = (int64_t)cu_count() * (16 / c->ns);
+        c->wide = (slots + per_round - 1) / per_round > SHORT_LAUNCH_STEPS;
+    }
     const int maxw = c->wide ? 16 : 8;
     if (c->ns > maxw || c->lds > 150 * 1024) return false;
     c->rs = maxw / c->ns;
@@ -2031,7 +2050,7 @@ int launch_qgemv1(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, cons
 template <int T>
 int launch_qgemv1_single(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
     B1Cfg c;
-    if (!batch1_cfg<T>(K, &c))
+    if (!batch1_cfg<T>(K, N, &c))
         return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB));
     Segs sg = {};
     sg.W[0] = (const uint8_t *)W;
@@ -2144,7 +2163,9 @@ int launch_group(int M, const std::vector<int> &ids, const void *const *W, const
     Segs sg;
     if (M == 1) {
         B1Cfg c;
-        if (!batch1_cfg<T>(K, &c)) {
+        int64_t rows = 0;
+        for (int i : ids) rows += N[i];
+        if (!batch1_cfg<T>(K, rows, &c)) {
             for (int i : ids) {
                 const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, c.lpr);
                 if (r) return r;
@@ -2185,7 +2206,7 @@ int launch_group(int M, const std::vector<int> &ids, const void *const *W, const
 // Batch-1 configuration of the 16-wave kernel whatever the format prefers
 // (the two passes of a mixed launch share the work-group shape).
 template <int T> bool batch1_wide_cfg(int K, B1Cfg *c) {
-    if (!batch1_cfg<T>(K, c)) return false;
+    if (!batch1_cfg<T>(K, 0, c)) return false;
     if (c->wide) return true;
     c->wide = true;
     if (c->ns > 16) return false;
@@ -2206,15 +2227,29 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     Segs sa, sb;
     next_segs(ia, pa, W, N, y, G, &sa);
     next_segs(ib, pb, W, N, y, G, &sb);
-    const int64_t slots = ((int64_t)(sa.start[sa.n] > sb.start[sb.n] ? sa.start[sa.n] : sb.start[sb.n]) + G - 1) / G;
-    const int64_t need = (slots + ca.rs - 1) / ca.rs;
+    const int64_t rba = Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK), rbb = Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK);
+    // work-groups each format needs for one step per row slot; when both do
+    // not fit one per compute unit, the units are split in proportion to the
+    // bytes of each format (each side keeps at least one)
+    const int64_t need_a = (((int64_t)sa.start[sa.n] + G - 1) / G + ca.rs - 1) / ca.rs;
+    const int64_t need_b = (((int64_t)sb.start[sb.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t cap = cu_count();
-    const int grid = (int)(need < cap ? need : cap);
+    int64_t ga = need_a, gb = need_b;
+    if (ga + gb > cap) {
+        const double bytes_a = (double)sa.start[sa.n] * rba, bytes_b = (double)sb.start[sb.n] * rbb;
+        gb = (int64_t)(cap * bytes_b / (bytes_a + bytes_b) + 0.5);
+        if (gb < 1) gb = 1;
+        if (gb > cap - 1) gb = cap - 1;
+        if (gb > need_b) gb = need_b;
+        ga = cap - gb < need_a ? cap - gb : need_a;
+    }
+    const int grid = (int)(ga + gb);
+    if (grid == 0) return KQ_OK;
     const size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
     auto kern = qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>()>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK),
-                       sb, Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK), K, ca.lpr, ca.ns, x);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, rba, sb, rbb, (int)gb, K, ca.lpr,
+                       ca.ns, x);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
