@@ -16,6 +16,9 @@ Other workloads (--workload) measure the remaining shapes the same way:
   single  one Q4_K 4096x4096 matrix, rotated over 1 GB of copies
   verify  70B shapes, M activation rows (--m), all-Q4_K_M / all-Q2_K / all-Q8_0
   moe     Qwen3-30B-A3B-shaped MoE FFN x48, T tokens (--m) routed top-8
+  stream  8B-shaped layers x32 held in page-locked HOST memory, copied
+          through a ring of --slots device slots ahead of each grouped GEMV
+          (host-to-device link bound; value includes the copies)
 
 Inputs are seeded synthetic data drawn directly in device memory.  Only one
 GPU is supported: the path has no collectives.
@@ -34,7 +37,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved weight GB/s (% of 8 TB/s HBM) + equiv tok/s, 70B-layer Q4_K_M GEMV M=1"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_gguf_amd", "csrc", "kqgemv.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "dequant_gemv_gguf_amd", "csrc", f) for f in ("kq_impl.h", "kq_inst.hip", "kqgemv.hip")]
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
 def parse():
@@ -42,7 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe"])
+    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream"])
+    ap.add_argument("--slots", type=int, default=3, help="stream: device slots in the ring")
     ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
     ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the model's)")
@@ -81,8 +86,11 @@ def check(status):
 
 
 def source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 CALIB_BYTES = 1 << 30
@@ -231,6 +239,57 @@ def main():
         config = {"workload": workload, "layers": layers, "hidden": spec["hidden"], "ffn": spec["ffn"],
                   "kv_dim": spec["kv"], "M": M, "matrices_per_step": n_mats, "calls_per_step": len(launches),
                   "grouped": ", ".join("+".join(t[0] for t in g) for g in groups if len(g) > 1) or "none"}
+    elif args.workload == "stream":
+        spec = kqsynth.LLAMA3_8B
+        layers = args.layers or spec["layers"]
+        layer = kqsynth.dense_layer(spec["hidden"], spec["ffn"], spec["kv"])
+        order = {"wv": 0, "wk": 1, "wq": 2, "wo": 3, "w1": 4, "w3": 5, "w2": 6}
+        source = {"wq": "a", "wk": "a", "wv": "a", "wo": "o", "w1": "f", "w3": "f", "w2": "h"}
+        layer = sorted(layer, key=lambda t: order[t[0]])
+        groups = []
+        for t in layer:
+            if groups and source[groups[-1][0][0]] == source[t[0]]:
+                groups[-1].append(t)
+            else:
+                groups.append([t])
+        align = lambda b: (b + 255) // 256 * 256
+        slot_bytes = max(sum(align(N * kq.kq_row_bytes(t, K)) for (_, t, N, K) in g) for g in groups)
+        slots = torch.empty(args.slots * slot_bytes, dtype=torch.uint8, device=dev)
+        streamer = kq.kq_streamer_create(slots, slot_bytes, args.slots, stream)
+        xs = {K: torch.randn(1, K, device=dev, generator=torch.Generator(device=dev).manual_seed(K))
+              for K in {K for (_, _, _, K) in layer}}
+        ys = {name: torch.empty(1, N, device=dev) for (name, _, N, _) in layer}
+        weights = []
+        L_ = kq.lib()
+        for L in range(layers):
+            for grp in groups:
+                Hs = []
+                for (name, qt, N, K) in grp:
+                    W = kqsynth.device_matrix(qt, N, K, seed=1000 * L + order[name], device=dev)
+                    Wh = torch.empty(W.numel(), dtype=torch.uint8, pin_memory=True)
+                    Wh.copy_(W.view(-1))
+                    if L == 0:
+                        host_sample.append((qt, N, K, W))
+                    else:
+                        del W
+                    Hs.append(Wh)
+                weights += Hs
+                n, K = len(grp), grp[0][3]
+                Ta = (ctypes.c_int * n)(*[t for (_, t, _, _) in grp])
+                Wa = (ctypes.c_void_p * n)(*[h.data_ptr() for h in Hs])
+                Na = (ctypes.c_int64 * n)(*[N for (_, _, N, _) in grp])
+                Ya = (ctypes.c_void_p * n)(*[ys[name].data_ptr() for (name, _, _, _) in grp])
+                nbytes = sum(N * kq.kq_row_bytes(t, K) for (_, t, N, _) in grp)
+                launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=xs[K], Ya=Ya:
+                                  check(L_.kq_stream_qgemv_multi(ctypes.c_void_p(streamer), n, Ta, Wa, Na, K,
+                                                                 ctypes.c_void_p(x.data_ptr()), 1, Ya))),
+                                 nbytes, True))
+        torch.cuda.synchronize()
+        workload = "llama3-8b layers x%d streamed from pinned host memory, %d device slots, M=1" % (layers,
+                                                                                                   args.slots)
+        config = {"workload": workload, "layers": layers, "hidden": spec["hidden"], "ffn": spec["ffn"],
+                  "kv_dim": spec["kv"], "M": 1, "slots": args.slots, "slot_bytes": slot_bytes,
+                  "calls_per_step": len(launches)}
     elif args.workload == "single":
         N = K = 4096
         qt = kqsynth.Q4_K
@@ -372,7 +431,7 @@ def main():
         "wall_s_timed": round(wall1 - wall0, 3),
         "roofline": {
             "kernel": (("batch-1 Q4_K launches (M=1: %s)" % ("wk, wq, wo, w1, w3" if args.no_group else
-                                                              "wk+wq with a Q6_K pass over wv, wo, w1+w3"))
+                                                              "wk+wq beside wv (Q6_K) in one launch, wo, w1+w3"))
                        if args.workload in ("70b", "8b") else "dominant launches"),
             "bound": "hbm",
             "achieved": round(dom_gbs, 1) if dom_gbs else None,
@@ -386,6 +445,13 @@ def main():
             "timing": "HIP events around each step's dominant launches, issued as one run in a second pass of the same steps",
         },
     }
+    if args.workload == "stream":
+        # every weight byte crosses the host link once per step: that link,
+        # not HBM, bounds the streamed path
+        out["roofline"] = {"kernel": "host-to-device copies through the slot ring, each overlapped with a grouped GEMV",
+                           "bound": "pcie", "achieved": round(gbs, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                           "timing": "whole step (copies and GEMVs), one event per step boundary"}
 
     if args.workload == "verify":
         out["positions_per_s"] = round(M * 1e3 / ms_per_step, 2)

@@ -1,7 +1,7 @@
 """Fused GGUF K-quant dequant-GEMV for AMD MI355X (gfx950).
 
 A thin ctypes binding of ``libkqgemv.so`` whose C ABI is declared in
-``include/kqgemv.h`` and ``include/kqgguf.h``.  The functions keep the C names and only marshal
+``include/kqgemv.h``, ``include/kqgguf.h`` and ``include/kqstream.h``.  The functions keep the C names and only marshal
 arguments (torch tensors -> device pointers, the current torch stream ->
 hipStream_t); every step of the computation runs in the HIP kernels.  There is
 no fallback: if the shared library is missing, loading it raises.
@@ -39,6 +39,11 @@ from ._binding import (  # noqa: F401
     kq_qmoe_gemv,
     kq_qmoe_workspace_bytes,
     kq_row_bytes,
+    kq_stream_qgemv,
+    kq_stream_qgemv_multi,
+    kq_streamer_create,
+    kq_streamer_destroy,
+    kq_streamer_sync,
     kq_status_string,
     kq_version,
     lib,

@@ -72,6 +72,12 @@ def lib():
         L.kq_gguf_meta_string.argtypes = [P, CP, ctypes.POINTER(P), ctypes.POINTER(U64)]
         L.kq_gguf_meta_array.argtypes = [P, CP, ctypes.POINTER(I), ctypes.POINTER(U64), ctypes.POINTER(P)]
         L.kq_gguf_meta_array_string.argtypes = [P, CP, U64, ctypes.POINTER(P), ctypes.POINTER(U64)]
+        L.kq_streamer_create.argtypes = [P, ctypes.c_size_t, I, P, ctypes.POINTER(P)]
+        L.kq_streamer_destroy.argtypes = [P]
+        L.kq_streamer_destroy.restype = None
+        L.kq_streamer_sync.argtypes = [P]
+        L.kq_stream_qgemv_multi.argtypes = [P, I, P, P, P, I64, P, I, P]
+        L.kq_stream_qgemv.argtypes = [P, I, P, I64, I64, P, I, P]
         _lib = L
     return _lib
 
@@ -250,3 +256,41 @@ def kq_gguf_meta_array_string(h, key, j):
     _check("kq_gguf_meta_array_string", lib().kq_gguf_meta_array_string(h, key.encode(), int(j), ctypes.byref(p),
                                                                         ctypes.byref(n)))
     return ctypes.string_at(p.value, n.value) if n.value else b""
+
+
+# ---- host-streamed GEMV (include/kqstream.h) -----------------------------------
+# A streamer is the opaque kq_streamer* as an int.  Weights are HOST tensors or
+# addresses (page-locked for overlap); x and y are device tensors.
+
+def kq_streamer_create(slots, slot_bytes, nslots, stream=None):
+    h = ctypes.c_void_p()
+    _check("kq_streamer_create", lib().kq_streamer_create(_ptr(slots), int(slot_bytes), int(nslots),
+                                                          _stream(stream, slots), ctypes.byref(h)))
+    return h.value
+
+
+def kq_streamer_destroy(h):
+    lib().kq_streamer_destroy(h)
+
+
+def kq_streamer_sync(h):
+    _check("kq_streamer_sync", lib().kq_streamer_sync(h))
+
+
+def kq_stream_qgemv_multi(h, types, Ws, Ns, K, x, M, ys):
+    count = len(Ws)
+    if isinstance(types, int):
+        types = [types] * count
+    if len(types) != count or len(Ns) != count or len(ys) != count:
+        raise ValueError("kq_stream_qgemv_multi: types, Ws, Ns and ys must have the same length")
+    n = max(count, 1)
+    Ta = (ctypes.c_int * n)(*[int(t) for t in types])
+    Wa = (ctypes.c_void_p * n)(*[_addr(w) for w in Ws])
+    Na = (ctypes.c_int64 * n)(*[int(v) for v in Ns])
+    Ya = (ctypes.c_void_p * n)(*[_addr(y) for y in ys])
+    _check("kq_stream_qgemv_multi", lib().kq_stream_qgemv_multi(h, count, Ta, Wa, Na, int(K), _ptr(x), int(M), Ya))
+
+
+def kq_stream_qgemv(h, qtype, W, N, K, x, M, y):
+    _check("kq_stream_qgemv", lib().kq_stream_qgemv(h, int(qtype), _ptr(W), int(N), int(K), _ptr(x), int(M),
+                                                    _ptr(y)))

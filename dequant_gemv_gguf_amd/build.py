@@ -1,8 +1,8 @@
 """Build the gfx950 shared library libkqgemv.so in-tree with hipcc.
 
 The library is several objects compiled in parallel: the C ABI
-(csrc/kqgemv.hip), the GGUF reader (csrc/kq_gguf.cpp, host code), and
-csrc/kq_inst.hip once per block format and once per
+(csrc/kqgemv.hip), the GGUF reader and the host-streamed calls (csrc/kq_gguf.cpp,
+csrc/kq_stream.cpp, host code), and csrc/kq_inst.hip once per block format and once per
 pair of K-quant formats served by one mixed launch (each instantiates the
 launchers and kernels of its format or pair).  They are linked with
 --no-undefined, so an instantiation missing from the lists below fails the
@@ -36,7 +36,7 @@ PAIRS = ((10, 11), (10, 12), (10, 13), (10, 14), (11, 12), (11, 13), (11, 14),
 
 def units():
     """(object name, source, defines) of every object of the library."""
-    out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", [])]
+    out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", []), ("kq_stream", "kq_stream.cpp", [])]
     out += [("kq_type%d" % t, "kq_inst.hip", ["-DKQ_INST_TYPE=%d" % t]) for t in TYPES]
     out += [("kq_mixed%d_%d" % p, "kq_inst.hip", ["-DKQ_INST_A=%d" % p[0], "-DKQ_INST_B=%d" % p[1]])
             for p in PAIRS]

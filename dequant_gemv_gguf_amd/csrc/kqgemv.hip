@@ -118,8 +118,11 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K, const float *x, int 
     });
 }
 
-int kq_qgemv_multi(int count, const int *types, const void *const *W, const int64_t *N, int64_t K, const float *x,
-                   int M, float *const *y, void *stream) {
+// Every argument check of kq_qgemv_multi, in its order (also used by the
+// host-streamed calls, on the slot addresses, before they issue anything).
+__attribute__((visibility("hidden"))) int kq_multi_check(int count, const int *types, const void *const *W,
+                                                         const int64_t *N, int64_t K, const float *x, int M,
+                                                         float *const *y) {
     if (count < 0) return KQ_ERR_ARG;
     if (count == 0) return KQ_OK;
     if (!types || !W || !N || !y) return KQ_ERR_NULL;
@@ -129,6 +132,22 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W, const int6
         if (r) return r;
     }
     if (M < 1 || M > 8) return KQ_ERR_M;
+    bool any = false;
+    for (int i = 0; i < count; ++i) {
+        if (N[i] == 0) continue;
+        if (!W[i] || !y[i]) return KQ_ERR_NULL;
+        if (!aligned(W[i], 16) || !aligned(y[i], 16)) return KQ_ERR_ALIGN;
+        any = true;
+    }
+    if (any && !x) return KQ_ERR_NULL;
+    if (any && !aligned(x, 16)) return KQ_ERR_ALIGN;
+    return KQ_OK;
+}
+
+int kq_qgemv_multi(int count, const int *types, const void *const *W, const int64_t *N, int64_t K, const float *x,
+                   int M, float *const *y, void *stream) {
+    const int chk = kq_multi_check(count, types, W, N, K, x, M, y);
+    if (chk || count == 0) return chk;
     // the matrices to compute, by format, in the caller's order
     constexpr int NT = 7, NKQ = 5;                    // formats; the first NKQ are K-quants
     const int tids[NT] = {KQ_TYPE_Q4_K, KQ_TYPE_Q6_K, KQ_TYPE_Q5_K, KQ_TYPE_Q3_K, KQ_TYPE_Q2_K, KQ_TYPE_Q8_0,
@@ -136,16 +155,12 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W, const int6
     std::vector<int> by[NT];
     for (int i = 0; i < count; ++i) {
         if (N[i] == 0) continue;
-        if (!W[i] || !y[i]) return KQ_ERR_NULL;
-        if (!aligned(W[i], 16) || !aligned(y[i], 16)) return KQ_ERR_ALIGN;
         for (int t = 0; t < NT; ++t)
             if (types[i] == tids[t]) by[t].push_back(i);
     }
     bool any = false;
     for (int t = 0; t < NT; ++t) any = any || !by[t].empty();
     if (!any) return KQ_OK;
-    if (!x) return KQ_ERR_NULL;
-    if (!aligned(x, 16)) return KQ_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     size_t pos[NT] = {};
     if (M == 1) {

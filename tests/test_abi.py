@@ -35,7 +35,9 @@ def test_header_declares_the_boundary():
                             "kq_gguf_tensor_count", "kq_gguf_find_tensor", "kq_gguf_tensor_info",
                             "kq_gguf_upload", "kq_gguf_meta_count", "kq_gguf_meta_key", "kq_gguf_meta_int",
                             "kq_gguf_meta_float", "kq_gguf_meta_string", "kq_gguf_meta_array",
-                            "kq_gguf_meta_array_string"])
+                            "kq_gguf_meta_array_string",
+                            "kq_streamer_create", "kq_streamer_destroy", "kq_streamer_sync",
+                            "kq_stream_qgemv_multi", "kq_stream_qgemv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,3 +150,21 @@ def test_workspace_bytes():
     assert kq.kq_qmoe_workspace_bytes(8, 8, 2048) == 8 * 8 * 2048 * 4
     assert kq.kq_qmoe_workspace_bytes(0, 8, 2048) == 0
     assert kq.kq_qmoe_workspace_bytes(8, 17, 2048) == 0
+
+
+def test_streamer_argument_errors():
+    L = kq.lib()
+    h = ctypes.c_void_p(77)
+    assert L.kq_streamer_create(None, 1 << 20, 2, None, ctypes.byref(h)) == -4 and h.value is None
+    assert L.kq_streamer_create(ctypes.c_void_p(FAKE), 1 << 20, 2, None, None) == -4
+    assert L.kq_streamer_create(ctypes.c_void_p(FAKE + 16), 1 << 20, 2, None, ctypes.byref(h)) == -5
+    for nslots, nbytes in [(0, 1 << 20), (65, 1 << 20), (2, 0), (2, 1000)]:
+        assert L.kq_streamer_create(ctypes.c_void_p(FAKE), nbytes, nslots, None, ctypes.byref(h)) == -6
+    one = (ctypes.c_int * 1)(Q4)
+    P1 = (ctypes.c_void_p * 1)(FAKE)
+    N1 = (ctypes.c_int64 * 1)(4)
+    assert L.kq_stream_qgemv_multi(None, 1, one, P1, N1, 256, ctypes.c_void_p(FAKE), 1, P1) == -4
+    assert L.kq_stream_qgemv(None, Q4, ctypes.c_void_p(FAKE), 4, 256, ctypes.c_void_p(FAKE), 1,
+                             ctypes.c_void_p(FAKE)) == -4
+    assert L.kq_streamer_sync(None) == -4
+    L.kq_streamer_destroy(None)
