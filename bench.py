@@ -347,6 +347,9 @@ def main():
     # contiguous run between two events, and then the others: an event record
     # costs the stream a few microseconds, which one bracket per step spreads
     # over all of the step's dominant launches.
+    if not any(d for (_, _, d) in launches):
+        # no Q4_K launch (an all-Q2_K or all-Q8_0 re-encoding): time them all
+        launches = [(fn, b, True) for (fn, b, _) in launches]
     dominant_idx = [i for i, (_, _, d) in enumerate(launches) if d]
     other_idx = [i for i, (_, _, d) in enumerate(launches) if not d]
 
