@@ -1682,6 +1682,7 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restr
                                                           float *__restrict__ y, int32_t *err_flag) {
     extern __shared__ float smem[];
     __shared__ int members[128];
+    __shared__ unsigned long long match[2];
     const int s = blockIdx.y;
     const int rows_per_wg = WAVES * (64 / lpr);
     const int row0 = blockIdx.x * rows_per_wg;
@@ -1692,14 +1693,31 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restr
         if (err_flag && threadIdx.x == 0 && blockIdx.x == 0) *err_flag = 1;
         return;
     }
-    for (int t = 0; t < s; ++t)
-        if (ids[t] == e) return;               // a lower slot serves this expert
     int n = 0;
-    for (int t = s; t < nslots; ++t)
-        if (ids[t] == e) {
-            if (threadIdx.x == 0) members[n] = t;
-            ++n;
-        }
+    if (nslots <= 16) {
+        // few slots: a scan of the ids
+        for (int t = 0; t < s; ++t)
+            if (ids[t] == e) return;           // a lower slot serves this expert
+        for (int t = s; t < nslots; ++t)
+            if (ids[t] == e) {
+                if (threadIdx.x == 0) members[n] = t;
+                ++n;
+            }
+    } else {
+        // thread t < nslots (<= 128: the first two waves) compares slot t's
+        // id: a lower slot with the same expert serves it; otherwise the
+        // matching slots, in ascending order, are the members
+        const int tid = threadIdx.x, lane = tid & 63;
+        const bool same = tid < nslots && ids[tid] == e;
+        if (__syncthreads_or(same && tid < s)) return;     // uniform
+        const unsigned long long bal = __ballot(same);
+        if (tid < 128 && lane == 0) match[tid >> 6] = bal;
+        __syncthreads();
+        const unsigned long long below = tid >= 64 ? match[0] : 0ull;
+        const int rank = __popcll(below) + __popcll(bal & ((1ull << lane) - 1ull));
+        if (same) members[rank] = tid;
+        n = __popcll(match[0]) + __popcll(match[1]);
+    }
     __syncthreads();
     const uint8_t *We = W + (int64_t)e * N * row_bytes;
     for (int b0 = 0; b0 < n; b0 += MAXM) {

@@ -352,6 +352,9 @@ MOE_CASES = [
     (kqsynth.Q5_K, 24, 96, 2048, 4, 6, 0),
     (kqsynth.Q3_K, 24, 200, 768, 2, 8, 1),
     (kqsynth.Q4_0, 10, 40, 1184, 1, 4, 1),
+    # 128 slots over 40 experts: the member scan across two waves, batches of 8
+    (kqsynth.Q4_K, 40, 96, 512, 8, 16, 0),
+    (kqsynth.Q6_K, 40, 64, 768, 8, 16, 1),
 ]
 
 
