@@ -73,6 +73,8 @@ template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BYTES = 34, UPB =
 template <> struct Fmt<T_Q4_0> { static constexpr int QK = 32, BYTES = 18, UPB = 1; };
 template <> struct Fmt<T_Q5_K> { static constexpr int QK = 256, BYTES = 176, UPB = 4; };
 template <> struct Fmt<T_Q3_K> { static constexpr int QK = 256, BYTES = 110, UPB = 4; };
+// Formats whose units carry the most raw registers (more than 4 bits a weight).
+template <int T> constexpr bool BIG_UNIT() { return T == T_Q6_K || T == T_Q5_K || T == T_Q3_K; }
 
 // ---------------------------------------------------------------------------
 // Small device helpers
@@ -1655,11 +1657,16 @@ __global__ __launch_bounds__(512) void qgemvm_kernel(const Segs sg, int64_t row_
     }
 }
 
+// Rows per lane group of the routed-expert kernel: one activation read from
+// LDS serves that many rows.  Two rows for the formats with large units and
+// for one-token calls, four otherwise (measured).
+template <int T, int MAXM> constexpr int MOE_ROWS() { return (BIG_UNIT<T>() || MAXM == 1) ? 2 : 4; }
+
 // Routed experts: work-group (row tile, slot s).  Only the lowest slot that
 // routes to an expert does the work; it collects every slot that routes to the
 // same expert and serves them in batches of up to MAXM activation rows with one
 // pass over the expert's weights per batch.  Invalid ids: zero output, flag.
-template <int T, int M>
+template <int T, int M, int R>
 __device__ __forceinline__ void moe_batch(float *smem, const uint8_t *We, int64_t row_bytes, int row0, int nrows,
                                           int K, int KC, int lpr, const int *members, int x_mode, int k,
                                           const float *x, float *y, int N) {
@@ -1671,7 +1678,7 @@ __device__ __forceinline__ void moe_batch(float *smem, const uint8_t *We, int64_
         xr[m] = x + (int64_t)(x_mode ? s : s / k) * K;
         yr[m] = y + (int64_t)s * N;
     }
-    gemv_tile<T, M, 1>(smem, We, row_bytes, row0, nrows, K, KC, lpr, xr, yr);
+    gemv_tile<T, M, R>(smem, We, row_bytes, row0, nrows, K, KC, lpr, xr, yr);
 }
 
 template <int T, int MAXM>
@@ -1684,7 +1691,8 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restr
     __shared__ int members[128];
     __shared__ unsigned long long match[2];
     const int s = blockIdx.y;
-    const int rows_per_wg = WAVES * (64 / lpr);
+    constexpr int R = MOE_ROWS<T, MAXM>();
+    const int rows_per_wg = WAVES * (64 / lpr) * R;
     const int row0 = blockIdx.x * rows_per_wg;
     const int nrows = (N - row0) < rows_per_wg ? (N - row0) : rows_per_wg;
     const int e = ids[s];
@@ -1725,7 +1733,7 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restr
         if (b0) __syncthreads();
         switch (mb) {
 #define KQ_MOE_CASE(MM) \
-    case MM: if constexpr (MM <= MAXM) moe_batch<T, MM>(smem, We, row_bytes, row0, nrows, K, KC, lpr, members + b0, x_mode, k, x, y, N); break;
+    case MM: if constexpr (MM <= MAXM) moe_batch<T, MM, R>(smem, We, row_bytes, row0, nrows, K, KC, lpr, members + b0, x_mode, k, x, y, N); break;
             KQ_MOE_CASE(1) KQ_MOE_CASE(2) KQ_MOE_CASE(3) KQ_MOE_CASE(4)
             KQ_MOE_CASE(5) KQ_MOE_CASE(6) KQ_MOE_CASE(7) KQ_MOE_CASE(8)
 #undef KQ_MOE_CASE
@@ -2001,7 +2009,6 @@ inline int cu_count() {
 // matters more than the wide one's extra waves.  PREFETCH is the number of
 // row steps each wave keeps in flight; it must divide every lanes-per-row
 // value (16, 32, 64).
-template <int T> constexpr bool BIG_UNIT() { return T == T_Q6_K || T == T_Q5_K || T == T_Q3_K; }
 template <int T, bool WIDE> constexpr int PREFETCH() {
     return WIDE ? (BIG_UNIT<T>() ? 1 : 2) : (Fmt<T>::QK == 32 || T == T_Q4_K ? 4 : 2);
 }
@@ -2279,7 +2286,7 @@ int launch_qmoe_t(const void *W, int64_t row_bytes, int E, int N, int K, const i
     const int KC = chunk_for(MAXM);
     const int kc = KC < K ? KC : K;
     const size_t lds = (size_t)lds_floats(MAXM, kc) * sizeof(float);
-    const int rows_per_wg = WAVES * (64 / lpr);
+    const int rows_per_wg = WAVES * (64 / lpr) * MOE_ROWS<T, MAXM>();
     dim3 grid((N + rows_per_wg - 1) / rows_per_wg, T_ * k);
     auto kern = qmoe_kernel<T, MAXM>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
