@@ -187,6 +187,8 @@ int parse(kq_gguf *g) {
         const uint64_t kat = c.str(&klen);
         m.type = c.u32();
         if (c.bad) return KQ_ERR_FORMAT;
+        // keys and names are looked up as C strings: an embedded NUL is malformed
+        if (memchr(g->map + kat, 0, (size_t)klen)) return KQ_ERR_FORMAT;
         m.key.assign((const char *)g->map + kat, (size_t)klen);
         m.pos = c.pos;
         m.elem_type = 0;
@@ -224,6 +226,7 @@ int parse(kq_gguf *g) {
         const uint64_t nat = c.str(&nlen);
         const uint32_t nd = c.u32();
         if (c.bad || nd < 1 || nd > 4) return KQ_ERR_FORMAT;
+        if (memchr(g->map + nat, 0, (size_t)nlen)) return KQ_ERR_FORMAT;
         t.name.assign((const char *)g->map + nat, (size_t)nlen);
         t.n_dims = (int)nd;
         for (int d = 0; d < 4; ++d) t.dims[d] = 1;

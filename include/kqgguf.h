@@ -72,8 +72,9 @@ typedef enum kq_gguf_value_type {
  * Returns KQ_OK, KQ_ERR_NULL, KQ_ERR_IO (open/stat/mmap failed) or
  * KQ_ERR_FORMAT (bad magic, unsupported version, a value or table entry that
  * runs past the end of the file, an unknown value type, a bad alignment, a
- * misaligned offset, a dimension that is not a whole number of blocks, or
- * tensor data past the end of the file). */
+ * misaligned offset, a dimension that is not a whole number of blocks, tensor
+ * data past the end of the file, or a key or tensor name holding a NUL byte,
+ * which could not be looked up as a C string). */
 int kq_gguf_open(const char *path, kq_gguf **out);
 
 /* Unmap and free.  NULL is a no-op. */

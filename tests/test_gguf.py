@@ -222,6 +222,9 @@ def test_malformed_tensor_entries(tmp_path):
     # 0 and 5 dimensions
     _check_format_error(tmp_path, _raw([], [("w", kqsynth.Q4_K, [], data)]), "dims0")
     _check_format_error(tmp_path, _raw([], [("w", kqsynth.Q4_K, [K, N, 1, 1, 1], data)]), "dims5")
+    # a name or key holding a NUL byte cannot be looked up as a C string
+    _check_format_error(tmp_path, _raw([], [("w\x00x", kqsynth.Q4_K, [K, N], data)]), "nul_name")
+    _check_format_error(tmp_path, _raw([("a\x00b", U32, 1)], []), "nul_key")
     # data past the end of the file: claim more rows than were written
     _check_format_error(tmp_path, _raw([], [("w", kqsynth.Q4_K, [K, N + 1], data)]), "past_end")
     # a misaligned offset
@@ -259,3 +262,58 @@ def test_random_corruption_never_crashes(tmp_path):
         assert r in (0, ERR_FORMAT)
         outcomes.add(r)
     assert ERR_FORMAT in outcomes
+
+
+def _build_sanitized_driver(tmp_path):
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("no g++")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "gguf_fuzz")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(root, "include"),
+           os.path.join(root, "tests", "gguf_fuzz_main.cpp"),
+           os.path.join(root, "dequant_gemv_gguf_amd", "csrc", "kq_gguf.cpp"), "-o", exe]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode:
+        pytest.skip("sanitized build unavailable: " + r.stdout[-300:])
+    return exe
+
+
+def test_reader_is_memory_safe_under_sanitizers(tmp_path):
+    # the reader compiled with ASan + UBSan opens valid, truncated, corrupted
+    # and crafted files; each must be read cleanly or rejected
+    import subprocess
+    exe = _build_sanitized_driver(tmp_path)
+    full = _raw(META, sample_tensors(9), alignment=64)
+    files = []
+
+    def add(name, data):
+        p = tmp_path / name
+        p.write_bytes(data)
+        files.append(str(p))
+
+    add("valid.gguf", full)
+    for n in range(0, len(full), 97):
+        add("trunc%d.gguf" % n, full[:n])
+    rnd = random.Random(99)
+    for i in range(300):
+        b = bytearray(full)
+        for _ in range(rnd.randint(1, 8)):
+            at = rnd.randrange(0, len(b)) if rnd.random() < 0.3 else rnd.randrange(0, min(len(b), 1200))
+            b[at] = rnd.randrange(256)
+        add("mut%d.gguf" % i, bytes(b))
+    # crafted: huge lengths and counts in every length field of a small file
+    small = _raw([("k", STRING, "v"), ("a", ARRAY, (STRING, ["x"]))], [("w", 0, [4], bytes(16))])
+    for off in range(8, len(small) - 8):
+        for v in (2 ** 63, 2 ** 40, len(small)):
+            b = bytearray(small)
+            b[off:off + 8] = struct.pack("<Q", v)
+            add("craft%d_%d.gguf" % (off, v.bit_length()), bytes(b))
+    for i in range(0, len(files), 200):
+        r = subprocess.run([exe] + files[i:i + 200], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                           timeout=120)
+        assert r.returncode == 0, r.stdout[-2000:]
+        assert "opened" in r.stdout
