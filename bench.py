@@ -7,7 +7,8 @@ Q4_K and wv 1024x8192, w2 8192x28672 in Q6_K (the Q4_K_M mix), all resident
 in HBM (43.5 GB of packed weights).  One step = one product over every one of
 the 560 matrices; matrices that read the same activations (k, q and v; w1
 and w3) go through one grouped call -- 320 launches per step, k+q+v as one
-launch with a Q4_K and a Q6_K pass (--no-group: one launch per matrix).  The metric is packed-weight bytes moved per second
+launch with the Q4_K and Q6_K rows side by side (--no-group: one launch per
+matrix).  The metric is packed-weight bytes moved per second
 (algorithmic bytes: every weight byte read once), reported in GB/s, as a
 fraction of the 8 TB/s HBM3E peak and as equivalent tokens/s.
 
@@ -16,6 +17,7 @@ Other workloads (--workload) measure the remaining shapes the same way:
   single  one Q4_K 4096x4096 matrix, rotated over 1 GB of copies
   verify  70B shapes, M activation rows (--m), all-Q4_K_M / all-Q2_K / all-Q8_0
   moe     Qwen3-30B-A3B-shaped MoE FFN x48, T tokens (--m) routed top-8
+          (gate and up in one grouped launch; --no-group: separately)
   stream  8B-shaped layers x32 held in page-locked HOST memory, copied
           through a ring of --slots device slots ahead of each grouped GEMV
           (host-to-device link bound; value includes the copies)
@@ -312,6 +314,7 @@ def main():
         x = torch.randn(T, H, device=dev, generator=g)
         h = torch.randn(T * k, F, device=dev, generator=g)
         yg = torch.empty(T, k, F, device=dev)
+        yu = torch.empty(T, k, F, device=dev)
         yd = torch.empty(T, H, device=dev)
         ws = torch.empty(kq.kq_qmoe_workspace_bytes(T, k, H) // 4, device=dev)
         weights = []
@@ -321,6 +324,7 @@ def main():
             ids = torch.from_numpy(ids_np).to(dev)
             p = torch.from_numpy(p_np).to(dev)
             distinct = len(set(ids_np.reshape(-1).tolist()))
+            gate_up = []
             for (name, qt, EE, N, K) in kqsynth.moe_layer(H, E, F):
                 W = kqsynth.device_matrix(qt, EE * N, K, seed=100 * L + len(weights), device=dev)
                 weights.append(W)
@@ -328,13 +332,24 @@ def main():
                 if name == "down":
                     fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids, p=p:
                           kq.kq_qmoe_gemv(qt, W, E, N, K, ids, p, T, k, h, 1, yd, ws, None, stream))
+                elif args.no_group:
+                    out = yg if name == "gate" else yu
+                    fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids, out=out:
+                          kq.kq_qmoe_gemv(qt, W, E, N, K, ids, None, T, k, x, 0, out, None, None, stream))
                 else:
-                    fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids:
-                          kq.kq_qmoe_gemv(qt, W, E, N, K, ids, None, T, k, x, 0, yg, None, None, stream))
+                    # gate and up share the routing and x: one grouped launch
+                    gate_up.append((W, distinct * per_expert))
+                    if len(gate_up) < 2:
+                        continue
+                    fn = (lambda qt=qt, Wg=gate_up[0][0], Wu=gate_up[1][0], N=N, K=K, ids=ids:
+                          kq.kq_qmoe_gemv_multi(qt, [Wg, Wu], E, N, K, ids, T, k, x, 0, [yg, yu], None, stream))
+                    launches.append((fn, gate_up[0][1] + gate_up[1][1], True))
+                    continue
                 launches.append((fn, distinct * per_expert, name != "down"))
         workload = "qwen3-30b-a3b MoE FFN x%d, top-%d of %d experts, T=%d" % (layers, k, E, T)
         config = {"workload": workload, "layers": layers, "experts": E, "top_k": k, "hidden": H,
-                  "expert_ffn": F, "tokens": T}
+                  "expert_ffn": F, "tokens": T, "calls_per_step": len(launches),
+                  "grouped": "none" if args.no_group else "gate+up"}
     torch.cuda.synchronize()
     step_bytes = sum(b for (_, b, _) in launches)
 

@@ -51,6 +51,7 @@ def lib():
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
+        L.kq_qmoe_gemv_multi.argtypes = [I, I, P, I64, I64, I64, P, I, I, P, I, P, P, P]
         U64, CP = ctypes.c_uint64, ctypes.c_char_p
         L.kq_gguf_open.argtypes = [CP, ctypes.POINTER(P)]
         L.kq_gguf_close.argtypes = [P]
@@ -170,6 +171,21 @@ def kq_qmoe_gemv(qtype, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, works
     _check("kq_qmoe_gemv", lib().kq_qmoe_gemv(int(qtype), _ptr(W_exps), int(E), int(N), int(K), _ptr(ids),
                                               _ptr(route_w), int(T), int(k), _ptr(x), int(x_mode), _ptr(y),
                                               _ptr(workspace), _ptr(err_flag), _stream(stream, y)))
+
+
+def kq_qmoe_gemv_multi(qtype, W_exps, E, N, K, ids, T, k, x, x_mode, ys, err_flag=None, stream=None):
+    """W_exps, ys: equal-length sequences (tensors or int addresses) marshalled
+    into the host arrays the C call takes."""
+    count = len(W_exps)
+    if len(ys) != count:
+        raise ValueError("kq_qmoe_gemv_multi: W_exps and ys must have the same length")
+    n = max(count, 1)
+    Wa = (ctypes.c_void_p * n)(*[_addr(w) for w in W_exps])
+    Ya = (ctypes.c_void_p * n)(*[_addr(y) for y in ys])
+    like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
+    _check("kq_qmoe_gemv_multi", lib().kq_qmoe_gemv_multi(count, int(qtype), Wa, int(E), int(N), int(K), _ptr(ids),
+                                                          int(T), int(k), _ptr(x), int(x_mode), Ya,
+                                                          _ptr(err_flag), _stream(stream, like)))
 
 
 # ---- GGUF reader (include/kqgguf.h) ------------------------------------------

@@ -1657,6 +1657,16 @@ __global__ __launch_bounds__(512) void qgemvm_kernel(const Segs sg, int64_t row_
     }
 }
 
+// Expert tensors of one routed-expert launch: tensors of one format, shape,
+// routing and activations (an MoE layer's gate and up projections), each with
+// its per-slot outputs.
+constexpr int MOE_SETS = 4;
+struct MoeSet {
+    const uint8_t *W[MOE_SETS];
+    float *y[MOE_SETS];
+    int n;
+};
+
 // Rows per lane group of the routed-expert kernel: one activation read from
 // LDS serves that many rows.  Two rows for the formats with large units and
 // for one-token calls, four otherwise (measured).
@@ -1682,15 +1692,17 @@ __device__ __forceinline__ void moe_batch(float *smem, const uint8_t *We, int64_
 }
 
 template <int T, int MAXM>
-__global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int E,
-                                                          int N, int K, int KC, int lpr,
-                                                          const int32_t *__restrict__ ids, int nslots, int k,
-                                                          const float *__restrict__ x, int x_mode,
-                                                          float *__restrict__ y, int32_t *err_flag) {
+__global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const MoeSet set, int64_t row_bytes, int E, int N, int K,
+                                                          int KC, int lpr, const int32_t *__restrict__ ids,
+                                                          int nslots, int k, const float *__restrict__ x,
+                                                          int x_mode, int32_t *err_flag) {
     extern __shared__ float smem[];
     __shared__ int members[128];
     __shared__ unsigned long long match[2];
-    const int s = blockIdx.y;
+    // grid.y: (expert tensor, slot)
+    const int ti = blockIdx.y / nslots, s = blockIdx.y - ti * nslots;
+    const uint8_t *__restrict__ W = set.W[ti];
+    float *__restrict__ y = set.y[ti];
     constexpr int R = MOE_ROWS<T, MAXM>();
     const int rows_per_wg = WAVES * (64 / lpr) * R;
     const int row0 = blockIdx.x * rows_per_wg;
@@ -2279,30 +2291,30 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
 }
 
 template <int T, int MAXM>
-int launch_qmoe_t(const void *W, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_, int k,
-                  const float *x, int x_mode, float *ys, int32_t *err, hipStream_t st) {
+int launch_qmoe_t(const MoeSet &set, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_, int k,
+                  const float *x, int x_mode, int32_t *err, hipStream_t st) {
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);
     const int KC = chunk_for(MAXM);
     const int kc = KC < K ? KC : K;
     const size_t lds = (size_t)lds_floats(MAXM, kc) * sizeof(float);
     const int rows_per_wg = WAVES * (64 / lpr) * MOE_ROWS<T, MAXM>();
-    dim3 grid((N + rows_per_wg - 1) / rows_per_wg, T_ * k);
+    dim3 grid((N + rows_per_wg - 1) / rows_per_wg, T_ * k * set.n);
     auto kern = qmoe_kernel<T, MAXM>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, grid, dim3(WG_THREADS), lds, st, (const uint8_t *)W, row_bytes, E, N, K, KC, lpr, ids,
-                       T_ * k, k, x, x_mode, ys, err);
+    hipLaunchKernelGGL(kern, grid, dim3(WG_THREADS), lds, st, set, row_bytes, E, N, K, KC, lpr, ids, T_ * k, k, x,
+                       x_mode, err);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
 template <int T>
-int launch_qmoe_m(int maxm, const void *W, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_,
-                  int k, const float *x, int x_mode, float *ys, int32_t *err, hipStream_t st) {
+int launch_qmoe_m(int maxm, const MoeSet &set, int64_t row_bytes, int E, int N, int K, const int32_t *ids, int T_,
+                  int k, const float *x, int x_mode, int32_t *err, hipStream_t st) {
     switch (maxm) {
-    case 1: return launch_qmoe_t<T, 1>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
-    case 2: return launch_qmoe_t<T, 2>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
-    case 3: case 4: return launch_qmoe_t<T, 4>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
-    default: return launch_qmoe_t<T, 8>(W, row_bytes, E, N, K, ids, T_, k, x, x_mode, ys, err, st);
+    case 1: return launch_qmoe_t<T, 1>(set, row_bytes, E, N, K, ids, T_, k, x, x_mode, err, st);
+    case 2: return launch_qmoe_t<T, 2>(set, row_bytes, E, N, K, ids, T_, k, x, x_mode, err, st);
+    case 3: case 4: return launch_qmoe_t<T, 4>(set, row_bytes, E, N, K, ids, T_, k, x, x_mode, err, st);
+    default: return launch_qmoe_t<T, 8>(set, row_bytes, E, N, K, ids, T_, k, x, x_mode, err, st);
     }
 }
 
@@ -2322,8 +2334,8 @@ int launch_dequant_t(const void *src, int64_t n, float *dst, hipStream_t st) {
     X int launch_group<T>(int, const std::vector<int> &, const void *const *, const int64_t *, int64_t, int,      \
                           const float *, float *const *, hipStream_t);                                          \
     X int launch_qgemv_m<T>(int, const void *, int64_t, int, int, const float *, float *, hipStream_t);          \
-    X int launch_qmoe_m<T>(int, const void *, int64_t, int, int, int, const int32_t *, int, int, const float *,   \
-                           int, float *, int32_t *, hipStream_t);                                               \
+    X int launch_qmoe_m<T>(int, const MoeSet &, int64_t, int, int, int, const int32_t *, int, int, const float *, \
+                           int, int32_t *, hipStream_t);                                                        \
     X int launch_dequant_t<T>(const void *, int64_t, float *, hipStream_t);
 #define KQ_MIXED_LAUNCHER(X, A, B)                                                                               \
     X int launch_mixed<A, B>(const std::vector<int> &, size_t *, const std::vector<int> &, size_t *,              \

@@ -209,19 +209,50 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, 
         (route_w && (!aligned(route_w, 4) || !aligned(workspace, 16))) || (err_flag && !aligned(err_flag, 4)))
         return KQ_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
-    float *ys = route_w ? workspace : y;
+    MoeSet set = {};
+    set.W[0] = (const uint8_t *)W_exps;
+    set.y[0] = route_w ? workspace : y;
+    set.n = 1;
     // a batch never holds more slots than there are tokens unless a token
     // repeats an expert; MAXM = T covers the distinct-ids case in one pass
     const int maxm = T;
     r = with_type(type, [&](auto tag) {
-        return launch_qmoe_m<decltype(tag)::value>(maxm, W_exps, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x,
-                                                   x_mode, ys, err_flag, st);
+        return launch_qmoe_m<decltype(tag)::value>(maxm, set, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x,
+                                                   x_mode, err_flag, st);
     });
     if (r || !route_w) return r;
     const int64_t total = (int64_t)T * N;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + WG_THREADS - 1) / WG_THREADS)), dim3(WG_THREADS),
                        0, st, workspace, route_w, T, k, (int)N, y);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+int kq_qmoe_gemv_multi(int count, int type, const void *const *W_exps, int64_t E, int64_t N, int64_t K,
+                       const int32_t *ids, int T, int k, const float *x, int x_mode, float *const *y,
+                       int32_t *err_flag, void *stream) {
+    int64_t row_bytes;
+    int r = check_gemv_shape(type, N, K, &row_bytes);
+    if (r) return r;
+    if (count < 1 || count > MOE_SETS) return KQ_ERR_ARG;
+    if (T < 1 || T > 8) return KQ_ERR_M;
+    if (E < 1 || E >= ((int64_t)1 << 31) || k < 1 || k > 16 || k > E || (x_mode != 0 && x_mode != 1))
+        return KQ_ERR_ARG;
+    if (!W_exps || !y) return KQ_ERR_NULL;
+    if (N == 0) return KQ_OK;
+    if (!ids || !x) return KQ_ERR_NULL;
+    MoeSet set = {};
+    for (int i = 0; i < count; ++i) {
+        if (!W_exps[i] || !y[i]) return KQ_ERR_NULL;
+        if (!aligned(W_exps[i], 16) || !aligned(y[i], 16)) return KQ_ERR_ALIGN;
+        set.W[i] = (const uint8_t *)W_exps[i];
+        set.y[i] = y[i];
+    }
+    set.n = count;
+    if (!aligned(x, 16) || !aligned(ids, 4) || (err_flag && !aligned(err_flag, 4))) return KQ_ERR_ALIGN;
+    return with_type(type, [&](auto tag) {
+        return launch_qmoe_m<decltype(tag)::value>(T, set, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode,
+                                                   err_flag, (hipStream_t)stream);
+    });
 }
 
 } // extern "C"

@@ -164,6 +164,20 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,
                  const float *x, int x_mode, float *y, float *workspace,
                  int32_t *err_flag, void *stream);
 
+/* Grouped routed-expert GEMV: `count` (1..4) stacked expert tensors of one
+ * format and shape that share the routing and the activations -- an MoE
+ * layer's gate and up projections -- in one launch, per-slot outputs only:
+ *   y[i][t][j] = W_exps[i][ids[t][j]] . x_(t,j)   (layouts as kq_qmoe_gemv).
+ *   W_exps, y: host arrays of `count` device pointers (16-B aligned).
+ * The fused projections of the Kortex pages ("Out-of-core LLM inference engine
+ * written from scratch in Rust", section Approach) run a layer's matrices in
+ * one pass; this is that grouping for the experts a token selected (the
+ * RunNburn post).  Limits and errors as for kq_qmoe_gemv; each y[i] is
+ * bit-identical to kq_qmoe_gemv(type, W_exps[i], ..., route_w = NULL, ...). */
+int kq_qmoe_gemv_multi(int count, int type, const void *const *W_exps, int64_t E, int64_t N, int64_t K,
+                       const int32_t *ids, int T, int k, const float *x, int x_mode, float *const *y,
+                       int32_t *err_flag, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

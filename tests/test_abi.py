@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
                             "kq_dequant", "kq_qgemv", "kq_qgemv_multi", "kq_qmoe_workspace_bytes",
-                            "kq_qmoe_gemv",
+                            "kq_qmoe_gemv", "kq_qmoe_gemv_multi",
                             "kq_gguf_open", "kq_gguf_close", "kq_gguf_version", "kq_gguf_alignment",
                             "kq_gguf_tensor_count", "kq_gguf_find_tensor", "kq_gguf_tensor_info",
                             "kq_gguf_upload", "kq_gguf_meta_count", "kq_gguf_meta_key", "kq_gguf_meta_int",
@@ -168,3 +168,21 @@ def test_streamer_argument_errors():
                              ctypes.c_void_p(FAKE)) == -4
     assert L.kq_streamer_sync(None) == -4
     L.kq_streamer_destroy(None)
+
+
+def test_qmoe_multi_argument_errors():
+    L = kq.lib()
+    P2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ids, x = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    call = lambda count, qtype=Q4, W=P2, E=16, N=64, K=256, T=1, k=2, xm=0, Y=P2, ids=ids, x=x: \
+        L.kq_qmoe_gemv_multi(count, qtype, W, E, N, K, ids, T, k, x, xm, Y, None, None)
+    assert call(0) == -6 and call(5) == -6                      # count outside 1..4
+    assert call(2, qtype=3) == -1                               # type
+    assert call(2, K=100) == -2                                 # K not a whole number of blocks
+    assert call(2, T=0) == -3 and call(2, T=9) == -3
+    assert call(2, k=17) == -6 and call(2, E=1) == -6 and call(2, xm=2) == -6
+    assert call(2, W=None) == -4 and call(2, Y=None) == -4 and call(2, ids=None) == -4
+    assert call(2, W=(ctypes.c_void_p * 2)(FAKE, None)) == -4
+    assert call(2, W=(ctypes.c_void_p * 2)(FAKE, ODD)) == -5
+    assert call(2, x=ctypes.c_void_p(ODD)) == -5
+    assert call(2, N=0) == 0                                     # nothing to do: no launch

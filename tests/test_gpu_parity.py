@@ -445,3 +445,26 @@ def test_qmoe_slot_rows_do_not_depend_on_grouping():
             e = ids[t, j]
             yg = gpu_gemv(qtype, Wd[e * per:(e + 1) * per], N, K, x[t:t + 1])
             assert np.array_equal(y[t, j].view(np.uint32), yg[0].view(np.uint32)), (t, j)
+
+
+@pytest.mark.parametrize("T,x_mode,count", [(1, 0, 2), (8, 0, 2), (3, 1, 3), (8, 0, 4)])
+def test_qmoe_multi_equals_separate_calls(T, x_mode, count):
+    # an MoE layer's gate and up projections (and more tensors of the same
+    # shape) in one launch: each output equals its own call bit for bit
+    qtype, E, N, K, k = kqsynth.Q4_K, 24, 160, 1024, 8
+    Ws = [moe_inputs(qtype, E, N, K, T, k, 20 + i, x_mode)[0] for i in range(count)]
+    _, ids, _, x = moe_inputs(qtype, E, N, K, T, k, 20, x_mode)
+    ids[0, 1] = E + 1                                   # one bad id: zeros and the flag
+    Wd = [dev(W.reshape(-1)) for W in Ws]
+    ys = [torch.full((T, k, N), float("nan"), device="cuda") for _ in range(count)]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kq.kq_qmoe_gemv_multi(qtype, Wd, E, N, K, dev(ids), T, k, dev(x), x_mode, ys, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    for i in range(count):
+        one, f1 = gpu_moe(qtype, Wd[i], E, N, K, ids, None, x, x_mode)
+        assert f1 == 1
+        assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), one.view(np.uint32)), i
+        assert np.all(ys[i].cpu().numpy()[0, 1] == 0)
+        yo, S, _ = oracle.moe(qtype, Ws[i], E, N, K, ids, None, x, x_mode)
+        check_close(ys[i].cpu().numpy(), yo, S, "tensor %d" % i)
