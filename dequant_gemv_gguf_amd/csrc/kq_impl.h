@@ -2267,13 +2267,17 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     const int64_t rba = Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK), rbb = Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK);
     // work-groups each format needs for one step per row slot; when both do
     // not fit one per compute unit, the units are split in proportion to the
-    // bytes of each format (each side keeps at least one)
+    // bytes of each format, weighted by its relative time per byte (each side
+    // keeps at least one).  The large-unit formats keep one row step in
+    // flight in this configuration: a weight of 1.8 measured best for the
+    // k+q (Q4_K) beside v (Q6_K) launch (1.3 to 2.0 within 1 %).
     const int64_t need_a = (((int64_t)sa.start[sa.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t need_b = (((int64_t)sb.start[sb.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t cap = cu_count();
     int64_t ga = need_a, gb = need_b;
     if (ga + gb > cap) {
-        const double bytes_a = (double)sa.start[sa.n] * rba, bytes_b = (double)sb.start[sb.n] * rbb;
+        const double wa = BIG_UNIT<TA>() ? 1.8 : 1.0, wb = BIG_UNIT<TB>() ? 1.8 : 1.0;
+        const double bytes_a = (double)sa.start[sa.n] * rba * wa, bytes_b = (double)sb.start[sb.n] * rbb * wb;
         gb = (int64_t)(cap * bytes_b / (bytes_a + bytes_b) + 0.5);
         if (gb < 1) gb = 1;
         if (gb > cap - 1) gb = cap - 1;
