@@ -6,17 +6,17 @@
 //
 // Prior art on the pages: fused dequant-matmul kernels that expand quantized
 // weights only in registers (Kortex summary, section Approach; Kortex article,
-// section Key components, item 3) and native K-quant kernels for Q2_K..Q6_K and
-// Q8_0 (RunNburn post).  Their designs target other hardware; this file is a
-// gfx950 design of the same operation.
+// section Key components, item 3) and native K-quant kernels for Q2_K..Q6_K,
+// Q4_0 and Q8_0 (RunNburn post).  Their designs target other hardware; this
+// file is a gfx950 design of the same operation.
 //
 // Design (memory-bound matvec, one pass over the packed weights):
 //  * Weights are read with 128-bit buffer loads (raw buffer resources give
 //    hardware bounds checks: a read past the tile returns zeros, never faults).
-//    Q6_K and Q8_0 blocks may start 2 bytes off a dword; their fields are
-//    read from the dword-aligned address below and realigned with
+//    Q6_K, Q3_K, Q8_0 and Q4_0 blocks may start 2 bytes off a dword; their
+//    fields are read from the dword-aligned address below and realigned with
 //    v_alignbyte.
-//  * Each lane owns "units" of 64 weights (32 for Q8_0) that share their
+//  * Each lane owns "units" of 64 weights (32 for Q8_0 and Q4_0) that share their
 //    scales; a group of LPR lanes (16, 32 or 64) walks the units of R rows, so
 //    one read of the activations serves R rows.  Unit u of a row always goes
 //    to lane u % LPR in ascending order, whatever M, R or the K chunk, so the
@@ -32,7 +32,9 @@
 //    activation with v_fma_mix_f32, which widens the half exactly.  The
 //    power-of-two factors are folded into the per-sub-block scales.
 //  * Per unit and sub-block: acc += (d*sc) * sum(q*x) - (dmin*m) * sum(x)
-//    (Q6_K: d*sc*(sum(q*x) - 32*sum(x)); Q8_0: d*(sum((q+128)*x) - 128*sum(x))).
+//    (Q6_K: d*sc*(sum(q*x) - 32*sum(x)); Q8_0: d*(sum((q+128)*x) - 128*sum(x));
+//    Q4_0: d*(sum(q*x) - 8*sum(x)); Q3_K: d*sc*(sum((low2 + 4*hbit)*x) -
+//    4*sum(x)) with q = low2 - 4 + 4*hbit; Q5_K as Q4_K with a fifth bit).
 //  * Lane partials are summed with DPP inside 16-lane rows and lane swizzles
 //    across rows; one lane per row group stores y.  No atomics anywhere.
 #pragma once
