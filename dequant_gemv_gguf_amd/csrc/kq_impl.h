@@ -44,7 +44,11 @@
 
 #include "kqgemv.h"
 
+#include <atomic>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 namespace kq {
@@ -1975,11 +1979,26 @@ inline int chunk_for(int M) { return M == 1 ? 8192 : 4096; }
 // Lanes per row: enough that a row of fewer than 64 units fits one stripe.
 inline int lanes_per_row(int units) { return units > 32 ? 64 : (units > 16 ? 32 : 16); }
 
+// Lets kernel k use `bytes` of dynamic LDS on the current device.  The limit
+// is only ever raised, under a lock: with calls from several host threads it
+// never drops below what a launch in flight on another thread needs.
+inline std::mutex &lds_limit_mutex() {
+    static std::mutex mu;
+    return mu;
+}
 template <typename Kern>
 hipError_t allow_lds(Kern k, size_t bytes) {
     if (bytes <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
+    static std::map<std::pair<const void *, int>, size_t> limit;   // (kernel, device) -> bytes allowed
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const void *f = reinterpret_cast<const void *>(k);
+    std::lock_guard<std::mutex> lock(lds_limit_mutex());
+    size_t &cur = limit[{f, dev}];
+    if (bytes <= cur) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) cur = bytes;
+    return e;
 }
 
 template <int T, int M, int R>
@@ -1999,15 +2018,15 @@ int launch_qgemv_t(const void *W, int64_t row_bytes, int N, int K, const float *
 
 // Compute units of the current device (cached per device).
 inline int cu_count() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cache[dev]) {
-        int n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int n = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (!n) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // Batch-1 configurations: a wide one (work-groups up to 16 waves, 4 per SIMD,

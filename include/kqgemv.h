@@ -37,7 +37,9 @@
  *  - Argument errors are returned synchronously as a negative kq_status before
  *    any HIP call is made.  A failed launch returns KQ_ERR_LAUNCH.  Faults in
  *    a kernel surface at the caller's next synchronisation.
- *  - The library holds no state; calls are reentrant and thread-safe.
+ *  - The library holds no per-call state (only caches of each device's compute
+ *    unit count and of the LDS limits granted to its kernels); calls are
+ *    reentrant and thread-safe.
  *  - Alignment: W, W_exps and src 16 B; x, y, dst, workspace 16 B; ids,
  *    route_w, err_flag 4 B.  Rows of Q6_K, Q3_K, Q8_0 and Q4_0 matrices may
  *    start at any even byte offset (e.g. 630-byte rows); that is handled

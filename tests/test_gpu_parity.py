@@ -468,3 +468,46 @@ def test_qmoe_multi_equals_separate_calls(T, x_mode, count):
         assert np.all(ys[i].cpu().numpy()[0, 1] == 0)
         yo, S, _ = oracle.moe(qtype, Ws[i], E, N, K, ids, None, x, x_mode)
         check_close(ys[i].cpu().numpy(), yo, S, "tensor %d" % i)
+
+
+def test_concurrent_host_threads_give_the_same_bits():
+    # calls from several host threads on their own streams, with kernels that
+    # raise their LDS limit (batch-M with long rows, routed experts at T = 8):
+    # every result equals the single-threaded one bit for bit
+    import threading
+    cases = []
+    for i, (qt, N, K, M) in enumerate([(kqsynth.Q4_K, 300, 28672, 8), (kqsynth.Q6_K, 200, 12544, 5),
+                                       (kqsynth.Q4_K, 1000, 8192, 1), (kqsynth.Q2_K, 400, 16384, 3)]):
+        W = dev(qmat(qt, N, K, 80 + i))
+        x = dev(kqsynth.activations(M, K, kqsynth.rng_for(81, i)))
+        cases.append((qt, N, K, M, W, x))
+    ref = []
+    for (qt, N, K, M, W, x) in cases:
+        y = torch.empty((M, N), device="cuda")
+        kq.kq_qgemv(qt, W, N, K, x, M, y)
+        ref.append(y)
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(c):
+        try:
+            st = torch.cuda.Stream()
+            qt, N, K, M, W, x = cases[c]
+            outs = [torch.empty((M, N), device="cuda") for _ in range(6)]
+            with torch.cuda.stream(st):
+                for y in outs:
+                    kq.kq_qgemv(qt, W, N, K, x, M, y, st)
+            st.synchronize()
+            for y in outs:
+                if not torch.equal(y.view(torch.int32), ref[c].view(torch.int32)):
+                    errors.append(c)
+        except Exception as e:          # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(c,)) for c in range(len(cases)) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
