@@ -511,3 +511,23 @@ def test_concurrent_host_threads_give_the_same_bits():
         t.join()
     torch.cuda.synchronize()
     assert not errors, errors
+
+
+@pytest.mark.parametrize("qtype", [kqsynth.Q4_K, kqsynth.Q6_K, kqsynth.Q8_0, kqsynth.Q3_K])
+@pytest.mark.parametrize("M", [1, 3])
+def test_maximum_K(qtype, M):
+    # K = 2^20, the largest K the calls accept: rows longer than any LDS
+    # staging, served by the chunked kernel; K + one block is refused
+    K, N = 1 << 20, 3
+    say("max K", kqsynth.TYPE_NAMES[qtype], "M", M)
+    W = qmat(qtype, N, K, 90)
+    x = kqsynth.activations(M, K, kqsynth.rng_for(91, M))
+    y = gpu_gemv(qtype, W, N, K, x)
+    yo, S = oracle.gemv(qtype, W, N, K, x)
+    check_close(y, yo, S, "K = 2^20")
+    y1 = gpu_gemv(qtype, W, N, K, x[:1])
+    assert np.array_equal(y1[0].view(np.uint32), y[0].view(np.uint32))
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_qgemv(qtype, dev(W[:, :kq.kq_row_bytes(qtype, 256 if qtype != kqsynth.Q8_0 else 32)]), 1,
+                    K + (256 if qtype != kqsynth.Q8_0 else 32), dev(x[:, :1024]), 1, torch.empty(1, 1, device="cuda"))
+    assert e.value.status == -2
