@@ -2036,21 +2036,22 @@ inline int cu_count() {
 // weight) and the 32-weight formats (Q8_0, Q4_0: a scale per 32) take the
 // narrow one when it still holds at least two row slots (32-weight formats:
 // one), which measured faster for Q6_K and Q8_0; with long rows the wide
-// one's extra waves win.  Q4_K (ring of 4) and Q3_K take the narrow one only
-// for launches of at most 8 row steps per wide row slot (a 8192 x 8192
-// matrix, an 8B model's projections), where having every step's loads in
-// flight early matters more than the wide one's extra waves (Q3_K 28672 x
-// 8192: +12 % wide; Q5_K and Q6_K measured better narrow throughout).
+// one's extra waves win.  Q4_K and Q2_K (ring of 4) and Q3_K take the narrow
+// one only for launches of at most 8 row steps per wide row slot (a 8192 x
+// 8192 matrix, an 8B model's projections), where having every step's loads
+// in flight early matters more than the wide one's extra waves (Q3_K 28672 x
+// 8192: +12 % wide; Q2_K 14336 x 4096: +11 % narrow; Q5_K and Q6_K measured
+// better narrow throughout).
 // PREFETCH is the number of row steps each wave keeps in flight; it must
 // divide every lanes-per-row value (16, 32, 64).
 template <int T, bool WIDE> constexpr int PREFETCH() {
-    return WIDE ? (BIG_UNIT<T>() ? 1 : 2) : (Fmt<T>::QK == 32 || T == T_Q4_K ? 4 : 2);
+    return WIDE ? (BIG_UNIT<T>() ? 1 : 2) : (Fmt<T>::QK == 32 || T == T_Q4_K || T == T_Q2_K ? 4 : 2);
 }
 template <int T> constexpr int NARROW_MAX_STRIPES() {
-    return BIG_UNIT<T>() ? 4 : (Fmt<T>::QK == 32 ? 8 : (T == T_Q4_K ? 2 : 0));
+    return BIG_UNIT<T>() ? 4 : (Fmt<T>::QK == 32 ? 8 : (T == T_Q4_K || T == T_Q2_K ? 2 : 0));
 }
 // formats that take the narrow configuration only for short launches
-template <int T> constexpr bool NARROW_SHORT_ONLY() { return T == T_Q4_K || T == T_Q3_K; }
+template <int T> constexpr bool NARROW_SHORT_ONLY() { return T == T_Q4_K || T == T_Q3_K || T == T_Q2_K; }
 constexpr int64_t SHORT_LAUNCH_STEPS = 8;
 
 struct B1Cfg {
