@@ -264,14 +264,16 @@ def test_qgemv_multi_mixed_full_size_attention_input():
         check_close(ys[i].cpu().numpy()[:, rows], yo, S, "matrix %d" % i)
 
 
-def test_qgemv_multi_full_size_projections():
-    # a 70B layer's k and q projections (Q4_K, K = 8192) in one launch
+@pytest.mark.parametrize("Ns,M", [([1024, 8192], 1), ([28672, 28672], 1), ([28672, 28672], 2)],
+                         ids=["wk+wq", "w1+w3", "w1+w3-M2"])
+def test_qgemv_multi_full_size_projections(Ns, M):
+    # a 70B layer's k and q projections, or its gate and up projections
+    # (Q4_K, K = 8192), in one launch as the bench issues them
     K = 8192
-    Ns = [1024, 8192]
     Ws = [kqsynth.device_matrix(kqsynth.Q4_K, n, K, seed=60 + i, device="cuda") for i, n in enumerate(Ns)]
-    x = kqsynth.activations(1, K, kqsynth.rng_for(61))
-    ys = [torch.empty((1, n), device="cuda") for n in Ns]
-    kq.kq_qgemv_multi(kqsynth.Q4_K, Ws, Ns, K, dev(x), 1, ys)
+    x = kqsynth.activations(M, K, kqsynth.rng_for(61, M))
+    ys = [torch.empty((M, n), device="cuda") for n in Ns]
+    kq.kq_qgemv_multi(kqsynth.Q4_K, Ws, Ns, K, dev(x), M, ys)
     torch.cuda.synchronize()
     for i, n in enumerate(Ns):
         one = gpu_gemv(kqsynth.Q4_K, Ws[i], n, K, x)
