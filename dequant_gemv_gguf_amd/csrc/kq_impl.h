@@ -44,6 +44,7 @@
 
 #include "kqgemv.h"
 
+#include <algorithm>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -1281,18 +1282,41 @@ template <bool MS> __device__ __forceinline__ int seg_of(const Segs &sg, int row
     return s;
 }
 
+// The segment of the rows a wave loads.  A wave's row steps mostly move
+// forward, so the cursor keeps the current segment's fields and compares the
+// row with the next segment's start; the fields of another segment are read
+// only when the row leaves the current one.  (Reading them through a computed
+// index at every step puts two dependent scalar-memory loads and their waits
+// in front of each step's weight loads.)  `row` is uniform over the wave.
+template <bool MS> struct SegCursor {
+    const uint8_t *W;
+    int s, start, rows, next;
+    __device__ __forceinline__ void set(const Segs &sg, int i) {
+        s = i;
+        W = sg.W[i];
+        start = sg.start[i];
+        rows = sg.rows[i];
+        next = (MS && i + 1 < sg.n) ? sg.start[i + 1] : 0x7fffffff;
+    }
+    __device__ __forceinline__ void seek(const Segs &sg, int row) {
+        if (!MS) return;
+        if ((unsigned)(row - start) >= (unsigned)(next - start)) set(sg, seg_of<MS>(sg, row));
+    }
+};
+
 // Issue the loads of one row step (rows row0 .. row0 + G - 1, one per lane
 // group).  Never conditional: a step past the last row gets an empty buffer
 // (its loads return zeros), so the loads of every ring slot stay in flight in
 // program order.
 template <int T, bool MS>
-__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, const Segs &sg, int64_t row_bytes,
-                                           int N, int G, int row0, int grp, bool act, u32 boff, int sub) {
-    const int sgi = seg_of<MS>(sg, row0 < N ? row0 : 0);
-    const int local = row0 - sg.start[sgi];
-    const int left = sg.rows[sgi] - local;
+__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, SegCursor<MS> &cur, const Segs &sg,
+                                           int64_t row_bytes, int N, int G, int row0, int grp, bool act, u32 boff,
+                                           int sub) {
+    cur.seek(sg, row0);
+    const int local = row0 - cur.start;
+    const int left = cur.rows - local;
     const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
-    const uintptr_t ta = (uintptr_t)(sg.W[sgi] + (int64_t)(nr ? local : 0) * row_bytes);
+    const uintptr_t ta = (uintptr_t)(cur.W + (int64_t)(nr ? local : 0) * row_bytes);
     const u32 delta = (u32)(ta & 3u);
     const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
     load_unit(raw, rs, (act && grp < nr) ? delta + (u32)((int64_t)grp * row_bytes) + boff : OOB, sub);
@@ -1353,6 +1377,7 @@ template <int T, int D, bool MS> struct B1Pass {
     int N, lpr, ns, wave, lane, rsl, stripe, G, grp, slot, sub, rstride, first, wsteps, uc;
     bool act;
     u32 boff;
+    SegCursor<MS> cur;
     Raw ring[D][1];
 
     // wg / nwg: this work-group's index among the nwg that share the rows
@@ -1379,9 +1404,10 @@ template <int T, int D, bool MS> struct B1Pass {
         // run past N on empty buffers and store nothing
         const int f0 = wg * RS * G;
         wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
+        cur.set(sg, 0);
     }
     __device__ __forceinline__ void issue(int d, int step) {
-        issue_step<T, MS>(ring[d][0], sg, row_bytes, N, G, first + step * rstride, grp, act, boff, sub);
+        issue_step<T, MS>(ring[d][0], cur, sg, row_bytes, N, G, first + step * rstride, grp, act, boff, sub);
     }
     __device__ __forceinline__ void issue_first() {
 #pragma unroll
@@ -1485,8 +1511,8 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
 // serve the rows of format TB, the others those of format TA, side by side
 // (the host splits the grid in proportion to the bytes of each); each stages
 // the activations and makes one pass.
-template <int TA, int DA, int TB, int DB>
-__global__ __launch_bounds__(1024) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
+template <int TA, int DA, int TB, int DB, int LB>
+__global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
                                                            int gb, int K, int lpr, int ns,
                                                            const float *__restrict__ x) {
     extern __shared__ float smem[];
@@ -1524,14 +1550,14 @@ template <bool MS> __device__ __forceinline__ float *out_m(const Segs &sg, int N
 }
 
 template <int T, int R, bool MS>
-__device__ __forceinline__ void issue_rows(typename RawOf<T>::type (&raw)[R], const Segs &sg, int64_t row_bytes,
-                                           int N, int RG, int row0, bool live, int grp, bool act, u32 boff,
-                                           int sub) {
-    const int sgi = seg_of<MS>(sg, row0 < N ? row0 : 0);
-    const int local = row0 - sg.start[sgi];
-    const int left = sg.rows[sgi] - local;
+__device__ __forceinline__ void issue_rows(typename RawOf<T>::type (&raw)[R], SegCursor<MS> &cur, const Segs &sg,
+                                           int64_t row_bytes, int N, int RG, int row0, bool live, int grp, bool act,
+                                           u32 boff, int sub) {
+    cur.seek(sg, row0);
+    const int local = row0 - cur.start;
+    const int left = cur.rows - local;
     const int nr = (!live || row0 >= N || left <= 0) ? 0 : (left < RG ? left : RG);
-    const uintptr_t ta = (uintptr_t)(sg.W[sgi] + (int64_t)(nr ? local : 0) * row_bytes);
+    const uintptr_t ta = (uintptr_t)(cur.W + (int64_t)(nr ? local : 0) * row_bytes);
     const u32 delta = (u32)(ta & 3u);
     const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
 #pragma unroll
@@ -1584,6 +1610,8 @@ __global__ __launch_bounds__(512) void qgemvm_kernel(const Segs sg, int64_t row_
             }
         }
     };
+    SegCursor<MS> cur;
+    cur.set(sg, 0);
     auto issue = [&](Raw (&raw)[R], int c, int j, int st) {
         const int ul = st * lpr + slot;
         const int uc_n = c < nchunks - 1 ? ub_chunk : units_last;
@@ -1591,7 +1619,7 @@ __global__ __launch_bounds__(512) void qgemvm_kernel(const Segs sg, int64_t row_
         const int ug = c * ub_chunk + (act ? ul : 0);
         const u32 boff = (u32)(ug / F::UPB) * F::BYTES;
         const int row0 = ((j * gridDim.x + blockIdx.x) * NW + wave) * RG;
-        issue_rows<T, R, MS>(raw, sg, row_bytes, N, RG, row0, c < nchunks, grp, act, boff, sub);
+        issue_rows<T, R, MS>(raw, cur, sg, row_bytes, N, RG, row0, c < nchunks, grp, act, boff, sub);
     };
 
     Raw ring[D][R];
@@ -2287,30 +2315,45 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     Segs sa, sb;
     next_segs(ia, pa, W, N, y, G, &sa);
     next_segs(ib, pb, W, N, y, G, &sb);
+    // the 8-wave configuration when each format would take it for its own rows
+    // (short launches of Q4_K, Q3_K and Q2_K; rows of few stripes otherwise)
+    B1Cfg na, nb;
+    const bool narrow = batch1_cfg<TA>(K, sa.start[sa.n], &na) && batch1_cfg<TB>(K, sb.start[sb.n], &nb) &&
+                        !na.wide && !nb.wide && na.rs == nb.rs;
+    if (narrow) ca = na;
     const int64_t rba = Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK), rbb = Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK);
     // work-groups each format needs for one step per row slot; when both do
-    // not fit one per compute unit, the units are split in proportion to the
-    // bytes of each format, weighted by its relative time per byte (each side
-    // keeps at least one).  The large-unit formats keep one row step in
-    // flight in this configuration: a weight of 1.8 measured best for the
-    // k+q (Q4_K) beside v (Q6_K) launch (1.3 to 2.0 within 1 %).
+    // not fit one per compute unit, the units are split so that the slowest
+    // work-group finishes first: a work-group makes a whole number of row
+    // steps, each costing its format's row bytes weighted by the format's
+    // relative time per byte, and ties go to the split closer to proportional.
+    // The large-unit formats keep one row step in flight in the 16-wave
+    // configuration (weight 1.8) and two in the 8-wave one (weight 1.1).
     const int64_t need_a = (((int64_t)sa.start[sa.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t need_b = (((int64_t)sb.start[sb.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t cap = cu_count();
     int64_t ga = need_a, gb = need_b;
     if (ga + gb > cap) {
-        const double wa = BIG_UNIT<TA>() ? 1.8 : 1.0, wb = BIG_UNIT<TB>() ? 1.8 : 1.0;
-        const double bytes_a = (double)sa.start[sa.n] * rba * wa, bytes_b = (double)sb.start[sb.n] * rbb * wb;
-        gb = (int64_t)(cap * bytes_b / (bytes_a + bytes_b) + 0.5);
-        if (gb < 1) gb = 1;
-        if (gb > cap - 1) gb = cap - 1;
-        if (gb > need_b) gb = need_b;
+        const double big = narrow ? 1.1 : 1.8;
+        const double wa = (BIG_UNIT<TA>() ? big : 1.0) * rba, wb = (BIG_UNIT<TB>() ? big : 1.0) * rbb;
+        double best = 0, best_even = 0;
+        for (int64_t b = 1; b < cap && b <= need_b; ++b) {
+            const int64_t a = cap - b;
+            const double t = std::max((double)((need_a + a - 1) / a) * wa, (double)((need_b + b - 1) / b) * wb);
+            const double even = std::max((double)need_a / a * wa, (double)need_b / b * wb);
+            if (b == 1 || t < best || (t == best && even < best_even)) {
+                best = t;
+                best_even = even;
+                gb = b;
+            }
+        }
         ga = cap - gb < need_a ? cap - gb : need_a;
     }
     const int grid = (int)(ga + gb);
     if (grid == 0) return KQ_OK;
     const size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
-    auto kern = qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>()>;
+    auto kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512>
+                       : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, rba, sb, rbb, (int)gb, K, ca.lpr,
                        ca.ns, x);

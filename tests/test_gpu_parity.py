@@ -186,7 +186,7 @@ MULTI = [
 
 
 @pytest.mark.parametrize("case", MULTI, ids=lambda c: "%s-K%d-%d" % (kqsynth.TYPE_NAMES[c[0]], c[1], len(c[2])))
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 3, 8])
 def test_qgemv_multi_equals_separate_calls(case, M):
     qtype, K, Ns = case
     say("qgemv_multi", kqsynth.TYPE_NAMES[qtype], "K", K, "Ns", Ns, "M", M)
@@ -219,6 +219,8 @@ MIXED = [
             (kqsynth.Q4_K, 7)]),
     (1280, [(kqsynth.Q4_0, 7), (kqsynth.Q5_K, 64), (kqsynth.Q4_K, 3), (kqsynth.Q8_0, 5)]),
     (768, [(kqsynth.Q3_K, 70), (kqsynth.Q4_K, 9)]),
+    # five stripes per row: the 16-wave configuration for both formats
+    (20480, [(kqsynth.Q5_K, 40), (kqsynth.Q6_K, 21), (kqsynth.Q5_K, 7)]),
 ]
 
 
@@ -246,10 +248,14 @@ def test_qgemv_multi_mixed_formats(case, M):
         check_close(got, yo, S, "matrix %d" % i)
 
 
-def test_qgemv_multi_mixed_full_size_attention_input():
-    # a 70B layer's k, v and q projections in one launch (Q4_K, Q6_K, Q4_K)
+@pytest.mark.parametrize("mats", [[(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)],
+                                  [(kqsynth.Q4_K, 20480), (kqsynth.Q6_K, 1024)]], ids=["wk+wv+wq", "long-Q4_K"])
+def test_qgemv_multi_mixed_full_size(mats):
+    # a 70B layer's k, v and q projections in one launch (Q4_K, Q6_K, Q4_K:
+    # the 8-wave configuration), and Q4_K rows too many for it beside Q6_K
+    # rows (the 16-wave one)
     K = 8192
-    mats = [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)]
+    say("qgemv_multi mixed full size", mats)
     Ws = [kqsynth.device_matrix(t, n, K, seed=70 + i, device="cuda") for i, (t, n) in enumerate(mats)]
     x = kqsynth.activations(1, K, kqsynth.rng_for(71))
     ys = [torch.empty((1, n), device="cuda") for _, n in mats]
