@@ -1788,6 +1788,107 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const MoeSet set, int6
     }
 }
 
+// Routed experts, token-major: work-group (row tile, token t, expert tensor);
+// wave w serves slots w, w + MOEC_WAVES, ... of token t over the tile's rows,
+// each row summed in the canonical order.  Per-slot outputs (rw NULL) are
+// stored as they are; otherwise they go to LDS and
+// y[t][row] = sum_j rw[t][j] * s_j[row], ascending j, one fma per term from
+// +0 -- the arithmetic of the separate combine, so the bits are the same.
+// An expert routed to several tokens is read once per token (the slot-major
+// kernel reads it once per batch of 8), which the full-width grid and, for
+// the sum, the saved launch repay.  Invalid ids: the slot gives zero and sets
+// the flag.
+constexpr int MOEC_WAVES = 8;
+constexpr int MOEC_R = 2;          // rows per lane group per step
+template <int T>
+__global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
+    const MoeSet set, int64_t row_bytes, int E, int N, int K, int lpr, int RT, const int32_t *__restrict__ ids,
+    const float *__restrict__ rw, int k, const float *__restrict__ x, int x_mode, int32_t *err_flag) {
+    typedef Fmt<T> F;
+    typedef typename RawOf<T>::type Raw;
+    extern __shared__ float smem[];
+    const int T_ = gridDim.y / set.n;
+    const int ti = blockIdx.y / T_, t = blockIdx.y - ti * T_;
+    const uint8_t *__restrict__ W = set.W[ti];
+    float *__restrict__ y = set.y[ti];
+    const int row0 = blockIdx.x * RT;
+    const int nrows = (N - row0) < RT ? (N - row0) : RT;
+    const int XS = x_stride(K), SS = s_stride(K);
+    const int nx = x_mode ? k : 1;                 // activation rows staged
+    float *xs = smem, *ss = smem + nx * XS, *res = ss + nx * SS;
+    {
+        const int n16 = K >> 4;
+        for (int idx = threadIdx.x; idx < nx * n16; idx += blockDim.x) {
+            const int m = idx / n16, j = idx - m * n16;
+            const f4 *src = reinterpret_cast<const f4 *>(x + (int64_t)(x_mode ? t * k + m : t) * K + 16 * j);
+            const f4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+            f4 *dst = reinterpret_cast<f4 *>(xs + m * XS + xpad(16 * j));
+            dst[0] = v0;
+            dst[1] = v1;
+            dst[2] = v2;
+            dst[3] = v3;
+            ss[m * SS + j] = sum16(v0, v1, v2, v3);
+        }
+    }
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int G = 64 / lpr, grp = lane / lpr, slot = lane - grp * lpr;
+    const int units = (K / F::QK) * F::UPB;
+    const int nstripes = (units + lpr - 1) / lpr;
+    for (int j = wave; j < k; j += MOEC_WAVES) {
+        // slot j's results: LDS for the sum, else its output row
+        float *out = rw ? res + j * RT : y + ((int64_t)t * k + j) * N + row0;
+        const int e = ids[t * k + j];
+        if (e < 0 || e >= E) {                     // uniform over the wave
+            for (int i = lane; i < nrows; i += 64) out[i] = 0.f;
+            if (err_flag && lane == 0) *err_flag = 1;
+            continue;
+        }
+        const float *xj = xs + (x_mode ? j : 0) * XS, *sj = ss + (x_mode ? j : 0) * SS;
+        const uintptr_t ta = (uintptr_t)(W + ((int64_t)e * N + row0) * row_bytes);
+        const u32 delta = (u32)(ta & 3u);
+        const rsrc_t rs = make_rsrc((const void *)(ta - delta), delta + (u32)((int64_t)nrows * row_bytes));
+        for (int r0 = 0; r0 < nrows; r0 += G * MOEC_R) {
+            u32 roff[MOEC_R];
+            float acc[MOEC_R];
+#pragma unroll
+            for (int r = 0; r < MOEC_R; ++r) {
+                const int rr = r0 + grp * MOEC_R + r;
+                roff[r] = rr < nrows ? delta + (u32)((int64_t)rr * row_bytes) : OOB;
+                acc[r] = 0.f;
+            }
+            for (int i = 0; i < nstripes; ++i) {
+                const int ul = slot + lpr * i;
+                const bool act = ul < units;
+                const int uc = act ? ul : 0;
+                const int sub = uc % F::UPB;
+                const u32 boff = (u32)(uc / F::UPB) * F::BYTES;
+                Raw raw[MOEC_R];
+#pragma unroll
+                for (int r = 0; r < MOEC_R; ++r) load_unit(raw[r], rs, act ? roff[r] + boff : OOB, sub);
+                const int e0 = unit_e0<T>(uc);
+                const XLds xa{xj, sj, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+                float v[MOEC_R][1];
+                val_unit<1, MOEC_R>(raw, sub, xa, v);
+#pragma unroll
+                for (int r = 0; r < MOEC_R; ++r) acc[r] += group_sum(act ? v[r][0] : 0.f, lpr);
+            }
+#pragma unroll
+            for (int r = 0; r < MOEC_R; ++r) {
+                const int rr = r0 + grp * MOEC_R + r;
+                if (slot == 0 && rr < nrows) out[rr] = acc[r];
+            }
+        }
+    }
+    if (!rw) return;                               // uniform
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows; i += blockDim.x) {
+        float a = 0.f;
+        for (int j = 0; j < k; ++j) a = __builtin_fmaf(rw[t * k + j], res[j * RT + i], a);
+        y[(int64_t)t * N + row0 + i] = a;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Standalone dequantization, one unit per thread.  Each weight is the exact
 // product(s) with a single rounding at the subtraction; + 0.0f maps -0 to +0.
@@ -2388,6 +2489,32 @@ int launch_qmoe_m(int maxm, const MoeSet &set, int64_t row_bytes, int E, int N, 
     }
 }
 
+// The token-major routed-expert kernel (qmoe_tok_kernel) for T tokens and
+// set.n expert tensors, when the activation rows a work-group stages (and the
+// slot sums of a row tile, with rw) fit its LDS budget; KQ_ERR_ARG otherwise
+// (the caller then uses the slot-major kernel).  Row tiles of G * 2 * S rows,
+// S as large as keeps at least two work-groups per compute unit.
+constexpr size_t MOEC_LDS_MAX = 64 * 1024;
+template <int T>
+int launch_qmoe_tok_t(const MoeSet &set, int64_t row_bytes, int E, int N, int K, const int32_t *ids, const float *rw,
+                      int T_, int k, const float *x, int x_mode, int32_t *err, hipStream_t st) {
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int step = (64 / lpr) * MOEC_R;
+    const int64_t per_tile = (int64_t)T_ * set.n;
+    int S = 1;
+    while (S < 4 && (int64_t)((N + 2 * S * step - 1) / (2 * S * step)) * per_tile >= 2 * cu_count()) S *= 2;
+    const int RT = S * step;
+    const int nx = x_mode ? k : 1;
+    const size_t lds = ((size_t)nx * (x_stride(K) + s_stride(K)) + (rw ? (size_t)k * RT : 0)) * sizeof(float);
+    if (lds > MOEC_LDS_MAX) return KQ_ERR_ARG;
+    auto kern = qmoe_tok_kernel<T>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3((N + RT - 1) / RT, (unsigned)per_tile), dim3(64 * MOEC_WAVES), lds, st, set,
+                       row_bytes, E, N, K, lpr, RT, ids, rw, k, x, x_mode, err);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
 template <int T>
 int launch_dequant_t(const void *src, int64_t n, float *dst, hipStream_t st) {
     const int64_t nunits = (n / Fmt<T>::QK) * Fmt<T>::UPB;
@@ -2406,6 +2533,8 @@ int launch_dequant_t(const void *src, int64_t n, float *dst, hipStream_t st) {
     X int launch_qgemv_m<T>(int, const void *, int64_t, int, int, const float *, float *, hipStream_t);          \
     X int launch_qmoe_m<T>(int, const MoeSet &, int64_t, int, int, int, const int32_t *, int, int, const float *, \
                            int, int32_t *, hipStream_t);                                                        \
+    X int launch_qmoe_tok_t<T>(const MoeSet &, int64_t, int, int, int, const int32_t *, const float *, int, int,    \
+                               const float *, int, int32_t *, hipStream_t);                                        \
     X int launch_dequant_t<T>(const void *, int64_t, float *, hipStream_t);
 #define KQ_MIXED_LAUNCHER(X, A, B)                                                                               \
     X int launch_mixed<A, B>(const std::vector<int> &, size_t *, const std::vector<int> &, size_t *,              \

@@ -211,8 +211,16 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, 
     hipStream_t st = (hipStream_t)stream;
     MoeSet set = {};
     set.W[0] = (const uint8_t *)W_exps;
-    set.y[0] = route_w ? workspace : y;
+    set.y[0] = y;
     set.n = 1;
+    // token-major, with the routing-weighted sums in the same launch, when the
+    // activation rows fit; otherwise slot-major, then the separate sum
+    r = with_type(type, [&](auto tag) {
+        return launch_qmoe_tok_t<decltype(tag)::value>(set, row_bytes, (int)E, (int)N, (int)K, ids, route_w, T, k,
+                                                       x, x_mode, err_flag, st);
+    });
+    if (r != KQ_ERR_ARG) return r;
+    set.y[0] = route_w ? workspace : y;
     // a batch never holds more slots than there are tokens unless a token
     // repeats an expert; MAXM = T covers the distinct-ids case in one pass
     const int maxm = T;
@@ -250,8 +258,12 @@ int kq_qmoe_gemv_multi(int count, int type, const void *const *W_exps, int64_t E
     set.n = count;
     if (!aligned(x, 16) || !aligned(ids, 4) || (err_flag && !aligned(err_flag, 4))) return KQ_ERR_ALIGN;
     return with_type(type, [&](auto tag) {
-        return launch_qmoe_m<decltype(tag)::value>(T, set, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode,
-                                                   err_flag, (hipStream_t)stream);
+        constexpr int TT = decltype(tag)::value;
+        const int rt = launch_qmoe_tok_t<TT>(set, row_bytes, (int)E, (int)N, (int)K, ids, nullptr, T, k, x, x_mode,
+                                             err_flag, (hipStream_t)stream);
+        if (rt != KQ_ERR_ARG) return rt;
+        return launch_qmoe_m<TT>(T, set, row_bytes, (int)E, (int)N, (int)K, ids, T, k, x, x_mode, err_flag,
+                                 (hipStream_t)stream);
     });
 }
 

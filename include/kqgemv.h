@@ -152,13 +152,23 @@ size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N);
  *   route_w NULL: y is [T][k][N], y[t][j] = W_exps[ids[t][j]] . x_(t,j).
  *           non-NULL: [T][k] fp32 routing weights, y is [T][N],
  *           y[t] = sum_j route_w[t][j] * W_exps[ids[t][j]] . x_(t,j), summed
- *           in ascending j; `workspace` must then hold
- *           kq_qmoe_workspace_bytes(T, k, N) bytes (its contents are scratch).
+ *           in ascending j, one fused multiply-add per term starting from
+ *           +0; `workspace` must then hold kq_qmoe_workspace_bytes(T, k, N)
+ *           bytes (its contents are scratch).  When a token's activation
+ *           rows fit the kernel's LDS budget (below) the products and the sum
+ *           run in one launch and the workspace is not touched; otherwise the
+ *           per-slot results go through the workspace to a second launch.
+ *           Either way the result has the same bits.
  *   err_flag NULL or a device int32 the kernel sets to 1 (plain store) when
  *           an id is outside [0, E); such a slot contributes zero.  It is
  *           never cleared by the library.
- * 1 <= T <= 8, 1 <= k <= 16, k <= E.  Slots that route to the same expert are
- * served by one pass over that expert's weights (up to 8 slots per pass).
+ * 1 <= T <= 8, 1 <= k <= 16, k <= E.  When a token's activation rows (k rows
+ * with x_mode 1, one with x_mode 0) and, with route_w, the per-slot sums of a
+ * row tile fit the kernel's 64 KB LDS budget (about 14,000 activations: k = 16
+ * rows of K = 768, or one row of K = 12288), each token's slots are served
+ * together, an expert routed to several tokens being read once per token;
+ * otherwise slots that route to the same expert are served by one pass over
+ * that expert's weights (up to 8 slots per pass).
  * Results per slot are bit-identical to kq_qgemv with M = 1 on the expert's
  * matrix and that slot's activation row. */
 int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,

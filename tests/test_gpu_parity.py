@@ -6,6 +6,8 @@ chunks, 2-byte-aligned rows (Q6_K with K = 768, Q8_0 with an odd block count)
 and the degenerate cases (one block, one row, N = 0)."""
 import sys
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -453,6 +455,71 @@ def test_qmoe_slot_rows_do_not_depend_on_grouping():
             e = ids[t, j]
             yg = gpu_gemv(qtype, Wd[e * per:(e + 1) * per], N, K, x[t:t + 1])
             assert np.array_equal(y[t, j].view(np.uint32), yg[0].view(np.uint32)), (t, j)
+
+
+def fma_f32(a, b, c):
+    """fp32 fused multiply-add, exact: a*b + c rounded once to nearest, ties
+    to even (subnormals kept), from exact rational arithmetic."""
+    q = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))
+    if q == 0:
+        neg = (np.signbit(a) != np.signbit(b)) and np.signbit(c)
+        return np.float32(-0.0 if neg else 0.0)
+    neg, q = q < 0, abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    ulp = max(e - 23, -149)
+    scaled = q / Fraction(2) ** ulp
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = np.float32(float(n) * 2.0 ** ulp)
+    return -v if neg else v
+
+
+def test_fma_f32_helper():
+    # the rounding helper itself: exact cases, ties, subnormals
+    assert fma_f32(np.float32(3), np.float32(5), np.float32(1)) == 16
+    one, eps = np.float32(1), np.float32(2.0 ** -24)
+    assert fma_f32(one, eps, one) == 1                       # tie to even: stays 1
+    assert fma_f32(one, np.float32(3 * 2.0 ** -24), one) == np.float32(1 + 2.0 ** -22)
+    tiny = np.float32(2.0 ** -100)
+    assert fma_f32(tiny, np.float32(2.0 ** -48), np.float32(0)) == np.float32(2.0 ** -148)    # subnormal, exact
+    assert fma_f32(tiny, np.float32(2.0 ** -50), np.float32(0)) == 0                           # half the least: even
+    assert fma_f32(tiny, np.float32(3 * 2.0 ** -51), np.float32(0)) == np.float32(2.0 ** -149)
+    assert fma_f32(np.float32(-2), np.float32(0), np.float32(0)).tobytes() == np.float32(0).tobytes()
+    rng = np.random.default_rng(3)
+    for a, b, c in rng.standard_normal((200, 3)).astype(np.float32):
+        ref = np.float32(np.float64(a) * np.float64(b) + np.float64(c))   # exact product, one f64 rounding
+        got = fma_f32(a, b, c)
+        assert abs(float(got) - float(ref)) <= abs(float(ref)) * 2.0 ** -23
+
+
+@pytest.mark.parametrize("case", [(kqsynth.Q6_K, 20, 96, 768, 1, 8, 1), (kqsynth.Q6_K, 20, 200, 768, 3, 12, 1),
+                                  (kqsynth.Q4_K, 12, 72, 512, 2, 6, 0), (kqsynth.Q2_K, 40, 40, 4096, 1, 16, 1)],
+                         ids=["one-launch", "k12-two-slots-per-wave", "shared-x", "two-launch"])
+def test_qmoe_combine_bits(case):
+    # the routing-weighted sum equals the per-slot outputs summed in ascending
+    # slot order, one fp32 fma per term from +0, bit for bit -- whether the
+    # sum runs in the products' launch or in a second one (the last case's
+    # activation rows do not fit the one-launch kernel); a bad id adds zero
+    qtype, E, N, K, T, k, x_mode = case
+    say("qmoe combine bits", kqsynth.TYPE_NAMES[qtype], E, N, K, T, k, x_mode)
+    W, ids, p, x = moe_inputs(qtype, E, N, K, T, k, 14, x_mode)
+    ids[T - 1, k - 1] = E
+    Wd = dev(W.reshape(-1))
+    ys, f1 = gpu_moe(qtype, Wd, E, N, K, ids, None, x, x_mode)
+    y, f2 = gpu_moe(qtype, Wd, E, N, K, ids, p, x, x_mode)
+    assert f1 == 1 and f2 == 1
+    for t in range(T):
+        for o in range(N):
+            acc = np.float32(0)
+            for j in range(k):
+                acc = fma_f32(p[t, j], ys[t, j, o], acc)
+            assert acc.tobytes() == y[t, o].tobytes(), (t, o)
+    yo, S, _ = oracle.moe(qtype, W, E, N, K, ids, p, x, x_mode)
+    check_close(y, yo, S, "combined")
 
 
 @pytest.mark.parametrize("T,x_mode,count", [(1, 0, 2), (8, 0, 2), (3, 1, 3), (8, 0, 4)])
