@@ -1799,7 +1799,7 @@ __global__ __launch_bounds__(WG_THREADS) void qmoe_kernel(const MoeSet set, int6
 // the sum, the saved launch repay.  Invalid ids: the slot gives zero and sets
 // the flag.
 constexpr int MOEC_WAVES = 8;
-constexpr int MOEC_R = 2;          // rows per lane group per step
+constexpr int MOEC_R = 1;          // rows per lane group per step (1: measured best, few VGPRs)
 template <int T>
 __global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
     const MoeSet set, int64_t row_bytes, int E, int N, int K, int lpr, int RT, const int32_t *__restrict__ ids,
@@ -2492,7 +2492,7 @@ int launch_qmoe_m(int maxm, const MoeSet &set, int64_t row_bytes, int E, int N, 
 // The token-major routed-expert kernel (qmoe_tok_kernel) for T tokens and
 // set.n expert tensors, when the activation rows a work-group stages (and the
 // slot sums of a row tile, with rw) fit its LDS budget; KQ_ERR_ARG otherwise
-// (the caller then uses the slot-major kernel).  Row tiles of G * 2 * S rows,
+// (the caller then uses the slot-major kernel).  Row tiles of G * MOEC_R * S rows,
 // S as large as keeps at least two work-groups per compute unit.
 constexpr size_t MOEC_LDS_MAX = 64 * 1024;
 template <int T>
