@@ -545,6 +545,33 @@ def test_qmoe_multi_equals_separate_calls(T, x_mode, count):
         check_close(ys[i].cpu().numpy(), yo, S, "tensor %d" % i)
 
 
+def test_qmoe_slot_major_path_bits():
+    # activation rows too large for the token-major kernel (k = 4 rows of
+    # K = 8192 per token): the slot-major kernel serves the call, alone and
+    # grouped, and every slot still equals a batch-1 product bit for bit
+    qtype, E, N, K, T, k = kqsynth.Q4_K, 12, 96, 8192, 2, 4
+    say("qmoe slot-major", E, N, K, T, k)
+    Ws = [moe_inputs(qtype, E, N, K, T, k, 30 + i, 1)[0] for i in range(2)]
+    _, ids, p, x = moe_inputs(qtype, E, N, K, T, k, 30, 1)
+    ids[1, :] = ids[0, :]                               # both tokens share their experts
+    Wd = [dev(W.reshape(-1)) for W in Ws]
+    per = N * kqsynth.row_bytes(qtype, K)
+    ys = [torch.full((T, k, N), float("nan"), device="cuda") for _ in range(2)]
+    kq.kq_qmoe_gemv_multi(qtype, Wd, E, N, K, dev(ids), T, k, dev(x), 1, ys, None)
+    torch.cuda.synchronize()
+    for i in range(2):
+        one, _ = gpu_moe(qtype, Wd[i], E, N, K, ids, None, x, 1)
+        assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), one.view(np.uint32)), i
+        for t in range(T):
+            for j in range(k):
+                e = ids[t, j]
+                yg = gpu_gemv(qtype, Wd[i][e * per:(e + 1) * per], N, K, x[t * k + j:t * k + j + 1])
+                assert np.array_equal(one[t, j].view(np.uint32), yg[0].view(np.uint32)), (i, t, j)
+    yc, _ = gpu_moe(qtype, Wd[0], E, N, K, ids, p, x, 1)
+    yo, S, _ = oracle.moe(qtype, Ws[0], E, N, K, ids, p, x, 1)
+    check_close(yc, yo, S, "slot-major combined")
+
+
 def test_concurrent_host_threads_give_the_same_bits():
     # calls from several host threads on their own streams, with kernels that
     # raise their LDS limit (batch-M with long rows, routed experts at T = 8):
