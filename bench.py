@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved weight GB/s (% of 8 TB/s HBM) + equiv tok/s, 70B-layer Q4_K_M GEMV M=1"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRCS = [os.path.join(ROOT, "dequant_gemv_gguf_amd", "csrc", f) for f in ("kq_impl.h", "kq_inst.hip", "kqgemv.hip")]
+KERNEL_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqgemv.so")
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
@@ -87,11 +87,13 @@ def check(status):
         raise RuntimeError("kq_qgemv_multi failed with status %d" % status)
 
 
-def source_hash():
+def library_hash():
+    """Hash of the built library (its kernels and launch logic): traffic
+    counters taken with another build are not reported.  The build is
+    deterministic, so an edit that changes no code keeps the hash."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    with open(KERNEL_LIB, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -117,7 +119,7 @@ def summarize_pmc(args):
     """Traffic of the dominant kernel from a FETCH_SIZE and a WRITE_SIZE pass.
     Each counter is calibrated on the 1 GiB copy the passes ran first: the
     factor is 1 GiB over what the counter read for it."""
-    result = {"kernel": "qgemv1_kernel Q4_K (M=1)", "kernel_source_sha256_16": source_hash(),
+    result = {"kernel": "qgemv1_kernel Q4_K (M=1)", "library_sha256_16": library_hash(),
               "workload": args.workload, "command": args.pmc_command}
     per = {}
     for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),
@@ -425,7 +427,7 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as f:
             t = json.load(f)
-        if t.get("kernel_source_sha256_16") == source_hash():
+        if t.get("library_sha256_16") == library_hash():
             traffic = t.get("bytes_per_launch")
 
     out = {

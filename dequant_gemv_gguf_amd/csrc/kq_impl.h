@@ -1509,8 +1509,8 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
 // Two formats with the same K and work-group shape (the K-quants: same units
 // per row) and the same activations in one launch: the first `gb` work-groups
 // serve the rows of format TB, the others those of format TA, side by side
-// (the host splits the grid in proportion to the bytes of each); each stages
-// the activations and makes one pass.
+// (the host splits the grid so that both sides end together, counting whole
+// row steps); each stages the activations and makes one pass.
 template <int TA, int DA, int TB, int DB, int LB>
 __global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
                                                            int gb, int K, int lpr, int ns,
