@@ -2189,6 +2189,16 @@ struct B1Cfg {
     bool wide;
 };
 
+// One small matrix of short rows at M = 1 goes to the non-persistent LDS
+// kernel: many 4-wave work-groups, each issuing all its loads at once, reach
+// the first bytes sooner than the persistent kernel's per-CU ring (4096 x 4096
+// Q4_K 6.3 -> 5.0 us, 1024 x 4096 5.1 -> 4.0 us, Q2_K 4096 x 4096 5.9 -> 4.6
+// us); the two are even near 28 MB (12288 x 4096 Q4_K, 4096 x 8192 Q6_K), and
+// the persistent kernel wins for larger matrices and longer rows (8192 x 8192
+// Q4_K 11.5 vs 13.6 us; 1024 x 16384 7.1 vs 8.6 us).
+constexpr int64_t SMALL_LAUNCH_BYTES = 20 << 20;
+inline bool small_launch(int K, int64_t bytes) { return K <= 8192 && bytes <= SMALL_LAUNCH_BYTES; }
+
 // Batch-1 configuration for a launch over `rows` rows of K columns; false:
 // use the LDS kernel.
 template <int T> bool batch1_cfg(int K, int64_t rows, B1Cfg *c) {
@@ -2239,7 +2249,7 @@ int launch_qgemv1(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, cons
 template <int T>
 int launch_qgemv1_single(const void *W, int64_t row_bytes, int N, int K, const float *x, float *y, hipStream_t st) {
     B1Cfg c;
-    if (!batch1_cfg<T>(K, N, &c))
+    if (small_launch(K, (int64_t)N * row_bytes) || !batch1_cfg<T>(K, N, &c))
         return launch_qgemv_t<T, 1, 1>(W, row_bytes, N, K, x, y, st, lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB));
     Segs sg = {};
     sg.W[0] = (const uint8_t *)W;
@@ -2354,9 +2364,10 @@ int launch_group(int M, const std::vector<int> &ids, const void *const *W, const
         B1Cfg c;
         int64_t rows = 0;
         for (int i : ids) rows += N[i];
-        if (!batch1_cfg<T>(K, rows, &c)) {
+        if ((ids.size() == 1 && small_launch(K, rows * row_bytes)) || !batch1_cfg<T>(K, rows, &c)) {
+            const int lpr = lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB);
             for (int i : ids) {
-                const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, c.lpr);
+                const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, lpr);
                 if (r) return r;
             }
             return KQ_OK;
