@@ -250,13 +250,14 @@ def test_qgemv_multi_mixed_formats(case, M):
         check_close(got, yo, S, "matrix %d" % i)
 
 
-@pytest.mark.parametrize("mats", [[(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)],
-                                  [(kqsynth.Q4_K, 20480), (kqsynth.Q6_K, 1024)]], ids=["wk+wv+wq", "long-Q4_K"])
-def test_qgemv_multi_mixed_full_size(mats):
-    # a 70B layer's k, v and q projections in one launch (Q4_K, Q6_K, Q4_K:
-    # the 8-wave configuration), and Q4_K rows too many for it beside Q6_K
-    # rows (the 16-wave one)
-    K = 8192
+@pytest.mark.parametrize("K,mats", [(8192, [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)]),
+                                    (8192, [(kqsynth.Q4_K, 20480), (kqsynth.Q6_K, 1024)]),
+                                    (4096, [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 4096)])],
+                         ids=["70B-wk+wv+wq", "long-Q4_K", "8B-wk+wv+wq"])
+def test_qgemv_multi_mixed_full_size(K, mats):
+    # a 70B and an 8B layer's k, v and q projections in one launch (Q4_K,
+    # Q6_K, Q4_K: the 8-wave configuration), and Q4_K rows too many for it
+    # beside Q6_K rows (the 16-wave one)
     say("qgemv_multi mixed full size", mats)
     Ws = [kqsynth.device_matrix(t, n, K, seed=70 + i, device="cuda") for i, (t, n) in enumerate(mats)]
     x = kqsynth.activations(1, K, kqsynth.rng_for(71))
@@ -272,12 +273,12 @@ def test_qgemv_multi_mixed_full_size(mats):
         check_close(ys[i].cpu().numpy()[:, rows], yo, S, "matrix %d" % i)
 
 
-@pytest.mark.parametrize("Ns,M", [([1024, 8192], 1), ([28672, 28672], 1), ([28672, 28672], 2)],
-                         ids=["wk+wq", "w1+w3", "w1+w3-M2"])
-def test_qgemv_multi_full_size_projections(Ns, M):
-    # a 70B layer's k and q projections, or its gate and up projections
-    # (Q4_K, K = 8192), in one launch as the bench issues them
-    K = 8192
+@pytest.mark.parametrize("Ns,K,M", [([1024, 8192], 8192, 1), ([28672, 28672], 8192, 1), ([28672, 28672], 8192, 2),
+                                    ([14336, 14336], 4096, 1)],
+                         ids=["wk+wq", "w1+w3", "w1+w3-M2", "8B-w1+w3"])
+def test_qgemv_multi_full_size_projections(Ns, K, M):
+    # a 70B layer's k and q projections, or a 70B or 8B layer's gate and up
+    # projections (Q4_K), in one launch as the bench issues them
     Ws = [kqsynth.device_matrix(kqsynth.Q4_K, n, K, seed=60 + i, device="cuda") for i, n in enumerate(Ns)]
     x = kqsynth.activations(M, K, kqsynth.rng_for(61, M))
     ys = [torch.empty((M, n), device="cuda") for n in Ns]
@@ -304,6 +305,9 @@ FULL = [
     ("70B w1 Q5_K", kqsynth.Q5_K, 28672, 8192),
     ("70B w2 Q3_K", kqsynth.Q3_K, 8192, 28672),
     ("70B w1 Q4_0", kqsynth.Q4_0, 28672, 8192),
+    ("70B wo", kqsynth.Q4_K, 8192, 8192),
+    ("8B wo", kqsynth.Q4_K, 4096, 4096),
+    ("8B w2", kqsynth.Q6_K, 4096, 14336),
 ]
 
 
