@@ -1532,6 +1532,58 @@ __global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t
     }
 }
 
+// Small grouped launches at M = 1 (the non-persistent counterpart of the
+// grouped and mixed batch-1 kernels): one 4-wave work-group per row tile of
+// one matrix, the tiles of the TB matrices first, then those of the TA
+// matrices (TA may equal TB); each tile runs the LDS kernel body.  tiles[s]
+// is the first tile of segment s (tiles[n] the total), computed on the host;
+// the segment of a tile is found with compares and selects on the kernel
+// arguments at fixed offsets (no dependent loads before the weight loads).
+struct SegTiles {
+    int t[MAX_SEGS + 1];
+};
+template <int T>
+__device__ __forceinline__ void seg_tile(float *smem, const Segs &sg, const SegTiles &st, int64_t row_bytes, int tile,
+                                         int rows_per_wg, int K, int lpr, const float *x) {
+    const uint8_t *W = sg.W[0];
+    float *y = sg.y[0];
+    int rows = sg.rows[0], t0 = 0;
+#pragma unroll
+    for (int i = 1; i < MAX_SEGS; ++i) {
+        const bool in = i < sg.n && tile >= st.t[i];
+        W = in ? sg.W[i] : W;
+        y = in ? sg.y[i] : y;
+        rows = in ? sg.rows[i] : rows;
+        t0 = in ? st.t[i] : t0;
+    }
+    const int row0 = (tile - t0) * rows_per_wg;
+    const int nrows = (rows - row0) < rows_per_wg ? (rows - row0) : rows_per_wg;
+    // settle the tile's matrix here, before the activations are staged: left
+    // to itself the compiler reads these arguments only after the staging
+    // barrier, in front of the first weight loads
+    asm volatile("" ::"s"(W), "s"(y), "s"(row0), "s"(nrows), "s"(row_bytes));
+    const float *xr[1] = {x};
+    float *yr[1] = {y};
+    gemv_tile<T, 1, 1>(smem, W, row_bytes, row0, nrows, K, K, lpr, xr, yr);
+}
+
+template <int TA, int TB>
+__global__ __launch_bounds__(WG_THREADS) void qgemv_seg_kernel(const Segs sa, const SegTiles ta, int64_t rba,
+                                                               const Segs sb, const SegTiles tb, int64_t rbb,
+                                                               int tiles_b, int rows_per_wg, int K, int lpr,
+                                                               const float *__restrict__ x) {
+    extern __shared__ float smem[];
+    if constexpr (TA == TB) {
+        // one format: every tile is in sb (sa is empty)
+        seg_tile<TB>(smem, sb, tb, rbb, blockIdx.x, rows_per_wg, K, lpr, x);
+    } else {
+        if ((int)blockIdx.x < tiles_b)
+            seg_tile<TB>(smem, sb, tb, rbb, blockIdx.x, rows_per_wg, K, lpr, x);
+        else
+            seg_tile<TA>(smem, sa, ta, rba, blockIdx.x - tiles_b, rows_per_wg, K, lpr, x);
+    }
+}
+
 // Batch-M kernel (2 <= M <= 8).  Persistent work-groups of NW waves, one per
 // compute unit.  Rows are dealt out in row steps of RG = R * G rows (G lane
 // groups of LPR lanes per wave, R rows per group, so one read of a unit's
@@ -2145,6 +2197,26 @@ int launch_qgemv_t(const void *W, int64_t row_bytes, int N, int K, const float *
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
+// Launch of qgemv_seg_kernel over the segments sa (format TA) and sb (format
+// TB) at M = 1; both formats have the same units per row (the same lpr).
+template <int TA, int TB>
+int launch_seg_small(const Segs &sa, int64_t rba, const Segs &sb, int64_t rbb, int K, const float *x,
+                     hipStream_t st) {
+    const int lpr = lanes_per_row((K / Fmt<TA>::QK) * Fmt<TA>::UPB);
+    const int rows_per_wg = WAVES * (64 / lpr);
+    SegTiles ta = {}, tb = {};
+    for (int i = 0; i < sa.n; ++i) ta.t[i + 1] = ta.t[i] + (sa.rows[i] + rows_per_wg - 1) / rows_per_wg;
+    for (int i = 0; i < sb.n; ++i) tb.t[i + 1] = tb.t[i] + (sb.rows[i] + rows_per_wg - 1) / rows_per_wg;
+    const int64_t grid = (int64_t)ta.t[sa.n] + tb.t[sb.n];
+    if (grid == 0) return KQ_OK;
+    const size_t lds = (size_t)lds_floats(1, K) * sizeof(float);
+    auto kern = qgemv_seg_kernel<TA, TB>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WG_THREADS), lds, st, sa, ta, rba, sb, tb, rbb, tb.t[sb.n],
+                       rows_per_wg, K, lpr, x);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
 // Compute units of the current device (cached per device).
 inline int cu_count() {
     static std::atomic<int> cache[64];
@@ -2189,15 +2261,18 @@ struct B1Cfg {
     bool wide;
 };
 
-// One small matrix of short rows at M = 1 goes to the non-persistent LDS
-// kernel: many 4-wave work-groups, each issuing all its loads at once, reach
-// the first bytes sooner than the persistent kernel's per-CU ring (4096 x 4096
-// Q4_K 6.3 -> 5.0 us, 1024 x 4096 5.1 -> 4.0 us, Q2_K 4096 x 4096 5.9 -> 4.6
-// us); the two are even near 28 MB (12288 x 4096 Q4_K, 4096 x 8192 Q6_K), and
-// the persistent kernel wins for larger matrices and longer rows (8192 x 8192
-// Q4_K 11.5 vs 13.6 us; 1024 x 16384 7.1 vs 8.6 us).
+// Small launches of short rows at M = 1 go to the non-persistent LDS kernel
+// (one matrix) or its grouped form qgemv_seg_kernel (several, of one or two
+// formats): many 4-wave work-groups, each issuing all its loads at once,
+// reach the first bytes sooner than the persistent kernel's per-CU ring
+// (4096 x 4096 Q4_K 6.3 -> 5.0 us, 1024 x 4096 5.1 -> 4.0 us, Q2_K 4096 x 4096
+// 5.9 -> 4.6 us; an 8B layer's k+v+q 8.5 -> 7.2 us, three 2048 x 4096 Q4_K
+// 7.0 -> 6.1 us); the two are even near 28 MB (12288 x 4096 Q4_K, 4096 x 8192
+// Q6_K), and the persistent kernels win for larger launches and longer rows
+// (8192 x 8192 Q4_K 11.5 vs 13.6 us; 1024 x 16384 7.1 vs 8.6 us).
 constexpr int64_t SMALL_LAUNCH_BYTES = 20 << 20;
 inline bool small_launch(int K, int64_t bytes) { return K <= 8192 && bytes <= SMALL_LAUNCH_BYTES; }
+template <int T> constexpr int64_t rba_of(int K) { return Fmt<T>::BYTES * (int64_t)(K / Fmt<T>::QK); }
 
 // Batch-1 configuration for a launch over `rows` rows of K columns; false:
 // use the LDS kernel.
@@ -2364,7 +2439,17 @@ int launch_group(int M, const std::vector<int> &ids, const void *const *W, const
         B1Cfg c;
         int64_t rows = 0;
         for (int i : ids) rows += N[i];
-        if ((ids.size() == 1 && small_launch(K, rows * row_bytes)) || !batch1_cfg<T>(K, rows, &c)) {
+        if (small_launch(K, rows * row_bytes)) {
+            if (ids.size() == 1)
+                return launch_qgemv_t<T, 1, 1>(W[ids[0]], row_bytes, (int)N[ids[0]], K, x, y[ids[0]], st,
+                                               lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB));
+            while (next_segs(ids, &pos, W, N, y, 1, &sg)) {
+                const int r = launch_seg_small<T, T>(Segs{}, row_bytes, sg, row_bytes, K, x, st);
+                if (r) return r;
+            }
+            return KQ_OK;
+        }
+        if (!batch1_cfg<T>(K, rows, &c)) {
             const int lpr = lanes_per_row((K / Fmt<T>::QK) * Fmt<T>::UPB);
             for (int i : ids) {
                 const int r = launch_qgemv_t<T, 1, 1>(W[i], row_bytes, (int)N[i], K, x, y[i], st, lpr);
@@ -2427,6 +2512,10 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     Segs sa, sb;
     next_segs(ia, pa, W, N, y, G, &sa);
     next_segs(ib, pb, W, N, y, G, &sb);
+    int64_t bytes = 0;
+    for (int i = 0; i < sa.n; ++i) bytes += sa.rows[i] * rba_of<TA>(K);
+    for (int i = 0; i < sb.n; ++i) bytes += sb.rows[i] * rba_of<TB>(K);
+    if (small_launch(K, bytes)) return launch_seg_small<TA, TB>(sa, rba_of<TA>(K), sb, rba_of<TB>(K), K, x, st);
     // the 8-wave configuration when each format would take it for its own rows
     // (short launches of Q4_K, Q3_K and Q2_K; rows of few stripes otherwise)
     B1Cfg na, nb;
