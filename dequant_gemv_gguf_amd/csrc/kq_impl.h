@@ -37,6 +37,17 @@
 //    4*sum(x)) with q = low2 - 4 + 4*hbit; Q5_K as Q4_K with a fifth bit).
 //  * Lane partials are summed with DPP inside 16-lane rows and lane swizzles
 //    across rows; one lane per row group stores y.  No atomics anywhere.
+//
+// Kernels: qgemv1_kernel (M = 1, persistent, one work-group per compute unit,
+// several matrices of one format per launch), qgemv1_mixed_kernel (the same
+// for two formats side by side), qgemvm_kernel (M = 2..8, persistent),
+// qgemv_kernel and qgemv_seg_kernel (non-persistent, activations staged per
+// work-group: small launches at M = 1 and rows too long for the persistent
+// kernels), qmoe_tok_kernel (routed experts, one work-group per row tile and
+// token, with the routing-weighted sum) and qmoe_kernel + moe_combine_kernel
+// (routed experts grouped by expert, when a token's activations do not fit
+// the former's LDS budget), dequant_kernel.  All follow the same per-row
+// summation order, so a row's bits do not depend on which one computed it.
 #pragma once
 
 #include <hip/hip_runtime.h>
