@@ -223,6 +223,9 @@ MIXED = [
     (768, [(kqsynth.Q3_K, 70), (kqsynth.Q4_K, 9)]),
     # five stripes per row: the 16-wave configuration for both formats
     (20480, [(kqsynth.Q5_K, 40), (kqsynth.Q6_K, 21), (kqsynth.Q5_K, 7)]),
+    # more matrices of one format than a launch takes: a mixed launch of 8 + 3,
+    # then the remaining two in a grouped launch
+    (2048, [(kqsynth.Q4_K, 3 + 5 * i) for i in range(10)] + [(kqsynth.Q6_K, 1 + 9 * i) for i in range(3)]),
 ]
 
 
