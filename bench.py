@@ -21,6 +21,8 @@ Other workloads (--workload) measure the remaining shapes the same way:
   stream  8B-shaped layers x32 held in page-locked HOST memory, copied
           through a ring of --slots device slots ahead of each grouped GEMV
           (host-to-device link bound; value includes the copies)
+  dequant the standalone dequantizer over a 70B layer's matrices to fp32
+          (value counts packed bytes read plus fp32 bytes written)
 
 Inputs are seeded synthetic data drawn directly in device memory.  Only one
 GPU is supported: the path has no collectives.
@@ -48,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream"])
+    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream", "dequant"])
     ap.add_argument("--slots", type=int, default=3, help="stream: device slots in the ring")
     ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
     ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
@@ -307,6 +309,24 @@ def main():
         host_sample.append((qt, N, K, weights[0]))
         workload = "single Q4_K 4096x4096 M=1, rotated over %d copies" % copies
         config = {"workload": workload, "N": N, "K": K, "M": 1, "copies": copies}
+    elif args.workload == "dequant":
+        # the standalone dequantizer over a 70B layer's matrices (Q4_K_M mix):
+        # packed bytes in, fp32 out; the bytes of a launch count both
+        spec = kqsynth.LLAMA3_70B
+        layer = kqsynth.dense_layer(spec["hidden"], spec["ffn"], spec["kv"])
+        layers = args.layers or 1
+        out = torch.empty(max(N * K for (_, _, N, K) in layer), dtype=torch.float32, device=dev)
+        weights = []
+        for L in range(layers):
+            for i, (name, qt, N, K) in enumerate(layer):
+                W = kqsynth.device_matrix(qt, N, K, seed=1000 * L + i, device=dev)
+                weights.append(W)
+                nbytes = N * kq.kq_row_bytes(qt, K) + 4 * N * K
+                launches.append(((lambda qt=qt, W=W, n=N * K: kq.kq_dequant(qt, W, n, out, stream)), nbytes,
+                                 qt == kqsynth.Q4_K))
+        workload = "standalone dequant of llama3-70b layer matrices x%d to fp32" % layers
+        config = {"workload": workload, "layers": layers, "matrices_per_step": len(launches),
+                  "bytes": "packed in + fp32 out"}
     else:  # moe
         spec = kqsynth.QWEN3_30B_A3B_MOE
         layers = args.layers or spec["layers"]
