@@ -1969,158 +1969,178 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const uint8_t *__re
     const uintptr_t ta = (uintptr_t)(src + bfirst * F::BYTES);
     const u32 delta = (u32)(ta & 3u);
     const rsrc_t rs = make_rsrc((const void *)(ta - delta), delta + (u32)((bend - bfirst) * F::BYTES));
-    if (u >= nunits) return;
-    const int64_t b = u / F::UPB;
-    const int sub = (int)(u - b * F::UPB);
-    const u32 off = delta + (u32)((b - bfirst) * F::BYTES);
-    float *out = dst + b * F::QK;
-    if constexpr (T == T_Q4_K) {
-        RawQ4K r;
-        load_unit(r, rs, off, sub);
-        const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
-        const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
-        const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
-        const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
-        const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
-        const u32 sel = (u32)(2 * sub) | ((u32)(2 * sub + 1) << 8) | 0x0C0C0000u;
-        const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel), mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
-        const float ds0 = d * (float)(sc & 0xFFu), ds1 = d * (float)((sc >> 8) & 0xFFu);
-        const float dm0 = dmin * (float)(mm & 0xFFu), dm1 = dmin * (float)((mm >> 8) & 0xFFu);
-        float lo[32], hi[32];
+    // each wave's 64 units are a contiguous run of 64 * UW outputs: they are
+    // written to LDS first and stored from there with contiguous 16-B lanes
+    // (a lane's own unit would be 64 separate cache lines per store)
+    constexpr int UW = F::QK / F::UPB;              // weights per unit
+    __shared__ f4 win4[WG_THREADS / 64][16 * UW];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t u0 = ufirst + 64 * wave;
+    if (u0 >= nunits) return;                        // uniform over the wave
+    float *win = reinterpret_cast<float *>(win4[wave]);
+    if (u < nunits) {
+        const int64_t b = u / F::UPB;
+        const int sub = (int)(u - b * F::UPB);
+        const u32 off = delta + (u32)((b - bfirst) * F::BYTES);
+        float *out = win + (b * F::QK - u0 * UW);
+        if constexpr (T == T_Q4_K) {
+            RawQ4K r;
+            load_unit(r, rs, off, sub);
+            const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
+            const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
+            const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
+            const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+            const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+            const u32 sel = (u32)(2 * sub) | ((u32)(2 * sub + 1) << 8) | 0x0C0C0000u;
+            const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel), mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
+            const float ds0 = d * (float)(sc & 0xFFu), ds1 = d * (float)((sc >> 8) & 0xFFu);
+            const float dm0 = dmin * (float)(mm & 0xFFu), dm1 = dmin * (float)((mm >> 8) & 0xFFu);
+            float lo[32], hi[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u32 D = i < 4 ? r.qa[i & 3] : r.qb[i & 3];
+            for (int i = 0; i < 8; ++i) {
+                const u32 D = i < 4 ? r.qa[i & 3] : r.qb[i & 3];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32 byte = (D >> (8 * j)) & 0xFFu;
-                lo[4 * i + j] = __builtin_fmaf(ds0, (float)(byte & 15u), -dm0) + 0.0f;
-                hi[4 * i + j] = __builtin_fmaf(ds1, (float)(byte >> 4), -dm1) + 0.0f;
+                for (int j = 0; j < 4; ++j) {
+                    const u32 byte = (D >> (8 * j)) & 0xFFu;
+                    lo[4 * i + j] = __builtin_fmaf(ds0, (float)(byte & 15u), -dm0) + 0.0f;
+                    hi[4 * i + j] = __builtin_fmaf(ds1, (float)(byte >> 4), -dm1) + 0.0f;
+                }
             }
-        }
-        f4 *o4 = reinterpret_cast<f4 *>(out + 64 * sub);
+            f4 *o4 = reinterpret_cast<f4 *>(out + 64 * sub);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o4[i] = f4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
+            for (int i = 0; i < 8; ++i) o4[i] = f4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
-    } else if constexpr (T == T_Q6_K) {
-        const int h = sub >> 1, q2 = sub & 1;
-        RawQ6K ru;
-        load_unit(ru, rs, off, sub);
-        const Q6KFields r = fields(ru);
-        const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
-        const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
+            for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
+        } else if constexpr (T == T_Q6_K) {
+            const int h = sub >> 1, q2 = sub & 1;
+            RawQ6K ru;
+            load_unit(ru, rs, off, sub);
+            const Q6KFields r = fields(ru);
+            const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+            const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float dsc = r.d * (float)(int)(signed char)(p >> (8 * g));
-            float w[16];
+            for (int g = 0; g < 4; ++g) {
+                const float dsc = r.d * (float)(int)(signed char)(p >> (8 * g));
+                float w[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const u32 lowb = (g & 1) ? r.b[i >> 2] : r.a[i >> 2];
+                    const u32 byte = (lowb >> (8 * (i & 3))) & 0xFFu;
+                    const u32 lo4 = (g < 2) ? (byte & 15u) : (byte >> 4);
+                    const u32 hi2 = (r.hq[i >> 2] >> (8 * (i & 3) + 2 * g)) & 3u;
+                    w[i] = dsc * (float)((int)(lo4 | (hi2 << 4)) - 32) + 0.0f;
+                }
+                f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * g + 16 * q2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            }
+        } else if constexpr (T == T_Q2_K) {
+            const int h = sub >> 1, q2 = sub & 1;
+            RawQ2K r;
+            load_unit(r, rs, off, sub);
+            const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
+            const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
+            const float d = half_lo(r.dd), dmin = half_lo(r.dd >> 16);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float dsc = d * (float)((p >> (8 * s)) & 15u);
+                const float dm = dmin * (float)((p >> (8 * s + 4)) & 15u);
+                float w[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const u32 q = (r.q[i >> 2] >> (8 * (i & 3) + 2 * s)) & 3u;
+                    w[i] = __builtin_fmaf(dsc, (float)q, -dm) + 0.0f;
+                }
+                f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * s + 16 * q2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            }
+        } else if constexpr (T == T_Q4_0) {
+            RawQ40 ru;
+            load_unit(ru, rs, off, 0);
+            const Q40Fields r = fields(ru);
+            float w[32];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const u32 lowb = (g & 1) ? r.b[i >> 2] : r.a[i >> 2];
-                const u32 byte = (lowb >> (8 * (i & 3))) & 0xFFu;
-                const u32 lo4 = (g < 2) ? (byte & 15u) : (byte >> 4);
-                const u32 hi2 = (r.hq[i >> 2] >> (8 * (i & 3) + 2 * g)) & 3u;
-                w[i] = dsc * (float)((int)(lo4 | (hi2 << 4)) - 32) + 0.0f;
+                const u32 byte = (r.q[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+                w[i] = r.d * (float)((int)(byte & 15u) - 8) + 0.0f;
+                w[16 + i] = r.d * (float)((int)(byte >> 4) - 8) + 0.0f;
             }
-            f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * g + 16 * q2);
+            f4 *o4 = reinterpret_cast<f4 *>(out);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-        }
-    } else if constexpr (T == T_Q2_K) {
-        const int h = sub >> 1, q2 = sub & 1;
-        RawQ2K r;
-        load_unit(r, rs, off, sub);
-        const u32 sel = (u32)q2 | ((u32)(q2 + 2) << 8) | ((u32)(q2 + 4) << 16) | ((u32)(q2 + 6) << 24);
-        const u32 p = __builtin_amdgcn_perm(r.s1, r.s0, sel);
-        const float d = half_lo(r.dd), dmin = half_lo(r.dd >> 16);
+            for (int i = 0; i < 8; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        } else if constexpr (T == T_Q5_K) {
+            RawQ5K r;
+            load_unit(r, rs, off, sub);
+            const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
+            const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
+            const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
+            const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+            const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+            const u32 sel = (u32)(2 * sub) | ((u32)(2 * sub + 1) << 8) | 0x0C0C0000u;
+            const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel), mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
+            const float ds0 = d * (float)(sc & 0xFFu), ds1 = d * (float)((sc >> 8) & 0xFFu);
+            const float dm0 = dmin * (float)(mm & 0xFFu), dm1 = dmin * (float)((mm >> 8) & 0xFFu);
+            float lo[32], hi[32];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float dsc = d * (float)((p >> (8 * s)) & 15u);
-            const float dm = dmin * (float)((p >> (8 * s + 4)) & 15u);
-            float w[16];
+            for (int i = 0; i < 8; ++i) {
+                const u32 D = i < 4 ? r.qa[i & 3] : r.qb[i & 3];
+                const u32 H = i < 4 ? r.ha[i & 3] : r.hb[i & 3];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const u32 q = (r.q[i >> 2] >> (8 * (i & 3) + 2 * s)) & 3u;
-                w[i] = __builtin_fmaf(dsc, (float)q, -dm) + 0.0f;
+                for (int j = 0; j < 4; ++j) {
+                    const u32 byte = (D >> (8 * j)) & 0xFFu, hb = (H >> (8 * j)) & 0xFFu;
+                    const u32 ql = (byte & 15u) | (((hb >> (2 * sub)) & 1u) << 4);
+                    const u32 qh = (byte >> 4) | (((hb >> (2 * sub + 1)) & 1u) << 4);
+                    lo[4 * i + j] = __builtin_fmaf(ds0, (float)ql, -dm0) + 0.0f;
+                    hi[4 * i + j] = __builtin_fmaf(ds1, (float)qh, -dm1) + 0.0f;
+                }
             }
-            f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * s + 16 * q2);
+            f4 *o4 = reinterpret_cast<f4 *>(out + 64 * sub);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-        }
-    } else if constexpr (T == T_Q4_0) {
-        RawQ40 ru;
-        load_unit(ru, rs, off, 0);
-        const Q40Fields r = fields(ru);
-        float w[32];
+            for (int i = 0; i < 8; ++i) o4[i] = f4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const u32 byte = (r.q[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            w[i] = r.d * (float)((int)(byte & 15u) - 8) + 0.0f;
-            w[16 + i] = r.d * (float)((int)(byte >> 4) - 8) + 0.0f;
-        }
-        f4 *o4 = reinterpret_cast<f4 *>(out);
+            for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
+        } else if constexpr (T == T_Q3_K) {
+            const int h = sub >> 1, q2 = sub & 1;
+            RawQ3K ru;
+            load_unit(ru, rs, off, sub);
+            const Q3KFields r = fields(ru);
+            float dsc[4];
+            q3k_scales(r, sub, dsc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    } else if constexpr (T == T_Q5_K) {
-        RawQ5K r;
-        load_unit(r, rs, off, sub);
-        const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
-        const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
-        const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
-        const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
-        const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
-        const u32 sel = (u32)(2 * sub) | ((u32)(2 * sub + 1) << 8) | 0x0C0C0000u;
-        const u32 sc = __builtin_amdgcn_perm(sc_hi, sc_lo, sel), mm = __builtin_amdgcn_perm(m_hi, m_lo, sel);
-        const float ds0 = d * (float)(sc & 0xFFu), ds1 = d * (float)((sc >> 8) & 0xFFu);
-        const float dm0 = dmin * (float)(mm & 0xFFu), dm1 = dmin * (float)((mm >> 8) & 0xFFu);
-        float lo[32], hi[32];
+            for (int s = 0; s < 4; ++s) {
+                float w[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u32 D = i < 4 ? r.qa[i & 3] : r.qb[i & 3];
-            const u32 H = i < 4 ? r.ha[i & 3] : r.hb[i & 3];
+                for (int i = 0; i < 16; ++i) {
+                    const u32 q = (r.q[i >> 2] >> (8 * (i & 3) + 2 * s)) & 3u;
+                    const u32 hb = (r.mk[i >> 2] >> (8 * (i & 3) + 4 * h + s)) & 1u;
+                    w[i] = dsc[s] * (float)((int)(q | (hb << 2)) - 4) + 0.0f;
+                }
+                f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * s + 16 * q2);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32 byte = (D >> (8 * j)) & 0xFFu, hb = (H >> (8 * j)) & 0xFFu;
-                const u32 ql = (byte & 15u) | (((hb >> (2 * sub)) & 1u) << 4);
-                const u32 qh = (byte >> 4) | (((hb >> (2 * sub + 1)) & 1u) << 4);
-                lo[4 * i + j] = __builtin_fmaf(ds0, (float)ql, -dm0) + 0.0f;
-                hi[4 * i + j] = __builtin_fmaf(ds1, (float)qh, -dm1) + 0.0f;
+                for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
             }
+        } else {
+            RawQ80 ru;
+            load_unit(ru, rs, off, 0);
+            const Q80Fields r = fields(ru);
+            float w[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) w[i] = r.d * (float)(int)(signed char)(r.q[i >> 2] >> (8 * (i & 3))) + 0.0f;
+            f4 *o4 = reinterpret_cast<f4 *>(out);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
         }
-        f4 *o4 = reinterpret_cast<f4 *>(out + 64 * sub);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t n4 = ((nunits - u0 < 64 ? nunits - u0 : 64) * UW) >> 2;
+    f4 *dst4 = reinterpret_cast<f4 *>(dst + u0 * UW);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o4[i] = f4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o4[8 + i] = f4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
-    } else if constexpr (T == T_Q3_K) {
-        const int h = sub >> 1, q2 = sub & 1;
-        RawQ3K ru;
-        load_unit(ru, rs, off, sub);
-        const Q3KFields r = fields(ru);
-        float dsc[4];
-        q3k_scales(r, sub, dsc);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            float w[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const u32 q = (r.q[i >> 2] >> (8 * (i & 3) + 2 * s)) & 3u;
-                const u32 hb = (r.mk[i >> 2] >> (8 * (i & 3) + 4 * h + s)) & 1u;
-                w[i] = dsc[s] * (float)((int)(q | (hb << 2)) - 4) + 0.0f;
-            }
-            f4 *o4 = reinterpret_cast<f4 *>(out + 128 * h + 32 * s + 16 * q2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-        }
-    } else {
-        RawQ80 ru;
-        load_unit(ru, rs, off, 0);
-        const Q80Fields r = fields(ru);
-        float w[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) w[i] = r.d * (float)(int)(signed char)(r.q[i >> 2] >> (8 * (i & 3))) + 0.0f;
-        f4 *o4 = reinterpret_cast<f4 *>(out);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o4[i] = f4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    for (int i = 0; i < UW / 4; ++i) {
+        const int q = 64 * i + lane;
+        if (q < n4) dst4[q] = win4[wave][q];
     }
 }
 
