@@ -39,8 +39,9 @@
 //    across rows; one lane per row group stores y.  No atomics anywhere.
 //
 // Kernels: qgemv1_kernel (M = 1, persistent, one work-group per compute unit,
-// several matrices of one format per launch), qgemv1_mixed_kernel (the same
-// for two formats side by side), qgemvm_kernel (M = 2..8, persistent),
+// several matrices of one format per launch), qgemv1_dma_kernel (its Q4_K form
+// with the weight ring in LDS, filled by buffer-to-LDS loads),
+// qgemv1_mixed_kernel (the same for two formats side by side), qgemvm_kernel (M = 2..8, persistent),
 // qgemv_kernel and qgemv_seg_kernel (non-persistent, activations staged per
 // work-group: small launches at M = 1 and rows too long for the persistent
 // kernels), qmoe_tok_kernel (routed experts, one work-group per row tile and
@@ -1355,20 +1356,31 @@ __device__ __forceinline__ void xreg_from_lds(XReg<T> &xr, const XLds &xa) {
 // Write the parked sums of steps [b0, b0 + LPR): one stripe -- store; several
 // stripes -- add them in stripe order through LDS (barriers: every wave of the
 // work-group calls this at the same steps).
-template <bool MS>
+// Work-group barrier.  With buffer-to-LDS loads in flight (DMA) it waits only
+// for the wave's own LDS accesses: __syncthreads would also wait for every
+// outstanding buffer-to-LDS load (the compiler cannot tell that only the
+// issuing wave reads their destination) and drain the weight ring.
+template <bool DMA> __device__ __forceinline__ void wg_sync() {
+    if constexpr (DMA)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        __syncthreads();
+}
+
+template <bool MS, bool DMA = false>
 __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first, int rstride, int N, int ns,
                                        int wave, int lane, int rsl, int stripe, int grp, int slot,
                                        float (*part)[64], const Segs &sg) {
     if (ns > 1) {
         part[wave][lane] = keep;
-        __syncthreads();
+        wg_sync<DMA>();
         float *o = out_of<MS>(sg, N, first + (b0 + lane) * rstride);
         if (stripe == 0 && b0 + lane < wsteps && o) {
             float s = 0.f;
             for (int w = 0; w < ns; ++w) s += part[rsl * ns + w][lane];
             *o = s;
         }
-        __syncthreads();
+        wg_sync<DMA>();
     } else {
         float *o = out_of<MS>(sg, N, first + (b0 + slot) * rstride + grp);
         if (b0 + slot < wsteps && o) *o = 0.f + keep;
@@ -1469,7 +1481,7 @@ template <int T, int D, bool MS> struct B1Pass {
 // of 16 per thread), then `issue` (the first row loads), then the LDS writes
 // of the activations and their 16-sums -- waiting for the activations leaves
 // the row loads in flight.
-template <class Issue>
+template <bool DMA = false, class Issue>
 __device__ __forceinline__ void stage_x1(const float *__restrict__ x, int K, float *smem, float *xs, float *ss,
                                          Issue issue) {
     const int nthreads = blockDim.x;
@@ -1496,7 +1508,7 @@ __device__ __forceinline__ void stage_x1(const float *__restrict__ x, int K, flo
         for (int k = 0; k < 4; ++k) dst[k] = xg[it][k];
         (ok ? ss[idx] : smem[16]) = sum16(xg[it][0], xg[it][1], xg[it][2], xg[it][3]);
     }
-    __syncthreads();
+    wg_sync<DMA>();
 }
 
 // Batch-1 kernel: one persistent work-group per compute unit, RS row slots of
@@ -1517,30 +1529,190 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     p.run(xs, ss, XS, SS, part);
 }
 
-// Two formats with the same K and work-group shape (the K-quants: same units
-// per row) and the same activations in one launch: the first `gb` work-groups
-// serve the rows of format TB, the others those of format TA, side by side
-// (the host splits the grid so that both sides end together, counting whole
-// row steps); each stages the activations and makes one pass.
-template <int TA, int DA, int TB, int DB, int LB>
-__global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
-                                                           int gb, int K, int lpr, int ns,
-                                                           const float *__restrict__ x) {
+// Batch-1 pass for Q4_K with the weight ring in LDS.  A wave's row step
+// covers 64 units: at most 16 blocks, 2304 contiguous bytes of the matrix
+// (one stripe of a long row, or G whole short rows).  The wave copies them with
+// three buffer-to-LDS loads of 16 bytes per lane (lane i: bytes 1024k + 16i),
+// each covering whole 128-byte lines, so they can bypass the caches
+// (non-temporal) without a line being fetched twice; each lane then reads its
+// unit's header and 32 quant bytes from LDS.  Compared with the register ring
+// of B1Pass this frees the ring's registers, and every load instruction is a
+// single coalesced 1-KB request.  The compiler does not order LDS reads after
+// these loads, so the waits are explicit: before reading slot d a wave lets at
+// most 3(D-1) loads stay outstanding (those of the D-1 later steps; loads
+// complete in issue order).  Requires 16-byte aligned matrices.
+constexpr int DMA_SLOT = 3072;   // bytes per ring slot (three 1-KB loads)
+constexpr int DMA_SPAN = 2304;   // 16 Q4_K blocks
+#define KQ_LDS __attribute__((address_space(3)))
+
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D, bool MS> struct B1DmaQ4K {
+    typedef Fmt<T_Q4_K> F;
+    const Segs &sg;
+    int64_t row_bytes;
+    int N, lpr, ns, wave, lane, rsl, stripe, G, grp, slot, sub, rstride, first, wsteps, uc;
+    bool act;
+    u32 rbase, span, lofs;
+    char *ring;   // this wave's D slots
+    SegCursor<MS> cur;
+
+    __device__ __forceinline__ B1DmaQ4K(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_,
+                                        int wg, int nwg, char *ring_)
+        : sg(s), row_bytes(rb), lpr(lpr_), ns(ns_), wave(wave_), lane(lane_), ring(ring_) {
+        N = sg.start[sg.n];
+        const int RS = (blockDim.x >> 6) / ns;
+        rsl = wave / ns;
+        stripe = wave - rsl * ns;
+        G = 64 / lpr;
+        grp = lane / lpr;
+        slot = lane - grp * lpr;
+        const int units = (K / F::QK) * F::UPB;
+        const int u = stripe * 64 + slot;
+        act = u < units;
+        uc = act ? u : 0;
+        sub = uc % F::UPB;
+        rstride = nwg * RS * G;
+        first = (wg * RS + rsl) * G;
+        const int f0 = wg * RS * G;
+        wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
+        rbase = (u32)stripe * DMA_SPAN;
+        const int64_t rest = rb - (int64_t)rbase;
+        span = ns > 1 ? (u32)(rest < DMA_SPAN ? rest : DMA_SPAN) : (u32)(G * rb);
+        // a lane's unit inside the slot (inactive lanes stay inside the slot)
+        lofs = (u32)(grp * (ns > 1 ? 0 : rb)) + (u32)(slot >> 2) * F::BYTES;
+        cur.set(sg, 0);
+    }
+    __device__ __forceinline__ void issue(int d, int step) {
+        const int row0 = first + step * rstride;
+        cur.seek(sg, row0);
+        const int local = row0 - cur.start;
+        const int left = cur.rows - local;
+        const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
+        const rsrc_t rs = make_rsrc(cur.W + (int64_t)(nr ? local : 0) * row_bytes, (u32)((int64_t)nr * row_bytes));
+        char *dst = ring + d * DMA_SLOT;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const u32 o = 1024u * k + 16u * lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (KQ_LDS void *)(dst + 1024 * k), 16, o < span ? rbase + o : OOB,
+                                                     0, 0, 2 /* nt */);
+        }
+    }
+    __device__ __forceinline__ void issue_first() {
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(d, d);
+    }
+    __device__ __forceinline__ void read(RawQ4K &r, int d) const {
+        const char *p = ring + d * DMA_SLOT + lofs;
+        r.h = *reinterpret_cast<const u4 *>(p);
+        r.qa = *reinterpret_cast<const u4 *>(p + 16 + 32 * sub);
+        r.qb = *reinterpret_cast<const u4 *>(p + 32 + 32 * sub);
+    }
+    __device__ __forceinline__ void flush(float keep, int b0, float (*part)[64]) {
+        flush1<MS, true>(keep, b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
+    }
+    __device__ __forceinline__ float value(const RawQ4K &r, const XReg<T_Q4_K> &xa) const {
+        const RawQ4K rr[1] = {r};
+        float v[1][1];
+        val_unit<1, 1>(rr, sub, xa, v);
+        return group_sum(act ? v[0][0] : 0.f, lpr);
+    }
+    // the loads of the first D steps must have been issued (issue_first)
+    __device__ __forceinline__ void run(const float *xs, const float *ss, int XS, int SS, float (*part)[64]) {
+        XReg<T_Q4_K> xa;
+        {
+            const int e0 = unit_e0<T_Q4_K>(uc);
+            const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T_Q4_K>()};
+            xreg_from_lds<T_Q4_K>(xa, xl);
+        }
+        float keep = 0.f;
+        int j = 0;
+        for (; j + D <= wsteps; j += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                RawQ4K r;
+                wait_vm<3 * (D - 1)>();
+                read(r, d);
+                wait_lgkm0();
+                issue(d, j + d + D);
+                const float S = value(r, xa);
+                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+            }
+            if (((j + D) & (lpr - 1)) == 0) flush(keep, j + D - lpr, part);
+            wg_sync<true>();
+        }
+        wait_vm<0>();
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            if (j + d < wsteps) {
+                RawQ4K r;
+                read(r, d);
+                const float S = value(r, xa);
+                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+            }
+        }
+        if (wsteps & (lpr - 1)) flush(keep, wsteps & ~(lpr - 1), part);
+    }
+};
+
+// LDS of the batch-1 kernels: [16][64] flush area, the staged activations and
+// 16-sums, then (Q4_K through LDS) the weight ring, 16-byte aligned.
+__host__ __device__ constexpr size_t b1_ring_offset(int K) {
+    return ((size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float) + 15) & ~(size_t)15;
+}
+
+template <int D, int LB, bool MS>
+__global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
+                                                        const float *__restrict__ x) {
     extern __shared__ float smem[];
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
     const int XS = x_stride(K), SS = s_stride(K);
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if ((int)blockIdx.x < gb) {
-        B1Pass<TB, DB, true> pb(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb);
-        stage_x1(x, K, smem, xs, ss, [&] { pb.issue_first(); });
-        pb.run(xs, ss, XS, SS, part);
+    char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DMA_SLOT;
+    B1DmaQ4K<D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
+    stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
+    p.run(xs, ss, XS, SS, part);
+}
+
+// Two formats with the same K and work-group shape (the K-quants: same units
+// per row) and the same activations in one launch: the first `gb` work-groups
+// serve the rows of format TB, the others those of format TA, side by side
+// (the host splits the grid so that both sides end together, counting whole
+// row steps); each stages the activations and makes one pass.
+// One side of a mixed launch: this work-group's share of the rows of one
+// format (Q4_K through the LDS ring when DMA is set).
+template <int T, int D, bool DMA>
+__device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int lpr, int ns, int wave, int lane, int wg,
+                                        int nwg, const float *__restrict__ x, float *smem) {
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    float *ss = xs + XS;
+    if constexpr (DMA && T == T_Q4_K) {
+        char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DMA_SLOT;
+        B1DmaQ4K<D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
+        stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
+        p.run(xs, ss, XS, SS, part);
     } else {
-        B1Pass<TA, DA, true> pa(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb);
-        stage_x1(x, K, smem, xs, ss, [&] { pa.issue_first(); });
-        pa.run(xs, ss, XS, SS, part);
+        B1Pass<T, D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
+        stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
+        p.run(xs, ss, XS, SS, part);
     }
+}
+
+template <int TA, int DA, int TB, int DB, int LB, bool DMA>
+__global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
+                                                           int gb, int K, int lpr, int ns,
+                                                           const float *__restrict__ x) {
+    extern __shared__ float smem[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if ((int)blockIdx.x < gb)
+        b1_side<TB, DB, DMA>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, x, smem);
+    else
+        b1_side<TA, DA, DMA>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, x, smem);
 }
 
 // Small grouped launches at M = 1 (the non-persistent counterpart of the
@@ -2342,10 +2514,45 @@ int launch_qgemv1_cfg(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
+// Q4_K batch-1 launches with the weight ring in LDS (qgemv1_dma_kernel): the
+// same work-group shapes and ring depths as the register ring; needs 16-byte
+// aligned matrices and the ring's LDS beside the activations.
+constexpr size_t LDS_MAX = 160 * 1024;
+template <bool WIDE> constexpr int DMA_DEPTH() { return WIDE ? 2 : 4; }
+inline size_t dma_lds(const B1Cfg &c, int K) {
+    return b1_ring_offset(K) + (size_t)(c.ns * c.rs) * (c.wide ? DMA_DEPTH<true>() : DMA_DEPTH<false>()) * DMA_SLOT;
+}
+inline bool dma_ok(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K) {
+    if (row_bytes % 16 || dma_lds(c, K) > LDS_MAX) return false;
+    for (int i = 0; i < sg.n; ++i)
+        if ((uintptr_t)sg.W[i] % 16) return false;
+    return true;
+}
+template <bool WIDE>
+int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    constexpr int D = DMA_DEPTH<WIDE>(), LB = WIDE ? 1024 : 512;
+    const int nt = 64 * c.ns * c.rs;
+    const int G = 64 / c.lpr;
+    const size_t lds = dma_lds(c, K);
+    auto kern = sg.n > 1 ? qgemv1_dma_kernel<D, LB, true> : qgemv1_dma_kernel<D, LB, false>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
+    const int64_t need = (slots + c.rs - 1) / c.rs;
+    const int64_t cap = cu_count();
+    const int grid = (int)(need < cap ? need : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, sg, row_bytes, K, c.lpr, c.ns, x);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
 // Batch-1 launch over one or more segments (same format and K): one lane per
 // unit, stripes of 64 units, one work-group per compute unit (persistent).
 template <int T>
 int launch_qgemv1(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    if constexpr (T == T_Q4_K) {
+        if (dma_ok(c, sg, row_bytes, K))
+            return c.wide ? launch_qgemv1_dma<true>(c, sg, row_bytes, K, x, st)
+                          : launch_qgemv1_dma<false>(c, sg, row_bytes, K, x, st);
+    }
     if constexpr (NARROW_MAX_STRIPES<T>() > 0) {
         if (!c.wide) return launch_qgemv1_cfg<T, false>(c, sg, row_bytes, K, x, st);
     }
@@ -2374,7 +2581,6 @@ int launch_qgemv1_single(const void *W, int64_t row_bytes, int N, int K, const f
 // row sums.
 template <int T, int M> constexpr int MROWS() { return 2; }
 template <int T, int M> constexpr int MRING() { return (BIG_UNIT<T>() && M > 4) ? 1 : 2; }
-constexpr size_t LDS_MAX = 160 * 1024;
 
 // Batch-M launch over one or more segments (starts padded to the row step).
 // Returns KQ_ERR_ARG when the activations of one 4096-column chunk do not fit
@@ -2583,9 +2789,19 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     }
     const int grid = (int)(ga + gb);
     if (grid == 0) return KQ_OK;
-    const size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
-    auto kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512>
-                       : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024>;
+    size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
+    auto kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false>
+                       : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false>;
+    if constexpr (TA == T_Q4_K || TB == T_Q4_K) {
+        // the Q4_K side through the LDS ring
+        B1Cfg cq = ca;
+        cq.wide = !narrow;
+        if (dma_ok(cq, TA == T_Q4_K ? sa : sb, TA == T_Q4_K ? rba : rbb, K)) {
+            lds = std::max(lds, dma_lds(cq, K));
+            kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true>
+                          : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true>;
+        }
+    }
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, rba, sb, rbb, (int)gb, K, ca.lpr,
                        ca.ns, x);
