@@ -100,7 +100,9 @@ def library_hash():
 
 
 CALIB_BYTES = 1 << 30
-DOMINANT_KERNELS = ("qgemv1_kernel<12,", "qgemv1_mixed_kernel<12,")   # batch-1 launches with a Q4_K pass
+# batch-1 launches with a Q4_K pass (the LDS-ring kernel, or the register-ring
+# one for unaligned matrices)
+DOMINANT_KERNELS = ("qgemv1_dma_kernel<12,", "qgemv1_kernel<12,", "qgemv1_mixed_kernel<12,")
 
 
 def pmc_per_dispatch(path, counter):
@@ -121,7 +123,7 @@ def summarize_pmc(args):
     """Traffic of the dominant kernel from a FETCH_SIZE and a WRITE_SIZE pass.
     Each counter is calibrated on the 1 GiB copy the passes ran first: the
     factor is 1 GiB over what the counter read for it."""
-    result = {"kernel": "qgemv1_kernel Q4_K (M=1)", "library_sha256_16": library_hash(),
+    result = {"kernel": "batch-1 Q4_K launches (M=1)", "library_sha256_16": library_hash(),
               "workload": args.workload, "command": args.pmc_command}
     per = {}
     for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),

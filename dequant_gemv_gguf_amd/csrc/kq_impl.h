@@ -1529,27 +1529,39 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     p.run(xs, ss, XS, SS, part);
 }
 
-// Batch-1 pass for Q4_K with the weight ring in LDS.  A wave's row step
-// covers 64 units: at most 16 blocks, 2304 contiguous bytes of the matrix
-// (one stripe of a long row, or G whole short rows).  The wave copies them with
-// three buffer-to-LDS loads of 16 bytes per lane (lane i: bytes 1024k + 16i),
-// each covering whole 128-byte lines, so they can bypass the caches
-// (non-temporal) without a line being fetched twice; each lane then reads its
-// unit's header and 32 quant bytes from LDS.  Compared with the register ring
-// of B1Pass this frees the ring's registers, and every load instruction is a
-// single coalesced 1-KB request.  The compiler does not order LDS reads after
-// these loads, so the waits are explicit: before reading slot d a wave lets at
-// most 3(D-1) loads stay outstanding (those of the D-1 later steps; loads
-// complete in issue order).  Requires 16-byte aligned matrices.
-constexpr int DMA_SLOT = 3072;   // bytes per ring slot (three 1-KB loads)
-constexpr int DMA_SPAN = 2304;   // 16 Q4_K blocks
+// Batch-1 pass with the weight ring in LDS (used for Q4_K).  A wave's row step
+// covers 64 units: at most 16 blocks (Q4_K: 2304 contiguous bytes, one stripe
+// of a long row or G whole short rows).  The wave copies them with NLD
+// buffer-to-LDS loads of 16 bytes per lane (lane i: bytes 1024k + 16i), each
+// covering whole 128-byte lines, so they can bypass the caches (non-temporal)
+// without a line being fetched twice; each lane then reads its unit's header
+// and quant bytes from LDS.  Compared
+// with the register ring of B1Pass this frees the ring's registers, and every
+// load instruction is a single coalesced 1-KB request.  The compiler does not
+// order LDS reads after these loads, so the waits are explicit: before
+// reading slot d a wave lets at most NLD(D-1) loads stay outstanding (those of
+// the D-1 later steps; loads complete in issue order).  Requires 16-byte
+// aligned matrices and rows.
 #define KQ_LDS __attribute__((address_space(3)))
 
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, bool MS> struct B1DmaQ4K {
-    typedef Fmt<T_Q4_K> F;
+template <int T> struct DmaGeom {
+    static constexpr int SPAN = 16 * Fmt<T>::BYTES;          // bytes of 64 units
+    static constexpr int NLD = (SPAN + 1023) / 1024;         // 1-KB loads per step
+    static constexpr int SLOT = NLD * 1024;                  // bytes per ring slot
+};
+
+__device__ __forceinline__ void read_unit(RawQ4K &r, const char *blk, int g) {
+    r.h = *reinterpret_cast<const u4 *>(blk);
+    r.qa = *reinterpret_cast<const u4 *>(blk + 16 + 32 * g);
+    r.qb = *reinterpret_cast<const u4 *>(blk + 32 + 32 * g);
+}
+template <int T, int D, bool MS> struct B1Dma {
+    typedef Fmt<T> F;
+    typedef DmaGeom<T> GM;
+    typedef typename RawOf<T>::type Raw;
     const Segs &sg;
     int64_t row_bytes;
     int N, lpr, ns, wave, lane, rsl, stripe, G, grp, slot, sub, rstride, first, wsteps, uc;
@@ -1558,8 +1570,8 @@ template <int D, bool MS> struct B1DmaQ4K {
     char *ring;   // this wave's D slots
     SegCursor<MS> cur;
 
-    __device__ __forceinline__ B1DmaQ4K(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_,
-                                        int wg, int nwg, char *ring_)
+    __device__ __forceinline__ B1Dma(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_, int wg,
+                                     int nwg, char *ring_)
         : sg(s), row_bytes(rb), lpr(lpr_), ns(ns_), wave(wave_), lane(lane_), ring(ring_) {
         N = sg.start[sg.n];
         const int RS = (blockDim.x >> 6) / ns;
@@ -1577,11 +1589,11 @@ template <int D, bool MS> struct B1DmaQ4K {
         first = (wg * RS + rsl) * G;
         const int f0 = wg * RS * G;
         wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
-        rbase = (u32)stripe * DMA_SPAN;
+        rbase = (u32)stripe * GM::SPAN;
         const int64_t rest = rb - (int64_t)rbase;
-        span = ns > 1 ? (u32)(rest < DMA_SPAN ? rest : DMA_SPAN) : (u32)(G * rb);
-        // a lane's unit inside the slot (inactive lanes stay inside the slot)
-        lofs = (u32)(grp * (ns > 1 ? 0 : rb)) + (u32)(slot >> 2) * F::BYTES;
+        span = ns > 1 ? (u32)(rest < GM::SPAN ? rest : GM::SPAN) : (u32)(G * rb);
+        // a lane's block inside the slot (inactive lanes stay inside the slot)
+        lofs = (u32)(grp * (ns > 1 ? 0 : rb)) + (u32)(slot / F::UPB) * F::BYTES;
         cur.set(sg, 0);
     }
     __device__ __forceinline__ void issue(int d, int step) {
@@ -1591,9 +1603,9 @@ template <int D, bool MS> struct B1DmaQ4K {
         const int left = cur.rows - local;
         const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
         const rsrc_t rs = make_rsrc(cur.W + (int64_t)(nr ? local : 0) * row_bytes, (u32)((int64_t)nr * row_bytes));
-        char *dst = ring + d * DMA_SLOT;
+        char *dst = ring + d * GM::SLOT;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < GM::NLD; ++k) {
             const u32 o = 1024u * k + 16u * lane;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (KQ_LDS void *)(dst + 1024 * k), 16, o < span ? rbase + o : OOB,
                                                      0, 0, 2 /* nt */);
@@ -1603,37 +1615,31 @@ template <int D, bool MS> struct B1DmaQ4K {
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(d, d);
     }
-    __device__ __forceinline__ void read(RawQ4K &r, int d) const {
-        const char *p = ring + d * DMA_SLOT + lofs;
-        r.h = *reinterpret_cast<const u4 *>(p);
-        r.qa = *reinterpret_cast<const u4 *>(p + 16 + 32 * sub);
-        r.qb = *reinterpret_cast<const u4 *>(p + 32 + 32 * sub);
-    }
     __device__ __forceinline__ void flush(float keep, int b0, float (*part)[64]) {
         flush1<MS, true>(keep, b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
     }
-    __device__ __forceinline__ float value(const RawQ4K &r, const XReg<T_Q4_K> &xa) const {
-        const RawQ4K rr[1] = {r};
+    __device__ __forceinline__ float value(const Raw &r, const XReg<T> &xa) const {
+        const Raw rr[1] = {r};
         float v[1][1];
         val_unit<1, 1>(rr, sub, xa, v);
         return group_sum(act ? v[0][0] : 0.f, lpr);
     }
+    // activations of the lane's unit from the staged copy in LDS
+    __device__ __forceinline__ void x_from_lds(XReg<T> &xa, const float *xs, const float *ss, int XS, int SS) const {
+        const int e0 = unit_e0<T>(uc);
+        const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T>()};
+        xreg_from_lds<T>(xa, xl);
+    }
     // the loads of the first D steps must have been issued (issue_first)
-    __device__ __forceinline__ void run(const float *xs, const float *ss, int XS, int SS, float (*part)[64]) {
-        XReg<T_Q4_K> xa;
-        {
-            const int e0 = unit_e0<T_Q4_K>(uc);
-            const XLds xl{xs, ss, XS, SS, xpad(e0), e0 >> 4, sum_run_stride<T_Q4_K>()};
-            xreg_from_lds<T_Q4_K>(xa, xl);
-        }
+    __device__ __forceinline__ void run(const XReg<T> &xa, float (*part)[64]) {
         float keep = 0.f;
         int j = 0;
         for (; j + D <= wsteps; j += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                RawQ4K r;
-                wait_vm<3 * (D - 1)>();
-                read(r, d);
+                Raw r;
+                wait_vm<GM::NLD * (D - 1)>();
+                read_unit(r, ring + d * GM::SLOT + lofs, sub);
                 wait_lgkm0();
                 issue(d, j + d + D);
                 const float S = value(r, xa);
@@ -1646,8 +1652,8 @@ template <int D, bool MS> struct B1DmaQ4K {
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) {
             if (j + d < wsteps) {
-                RawQ4K r;
-                read(r, d);
+                Raw r;
+                read_unit(r, ring + d * GM::SLOT + lofs, sub);
                 const float S = value(r, xa);
                 keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
             }
@@ -1657,12 +1663,12 @@ template <int D, bool MS> struct B1DmaQ4K {
 };
 
 // LDS of the batch-1 kernels: [16][64] flush area, the staged activations and
-// 16-sums, then (Q4_K through LDS) the weight ring, 16-byte aligned.
+// 16-sums, then (ring in LDS) the weight ring, 16-byte aligned.
 __host__ __device__ constexpr size_t b1_ring_offset(int K) {
     return ((size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float) + 15) & ~(size_t)15;
 }
 
-template <int D, int LB, bool MS>
+template <int T, int D, int LB, bool MS>
 __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
                                                         const float *__restrict__ x) {
     extern __shared__ float smem[];
@@ -1671,17 +1677,14 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t r
     const int XS = x_stride(K), SS = s_stride(K);
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DMA_SLOT;
-    B1DmaQ4K<D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
+    char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
+    B1Dma<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
     stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
-    p.run(xs, ss, XS, SS, part);
+    XReg<T> xa;
+    p.x_from_lds(xa, xs, ss, XS, SS);
+    p.run(xa, part);
 }
 
-// Two formats with the same K and work-group shape (the K-quants: same units
-// per row) and the same activations in one launch: the first `gb` work-groups
-// serve the rows of format TB, the others those of format TA, side by side
-// (the host splits the grid so that both sides end together, counting whole
-// row steps); each stages the activations and makes one pass.
 // One side of a mixed launch: this work-group's share of the rows of one
 // format (Q4_K through the LDS ring when DMA is set).
 template <int T, int D, bool DMA>
@@ -1692,10 +1695,12 @@ __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int l
     const int XS = x_stride(K), SS = s_stride(K);
     float *ss = xs + XS;
     if constexpr (DMA && T == T_Q4_K) {
-        char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DMA_SLOT;
-        B1DmaQ4K<D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
+        char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
+        B1Dma<T, D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
         stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
-        p.run(xs, ss, XS, SS, part);
+        XReg<T> xa;
+        p.x_from_lds(xa, xs, ss, XS, SS);
+        p.run(xa, part);
     } else {
         B1Pass<T, D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
         stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
@@ -2514,27 +2519,32 @@ int launch_qgemv1_cfg(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
-// Q4_K batch-1 launches with the weight ring in LDS (qgemv1_dma_kernel): the
-// same work-group shapes and ring depths as the register ring; needs 16-byte
-// aligned matrices and the ring's LDS beside the activations.
+// Batch-1 launches with the weight ring in LDS (qgemv1_dma_kernel), for Q4_K:
+// the same work-group shapes and ring depths as the register ring (2 steps
+// with 16 waves, 4 with 8); needs 16-byte aligned matrices and rows and the
+// ring's LDS beside the staged activations.  (The same pass for Q6_K, with
+// each lane's activations loaded from global memory to make room for the
+// ring, measured 3-10 % slower than its register ring.)
 constexpr size_t LDS_MAX = 160 * 1024;
+template <int T> constexpr bool DMA_FMT() { return T == T_Q4_K; }
 template <bool WIDE> constexpr int DMA_DEPTH() { return WIDE ? 2 : 4; }
-inline size_t dma_lds(const B1Cfg &c, int K) {
-    return b1_ring_offset(K) + (size_t)(c.ns * c.rs) * (c.wide ? DMA_DEPTH<true>() : DMA_DEPTH<false>()) * DMA_SLOT;
+template <int T> size_t dma_lds(const B1Cfg &c, int K) {
+    return b1_ring_offset(K) +
+           (size_t)(c.ns * c.rs) * (c.wide ? DMA_DEPTH<true>() : DMA_DEPTH<false>()) * DmaGeom<T>::SLOT;
 }
-inline bool dma_ok(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K) {
-    if (row_bytes % 16 || dma_lds(c, K) > LDS_MAX) return false;
+template <int T> bool dma_ok(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K) {
+    if (row_bytes % 16 || dma_lds<T>(c, K) > LDS_MAX) return false;
     for (int i = 0; i < sg.n; ++i)
         if ((uintptr_t)sg.W[i] % 16) return false;
     return true;
 }
-template <bool WIDE>
+template <int T, bool WIDE>
 int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
     constexpr int D = DMA_DEPTH<WIDE>(), LB = WIDE ? 1024 : 512;
     const int nt = 64 * c.ns * c.rs;
     const int G = 64 / c.lpr;
-    const size_t lds = dma_lds(c, K);
-    auto kern = sg.n > 1 ? qgemv1_dma_kernel<D, LB, true> : qgemv1_dma_kernel<D, LB, false>;
+    const size_t lds = dma_lds<T>(c, K);
+    auto kern = sg.n > 1 ? qgemv1_dma_kernel<T, D, LB, true> : qgemv1_dma_kernel<T, D, LB, false>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
     const int64_t need = (slots + c.rs - 1) / c.rs;
@@ -2548,10 +2558,10 @@ int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
 // unit, stripes of 64 units, one work-group per compute unit (persistent).
 template <int T>
 int launch_qgemv1(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
-    if constexpr (T == T_Q4_K) {
-        if (dma_ok(c, sg, row_bytes, K))
-            return c.wide ? launch_qgemv1_dma<true>(c, sg, row_bytes, K, x, st)
-                          : launch_qgemv1_dma<false>(c, sg, row_bytes, K, x, st);
+    if constexpr (DMA_FMT<T>()) {
+        if (dma_ok<T>(c, sg, row_bytes, K))
+            return c.wide ? launch_qgemv1_dma<T, true>(c, sg, row_bytes, K, x, st)
+                          : launch_qgemv1_dma<T, false>(c, sg, row_bytes, K, x, st);
     }
     if constexpr (NARROW_MAX_STRIPES<T>() > 0) {
         if (!c.wide) return launch_qgemv1_cfg<T, false>(c, sg, row_bytes, K, x, st);
@@ -2796,8 +2806,8 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
         // the Q4_K side through the LDS ring
         B1Cfg cq = ca;
         cq.wide = !narrow;
-        if (dma_ok(cq, TA == T_Q4_K ? sa : sb, TA == T_Q4_K ? rba : rbb, K)) {
-            lds = std::max(lds, dma_lds(cq, K));
+        if (dma_ok<T_Q4_K>(cq, TA == T_Q4_K ? sa : sb, TA == T_Q4_K ? rba : rbb, K)) {
+            lds = std::max(lds, dma_lds<T_Q4_K>(cq, K));
             kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true>
                           : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true>;
         }
