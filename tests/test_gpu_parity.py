@@ -331,6 +331,37 @@ def test_full_size_sampled_rows(name, qtype, N, K, M):
     del W
 
 
+# Q4_K batch-1 launches stream the weights through a ring in LDS when the ring
+# fits beside the staged activations (K <= 13568); shapes at the edges of that
+# path: two and four short rows per wave step, a ragged row count, three
+# stripes of 15 waves, the longest rows that fit (a partial last stripe, 163456
+# of 163840 LDS bytes) and the first that do not (register ring).  Each is
+# checked on sampled rows against the oracle and bit for bit against the
+# two-row kernel (a row's bits do not depend on M).
+Q4K_RING = [(65536, 2048), (100003, 1024), (24000, 12288), (9000, 13568), (5000, 13824)]
+
+
+@pytest.mark.parametrize("N,K", Q4K_RING)
+def test_q4k_lds_ring_shapes(N, K):
+    qtype = kqsynth.Q4_K
+    say("q4k ring", N, K)
+    W = kqsynth.device_matrix(qtype, N, K, seed=N + K, device="cuda")
+    x = kqsynth.activations(2, K, kqsynth.rng_for(11, N, K))
+    y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((2, N), dtype=torch.float32, device="cuda")
+    kq.kq_qgemv(qtype, W, N, K, dev(x[:1]), 1, y1)
+    kq.kq_qgemv(qtype, W, N, K, dev(x), 2, y2)
+    torch.cuda.synchronize()
+    a, b = y1.cpu().numpy()[0], y2.cpu().numpy()[0]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "M = 1 and M = 2 rows differ"
+    rows = np.unique(np.concatenate([[0, 1, 2, 3, N - 1, N - 2], np.random.default_rng(N).integers(0, N, 40)]))
+    Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yo, S = oracle.gemv(qtype, Wr, len(rows), K, x[:1])
+    worst = check_close(y1.cpu().numpy()[:, rows], yo, S, "Q4_K %dx%d" % (N, K))
+    say("  worst |dy|/bound", worst)
+    del W
+
+
 # ---- routed experts ---------------------------------------------------------------
 
 def moe_inputs(qtype, E, N, K, T, k, seed, x_mode):
