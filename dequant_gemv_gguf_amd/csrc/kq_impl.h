@@ -40,7 +40,8 @@
 //
 // Kernels: qgemv1_kernel (M = 1, persistent, one work-group per compute unit,
 // several matrices of one format per launch), qgemv1_dma_kernel (its Q4_K form
-// with the weight ring in LDS, filled by buffer-to-LDS loads),
+// with the weight ring in LDS, filled by buffer-to-LDS loads; qgemv1m_dma_kernel
+// the same at M = 2 for short launches),
 // qgemv1_mixed_kernel (the same for two formats side by side), qgemvm_kernel (M = 2..8, persistent),
 // qgemv_kernel and qgemv_seg_kernel (non-persistent, activations staged per
 // work-group: small launches at M = 1 and rows too long for the persistent
@@ -1335,11 +1336,12 @@ __device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, SegCurs
 }
 
 // Output slot of a row, or NULL for a padding row or a row past the end.
-template <bool MS> __device__ __forceinline__ float *out_of(const Segs &sg, int N, int row) {
+// (m: the activation row; a segment's outputs are [M][rows])
+template <bool MS> __device__ __forceinline__ float *out_of(const Segs &sg, int N, int row, int m = 0) {
     if (row >= N) return nullptr;
     const int s = seg_of<MS>(sg, row);
     const int local = row - sg.start[s];
-    return local < sg.rows[s] ? sg.y[s] + local : nullptr;
+    return local < sg.rows[s] ? sg.y[s] + (int64_t)m * sg.rows[s] + local : nullptr;
 }
 
 // Registers <- LDS for one unit's activations (same values as XReg::load).
@@ -1370,11 +1372,11 @@ template <bool DMA> __device__ __forceinline__ void wg_sync() {
 template <bool MS, bool DMA = false>
 __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first, int rstride, int N, int ns,
                                        int wave, int lane, int rsl, int stripe, int grp, int slot,
-                                       float (*part)[64], const Segs &sg) {
+                                       float (*part)[64], const Segs &sg, int m = 0) {
     if (ns > 1) {
         part[wave][lane] = keep;
         wg_sync<DMA>();
-        float *o = out_of<MS>(sg, N, first + (b0 + lane) * rstride);
+        float *o = out_of<MS>(sg, N, first + (b0 + lane) * rstride, m);
         if (stripe == 0 && b0 + lane < wsteps && o) {
             float s = 0.f;
             for (int w = 0; w < ns; ++w) s += part[rsl * ns + w][lane];
@@ -1382,7 +1384,7 @@ __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first
         }
         wg_sync<DMA>();
     } else {
-        float *o = out_of<MS>(sg, N, first + (b0 + slot) * rstride + grp);
+        float *o = out_of<MS>(sg, N, first + (b0 + slot) * rstride + grp, m);
         if (b0 + slot < wsteps && o) *o = 0.f + keep;
     }
 }
@@ -1558,7 +1560,17 @@ __device__ __forceinline__ void read_unit(RawQ4K &r, const char *blk, int g) {
     r.qa = *reinterpret_cast<const u4 *>(blk + 16 + 32 * g);
     r.qb = *reinterpret_cast<const u4 *>(blk + 32 + 32 * g);
 }
-template <int T, int D, bool MS> struct B1Dma {
+// M activation rows held in registers, one XReg each (the LDS-ring pass at
+// M = 2: with the weight ring in LDS two rows' activations fit the registers
+// of an 8-wave work-group).
+template <int T, int M> struct XRegM {
+    static constexpr bool FENCE = false;
+    XReg<T> r[M];
+    __device__ __forceinline__ f4 x4(int m, int off) const { return r[m].x4(0, off); }
+    __device__ __forceinline__ float sum(int m, int run) const { return r[m].sum(0, run); }
+};
+
+template <int T, int D, bool MS, int M = 1> struct B1Dma {
     typedef Fmt<T> F;
     typedef DmaGeom<T> GM;
     typedef typename RawOf<T>::type Raw;
@@ -1615,14 +1627,22 @@ template <int T, int D, bool MS> struct B1Dma {
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(d, d);
     }
-    __device__ __forceinline__ void flush(float keep, int b0, float (*part)[64]) {
-        flush1<MS, true>(keep, b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
+    __device__ __forceinline__ void flush(const float (&keep)[M], int b0, float (*part)[64]) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            flush1<MS, true>(keep[m], b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg,
+                             m);
     }
-    __device__ __forceinline__ float value(const Raw &r, const XReg<T> &xa) const {
+    // park the step's row sums (one per activation row) in lane `step mod lpr`
+    template <class XA> __device__ __forceinline__ void value(const Raw &r, const XA &xa, int step, float (&keep)[M]) const {
         const Raw rr[1] = {r};
-        float v[1][1];
-        val_unit<1, 1>(rr, sub, xa, v);
-        return group_sum(act ? v[0][0] : 0.f, lpr);
+        float v[1][M];
+        val_unit<M, 1>(rr, sub, xa, v);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float S = group_sum(act ? v[0][m] : 0.f, lpr);
+            keep[m] = (slot == (step & (lpr - 1))) ? S : keep[m];
+        }
     }
     // activations of the lane's unit from the staged copy in LDS
     __device__ __forceinline__ void x_from_lds(XReg<T> &xa, const float *xs, const float *ss, int XS, int SS) const {
@@ -1631,8 +1651,10 @@ template <int T, int D, bool MS> struct B1Dma {
         xreg_from_lds<T>(xa, xl);
     }
     // the loads of the first D steps must have been issued (issue_first)
-    __device__ __forceinline__ void run(const XReg<T> &xa, float (*part)[64]) {
-        float keep = 0.f;
+    template <class XA> __device__ __forceinline__ void run(const XA &xa, float (*part)[64]) {
+        float keep[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) keep[m] = 0.f;
         int j = 0;
         for (; j + D <= wsteps; j += D) {
 #pragma unroll
@@ -1642,8 +1664,7 @@ template <int T, int D, bool MS> struct B1Dma {
                 read_unit(r, ring + d * GM::SLOT + lofs, sub);
                 wait_lgkm0();
                 issue(d, j + d + D);
-                const float S = value(r, xa);
-                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+                value(r, xa, j + d, keep);
             }
             if (((j + D) & (lpr - 1)) == 0) flush(keep, j + D - lpr, part);
             wg_sync<true>();
@@ -1654,8 +1675,7 @@ template <int T, int D, bool MS> struct B1Dma {
             if (j + d < wsteps) {
                 Raw r;
                 read_unit(r, ring + d * GM::SLOT + lofs, sub);
-                const float S = value(r, xa);
-                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+                value(r, xa, j + d, keep);
             }
         }
         if (wsteps & (lpr - 1)) flush(keep, wsteps & ~(lpr - 1), part);
@@ -1664,8 +1684,8 @@ template <int T, int D, bool MS> struct B1Dma {
 
 // LDS of the batch-1 kernels: [16][64] flush area, the staged activations and
 // 16-sums, then (ring in LDS) the weight ring, 16-byte aligned.
-__host__ __device__ constexpr size_t b1_ring_offset(int K) {
-    return ((size_t)(16 * 64 + x_stride(K) + s_stride(K)) * sizeof(float) + 15) & ~(size_t)15;
+__host__ __device__ constexpr size_t b1_ring_offset(int K, int M = 1) {
+    return ((size_t)(16 * 64 + M * (x_stride(K) + s_stride(K))) * sizeof(float) + 15) & ~(size_t)15;
 }
 
 template <int T, int D, int LB, bool MS>
@@ -1682,6 +1702,61 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t r
     stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
     XReg<T> xa;
     p.x_from_lds(xa, xs, ss, XS, SS);
+    p.run(xa, part);
+}
+
+// Prologue of the M-row LDS-ring kernel: stage_x1 for M activation rows (row
+// m at xs + m * (XS + SS), its 16-sums right after it), every activation load
+// ahead of `issue`.
+template <int M, class Issue>
+__device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, float *smem, float *xs, int XS, int SS,
+                                         Issue issue) {
+    const int nthreads = blockDim.x;
+    const int n16 = K >> 4;
+    f4 xg[M][2][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int idx = threadIdx.x + it * nthreads;
+            const f4 *src = reinterpret_cast<const f4 *>(x + (int64_t)m * K + 16 * (idx < n16 ? idx : 0));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xg[m][it][k] = src[k];
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int idx = threadIdx.x + it * nthreads;
+            const bool ok = idx < n16;
+            float *xm = xs + m * (XS + SS);
+            f4 *dst = reinterpret_cast<f4 *>(ok ? xm + xpad(16 * idx) : smem);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dst[k] = xg[m][it][k];
+            (ok ? xm[XS + idx] : smem[16]) = sum16(xg[m][it][0], xg[m][it][1], xg[m][it][2], xg[m][it][3]);
+        }
+    wg_sync<true>();
+}
+
+// The LDS-ring kernel at M > 1 (used for Q4_K at M = 2): 8 waves, both
+// activation rows in registers, the same per-row sums as at M = 1.
+template <int T, int D, int LB, bool MS, int M>
+__global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
+                                                         const float *__restrict__ x) {
+    extern __shared__ float smem[];
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K, M) + (size_t)wave * D * DmaGeom<T>::SLOT;
+    B1Dma<T, D, MS, M> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
+    stage_xm<M>(x, K, smem, xs, XS, SS, [&] { p.issue_first(); });
+    XRegM<T, M> xa;
+#pragma unroll
+    for (int m = 0; m < M; ++m) p.x_from_lds(xa.r[m], xs + m * (XS + SS), xs + m * (XS + SS) + XS, XS, SS);
     p.run(xa, part);
 }
 
@@ -2595,8 +2670,45 @@ template <int T, int M> constexpr int MRING() { return (BIG_UNIT<T>() && M > 4) 
 // Batch-M launch over one or more segments (starts padded to the row step).
 // Returns KQ_ERR_ARG when the activations of one 4096-column chunk do not fit
 // in LDS next to the row sums (then the caller uses the LDS kernel).
+// Q4_K at M = 2 on the LDS-ring kernel (8 waves, a ring of 2 steps) for short
+// launches -- at most DMA_M_STEPS row steps per row slot, where it beats the
+// batch-M kernel (70B wk + wq 20.3 -> 17.3 us, wk 10.1 -> 6.5 us); longer ones
+// run faster on the batch-M kernel (w1 28672 x 8192 37.6 vs 40.0 us).
+// KQ_ERR_ARG when the launch is long or does not fit (more than 8 stripes,
+// activations and ring beyond the LDS).
+constexpr int64_t DMA_M_STEPS = 10;
+template <int T, int M>
+int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    constexpr int D = 2, LB = 512;
+    const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
+    const int lpr = lanes_per_row(units);
+    const int ns = units > 64 ? (units + 63) / 64 : 1;
+    if (ns > 8) return KQ_ERR_ARG;
+    const int rs = 8 / ns;
+    if (K / 16 > 2 * 64 * ns * rs) return KQ_ERR_ARG;
+    const size_t lds = b1_ring_offset(K, M) + (size_t)(ns * rs) * D * DmaGeom<T>::SLOT;
+    if (row_bytes % 16 || lds > LDS_MAX) return KQ_ERR_ARG;
+    for (int i = 0; i < sg.n; ++i)
+        if ((uintptr_t)sg.W[i] % 16) return KQ_ERR_ARG;
+    const int G = 64 / lpr;
+    const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
+    const int64_t need = (slots + rs - 1) / rs;
+    const int64_t cap = cu_count();
+    const int grid = (int)(need < cap ? need : cap);
+    if (grid == 0) return KQ_OK;
+    if ((need + grid - 1) / grid > DMA_M_STEPS) return KQ_ERR_ARG;
+    auto kern = sg.n > 1 ? qgemv1m_dma_kernel<T, D, LB, true, M> : qgemv1m_dma_kernel<T, D, LB, false, M>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ns * rs), lds, st, sg, row_bytes, K, lpr, ns, x);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
 template <int T, int M>
 int launch_qgemvm(const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
+    if constexpr (T == T_Q4_K && M == 2) {
+        const int r = launch_qgemvm_dma<T, M>(sg, row_bytes, K, x, st);
+        if (r != KQ_ERR_ARG) return r;
+    }
     constexpr int R = MROWS<T, M>(), D = MRING<T, M>(), NW = 8;
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);

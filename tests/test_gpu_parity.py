@@ -362,6 +362,39 @@ def test_q4k_lds_ring_shapes(N, K):
     del W
 
 
+# Q4_K at M = 2 in short launches (at most 10 row steps per row slot) runs the
+# LDS-ring kernel with both activation rows in registers: a 70B wk + wq group,
+# wo, an 8B projection and a ragged short-row matrix; sampled rows against the
+# oracle and every row bit for bit against M = 1.
+Q4K_RING_M2 = [([1024, 8192], 8192), ([8192], 8192), ([4096], 4096), ([5001], 2048), ([3], 8192)]
+
+
+@pytest.mark.parametrize("Ns,K", Q4K_RING_M2)
+def test_q4k_lds_ring_two_rows(Ns, K):
+    qtype = kqsynth.Q4_K
+    say("q4k ring M=2", Ns, K)
+    Ws = [kqsynth.device_matrix(qtype, n, K, seed=77 + i, device="cuda") for i, n in enumerate(Ns)]
+    x = kqsynth.activations(2, K, kqsynth.rng_for(12, K, len(Ns)))
+    y1 = [torch.empty((1, n), dtype=torch.float32, device="cuda") for n in Ns]
+    y2 = [torch.empty((2, n), dtype=torch.float32, device="cuda") for n in Ns]
+    types = [qtype] * len(Ns)
+    kq.kq_qgemv_multi(types, Ws, Ns, K, dev(x[:1]), 1, y1)
+    kq.kq_qgemv_multi(types, Ws, Ns, K, dev(x), 2, y2)
+    x1 = x[1:2].copy()
+    y1b = [torch.empty((1, n), dtype=torch.float32, device="cuda") for n in Ns]
+    kq.kq_qgemv_multi(types, Ws, Ns, K, dev(x1), 1, y1b)
+    torch.cuda.synchronize()
+    for i, n in enumerate(Ns):
+        a = y2[i].cpu().numpy()
+        assert np.array_equal(a[0].view(np.uint32), y1[i].cpu().numpy()[0].view(np.uint32)), "row 0 differs from M = 1"
+        assert np.array_equal(a[1].view(np.uint32), y1b[i].cpu().numpy()[0].view(np.uint32)), "row 1 differs from M = 1"
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).integers(0, n, 30)]))
+        Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
+        worst = check_close(a[:, rows], yo, S, "Q4_K M=2 %dx%d" % (n, K))
+        say("  worst |dy|/bound", worst)
+
+
 # ---- routed experts ---------------------------------------------------------------
 
 def moe_inputs(qtype, E, N, K, T, k, seed, x_mode):
