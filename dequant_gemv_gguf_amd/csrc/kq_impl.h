@@ -1537,13 +1537,14 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
 // buffer-to-LDS loads of 16 bytes per lane (lane i: bytes 1024k + 16i), each
 // covering whole 128-byte lines, so they can bypass the caches (non-temporal)
 // without a line being fetched twice; each lane then reads its unit's header
-// and quant bytes from LDS.  Compared
-// with the register ring of B1Pass this frees the ring's registers, and every
-// load instruction is a single coalesced 1-KB request.  The compiler does not
-// order LDS reads after these loads, so the waits are explicit: before
-// reading slot d a wave lets at most NLD(D-1) loads stay outstanding (those of
-// the D-1 later steps; loads complete in issue order).  Requires 16-byte
-// aligned matrices and rows.
+// and quant bytes from LDS.  Compared with the register ring of B1Pass this
+// frees the ring's registers, and every load instruction is a single
+// coalesced 1-KB request.  The compiler does not order LDS reads after these
+// loads, so the waits are explicit: before reading slot d a wave lets at most
+// NLD(D-1) loads stay outstanding (those of the D-1 later steps; loads
+// complete in issue order, and a store issued in between only makes the wait
+// stricter), and its reads of a slot complete before the slot is refilled.
+// Requires 16-byte aligned matrices and rows.
 #define KQ_LDS __attribute__((address_space(3)))
 
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
