@@ -1571,7 +1571,7 @@ template <int T, int M> struct XRegM {
     __device__ __forceinline__ float sum(int m, int run) const { return r[m].sum(0, run); }
 };
 
-template <int T, int D, bool MS, int M = 1> struct B1Dma {
+template <int T, int D, bool MS, int M = 1, int LP = 0> struct B1Dma {
     typedef Fmt<T> F;
     typedef DmaGeom<T> GM;
     typedef typename RawOf<T>::type Raw;
@@ -1582,6 +1582,11 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
     u32 rbase, span, lofs;
     char *ring;   // this wave's D slots
     SegCursor<MS> cur;
+    int irow;              // first row of the next step to issue
+    const uint8_t *iptr;   // its bytes (valid while irow is in the cursor's segment)
+    int64_t sbytes;        // bytes between a row slot's consecutive steps
+    // lanes per row: LP when fixed at compile time (64: rows of >= 64 units)
+    __device__ __forceinline__ int lp() const { return LP ? LP : lpr; }
 
     __device__ __forceinline__ B1Dma(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_, int wg,
                                      int nwg, char *ring_)
@@ -1608,14 +1613,25 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
         // a lane's block inside the slot (inactive lanes stay inside the slot)
         lofs = (u32)(grp * (ns > 1 ? 0 : rb)) + (u32)(slot / F::UPB) * F::BYTES;
         cur.set(sg, 0);
+        irow = first;
+        iptr = cur.W + (int64_t)first * rb;
+        sbytes = (int64_t)rstride * rb;
     }
-    __device__ __forceinline__ void issue(int d, int step) {
-        const int row0 = first + step * rstride;
-        cur.seek(sg, row0);
+    // the loads of the wave's next row step (steps are issued in order)
+    __device__ __forceinline__ void issue(int d) {
+        const int row0 = irow;
+        if constexpr (MS) {
+            if ((unsigned)(row0 - cur.start) >= (unsigned)(cur.next - cur.start)) {
+                cur.set(sg, seg_of<MS>(sg, row0));
+                iptr = cur.W + (int64_t)(row0 - cur.start) * row_bytes;
+            }
+        }
         const int local = row0 - cur.start;
         const int left = cur.rows - local;
         const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
-        const rsrc_t rs = make_rsrc(cur.W + (int64_t)(nr ? local : 0) * row_bytes, (u32)((int64_t)nr * row_bytes));
+        const rsrc_t rs = make_rsrc(nr ? iptr : cur.W, (u32)((int64_t)nr * row_bytes));
+        irow = row0 + rstride;
+        iptr += sbytes;
         char *dst = ring + d * GM::SLOT;
 #pragma unroll
         for (int k = 0; k < GM::NLD; ++k) {
@@ -1626,7 +1642,7 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
     }
     __device__ __forceinline__ void issue_first() {
 #pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, d);
+        for (int d = 0; d < D; ++d) issue(d);
     }
     __device__ __forceinline__ void flush(const float (&keep)[M], int b0, float (*part)[64]) {
 #pragma unroll
@@ -1641,8 +1657,8 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
         val_unit<M, 1>(rr, sub, xa, v);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float S = group_sum(act ? v[0][m] : 0.f, lpr);
-            keep[m] = (slot == (step & (lpr - 1))) ? S : keep[m];
+            const float S = group_sum(act ? v[0][m] : 0.f, lp());
+            keep[m] = (slot == (step & (lp() - 1))) ? S : keep[m];
         }
     }
     // activations of the lane's unit from the staged copy in LDS
@@ -1664,10 +1680,10 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
                 wait_vm<GM::NLD * (D - 1)>();
                 read_unit(r, ring + d * GM::SLOT + lofs, sub);
                 wait_lgkm0();
-                issue(d, j + d + D);
+                issue(d);
                 value(r, xa, j + d, keep);
             }
-            if (((j + D) & (lpr - 1)) == 0) flush(keep, j + D - lpr, part);
+            if (((j + D) & (lp() - 1)) == 0) flush(keep, j + D - lp(), part);
             wg_sync<true>();
         }
         wait_vm<0>();
@@ -1679,7 +1695,7 @@ template <int T, int D, bool MS, int M = 1> struct B1Dma {
                 value(r, xa, j + d, keep);
             }
         }
-        if (wsteps & (lpr - 1)) flush(keep, wsteps & ~(lpr - 1), part);
+        if (wsteps & (lp() - 1)) flush(keep, wsteps & ~(lp() - 1), part);
     }
 };
 
@@ -1689,7 +1705,7 @@ __host__ __device__ constexpr size_t b1_ring_offset(int K, int M = 1) {
     return ((size_t)(16 * 64 + M * (x_stride(K) + s_stride(K))) * sizeof(float) + 15) & ~(size_t)15;
 }
 
-template <int T, int D, int LB, bool MS>
+template <int T, int D, int LB, bool MS, int LP>
 __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
                                                         const float *__restrict__ x) {
     extern __shared__ float smem[];
@@ -1699,7 +1715,7 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t r
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
-    B1Dma<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
+    B1Dma<T, D, MS, 1, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
     stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
     XReg<T> xa;
     p.x_from_lds(xa, xs, ss, XS, SS);
@@ -1744,7 +1760,7 @@ __device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, flo
 
 // The LDS-ring kernel at M > 1 (used for Q4_K at M = 2): 8 waves, both
 // activation rows in registers, the same per-row sums as at M = 1.
-template <int T, int D, int LB, bool MS, int M>
+template <int T, int D, int LB, bool MS, int M, int LP>
 __global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
                                                          const float *__restrict__ x) {
     extern __shared__ float smem[];
@@ -1753,7 +1769,7 @@ __global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t 
     const int XS = x_stride(K), SS = s_stride(K);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K, M) + (size_t)wave * D * DmaGeom<T>::SLOT;
-    B1Dma<T, D, MS, M> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
+    B1Dma<T, D, MS, M, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
     stage_xm<M>(x, K, smem, xs, XS, SS, [&] { p.issue_first(); });
     XRegM<T, M> xa;
 #pragma unroll
@@ -2620,7 +2636,9 @@ int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     const int nt = 64 * c.ns * c.rs;
     const int G = 64 / c.lpr;
     const size_t lds = dma_lds<T>(c, K);
-    auto kern = sg.n > 1 ? qgemv1_dma_kernel<T, D, LB, true> : qgemv1_dma_kernel<T, D, LB, false>;
+    // rows of 64 units or more (lpr 64) get the kernel with the lane count fixed
+    auto kern = sg.n > 1 ? (c.lpr == 64 ? qgemv1_dma_kernel<T, D, LB, true, 64> : qgemv1_dma_kernel<T, D, LB, true, 0>)
+                         : (c.lpr == 64 ? qgemv1_dma_kernel<T, D, LB, false, 64> : qgemv1_dma_kernel<T, D, LB, false, 0>);
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
     const int64_t need = (slots + c.rs - 1) / c.rs;
@@ -2698,7 +2716,8 @@ int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, 
     const int grid = (int)(need < cap ? need : cap);
     if (grid == 0) return KQ_OK;
     if ((need + grid - 1) / grid > DMA_M_STEPS) return KQ_ERR_ARG;
-    auto kern = sg.n > 1 ? qgemv1m_dma_kernel<T, D, LB, true, M> : qgemv1m_dma_kernel<T, D, LB, false, M>;
+    auto kern = sg.n > 1 ? (lpr == 64 ? qgemv1m_dma_kernel<T, D, LB, true, M, 64> : qgemv1m_dma_kernel<T, D, LB, true, M, 0>)
+                         : (lpr == 64 ? qgemv1m_dma_kernel<T, D, LB, false, M, 64> : qgemv1m_dma_kernel<T, D, LB, false, M, 0>);
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ns * rs), lds, st, sg, row_bytes, K, lpr, ns, x);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
