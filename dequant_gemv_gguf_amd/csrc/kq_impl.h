@@ -1317,24 +1317,6 @@ template <bool MS> struct SegCursor {
     }
 };
 
-// Issue the loads of one row step (rows row0 .. row0 + G - 1, one per lane
-// group).  Never conditional: a step past the last row gets an empty buffer
-// (its loads return zeros), so the loads of every ring slot stay in flight in
-// program order.
-template <int T, bool MS>
-__device__ __forceinline__ void issue_step(typename RawOf<T>::type &raw, SegCursor<MS> &cur, const Segs &sg,
-                                           int64_t row_bytes, int N, int G, int row0, int grp, bool act, u32 boff,
-                                           int sub) {
-    cur.seek(sg, row0);
-    const int local = row0 - cur.start;
-    const int left = cur.rows - local;
-    const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
-    const uintptr_t ta = (uintptr_t)(cur.W + (int64_t)(nr ? local : 0) * row_bytes);
-    const u32 delta = (u32)(ta & 3u);
-    const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
-    load_unit(raw, rs, (act && grp < nr) ? delta + (u32)((int64_t)grp * row_bytes) + boff : OOB, sub);
-}
-
 // Output slot of a row, or NULL for a padding row or a row past the end.
 // (m: the activation row; a segment's outputs are [M][rows])
 template <bool MS> __device__ __forceinline__ float *out_of(const Segs &sg, int N, int row, int m = 0) {
@@ -1394,7 +1376,7 @@ __device__ __forceinline__ void flush1(float keep, int b0, int wsteps, int first
 // owns one stripe of one row slot: its lane's unit never changes, so the
 // unit's activations are read from LDS into registers once, and every step
 // only streams weights.
-template <int T, int D, bool MS> struct B1Pass {
+template <int T, int D, bool MS, int LP = 0> struct B1Pass {
     typedef Fmt<T> F;
     typedef typename RawOf<T>::type Raw;
     const Segs &sg;
@@ -1404,6 +1386,11 @@ template <int T, int D, bool MS> struct B1Pass {
     u32 boff;
     SegCursor<MS> cur;
     Raw ring[D][1];
+    int irow;              // first row of the next step to issue
+    const uint8_t *iptr;   // its bytes (valid while irow is in the cursor's segment)
+    int64_t sbytes;        // bytes between a row slot's consecutive steps
+    // lanes per row: LP when fixed at compile time (64: rows of >= 64 units)
+    __device__ __forceinline__ int lp() const { return LP ? LP : lpr; }
 
     // wg / nwg: this work-group's index among the nwg that share the rows
     __device__ __forceinline__ B1Pass(const Segs &s, int64_t rb, int K, int lpr_, int ns_, int wave_, int lane_,
@@ -1430,13 +1417,36 @@ template <int T, int D, bool MS> struct B1Pass {
         const int f0 = wg * RS * G;
         wsteps = f0 < N ? (N - f0 + rstride - 1) / rstride : 0;
         cur.set(sg, 0);
+        irow = first;
+        iptr = cur.W + (int64_t)first * rb;
+        sbytes = (int64_t)rstride * rb;
     }
-    __device__ __forceinline__ void issue(int d, int step) {
-        issue_step<T, MS>(ring[d][0], cur, sg, row_bytes, N, G, first + step * rstride, grp, act, boff, sub);
+    // the loads of the wave's next row step (rows irow .. irow + G - 1, one per
+    // lane group; steps are issued in order, so the step's address is carried
+    // forward).  Never conditional: a step past the last row gets an empty
+    // buffer (its loads return zeros), so the loads of every ring slot stay
+    // in flight in program order.
+    __device__ __forceinline__ void issue(int d) {
+        const int row0 = irow;
+        if constexpr (MS) {
+            if ((unsigned)(row0 - cur.start) >= (unsigned)(cur.next - cur.start)) {
+                cur.set(sg, seg_of<MS>(sg, row0));
+                iptr = cur.W + (int64_t)(row0 - cur.start) * row_bytes;
+            }
+        }
+        const int local = row0 - cur.start;
+        const int left = cur.rows - local;
+        const int nr = row0 >= N || left <= 0 ? 0 : (left < G ? left : G);
+        const uintptr_t ta = (uintptr_t)(nr ? iptr : cur.W);
+        const u32 delta = (u32)(ta & 3u);
+        const rsrc_t rs = make_rsrc((const void *)(ta - delta), nr ? delta + (u32)((int64_t)nr * row_bytes) : 0u);
+        load_unit(ring[d][0], rs, (act && grp < nr) ? delta + (u32)((int64_t)grp * row_bytes) + boff : OOB, sub);
+        irow = row0 + rstride;
+        iptr += sbytes;
     }
     __device__ __forceinline__ void issue_first() {
 #pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, d);
+        for (int d = 0; d < D; ++d) issue(d);
     }
     __device__ __forceinline__ void flush(float keep, int b0, float (*part)[64]) {
         flush1<MS>(keep, b0, wsteps, first, rstride, N, ns, wave, lane, rsl, stripe, grp, slot, part, sg);
@@ -1456,11 +1466,11 @@ template <int T, int D, bool MS> struct B1Pass {
             for (int d = 0; d < D; ++d) {
                 float v[1][1];
                 val_unit<1, 1>(ring[d], sub, xa, v);
-                issue(d, j + d + D);
-                const float S = group_sum(act ? v[0][0] : 0.f, lpr);
-                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+                issue(d);
+                const float S = group_sum(act ? v[0][0] : 0.f, lp());
+                keep = (slot == ((j + d) & (lp() - 1))) ? S : keep;
             }
-            if (((j + D) & (lpr - 1)) == 0) flush(keep, j + D - lpr, part);
+            if (((j + D) & (lp() - 1)) == 0) flush(keep, j + D - lp(), part);
             // keep the waves of the work-group in step: otherwise the oldest
             // waves race ahead and the work-group ends on a few slow waves
             // with too few loads in flight
@@ -1471,11 +1481,11 @@ template <int T, int D, bool MS> struct B1Pass {
             if (j + d < wsteps) {
                 float v[1][1];
                 val_unit<1, 1>(ring[d], sub, xa, v);
-                const float S = group_sum(act ? v[0][0] : 0.f, lpr);
-                keep = (slot == ((j + d) & (lpr - 1))) ? S : keep;
+                const float S = group_sum(act ? v[0][0] : 0.f, lp());
+                keep = (slot == ((j + d) & (lp() - 1))) ? S : keep;
             }
         }
-        if (wsteps & (lpr - 1)) flush(keep, wsteps & ~(lpr - 1), part);
+        if (wsteps & (lp() - 1)) flush(keep, wsteps & ~(lp() - 1), part);
     }
 };
 
@@ -1515,7 +1525,7 @@ __device__ __forceinline__ void stage_x1(const float *__restrict__ x, int K, flo
 
 // Batch-1 kernel: one persistent work-group per compute unit, RS row slots of
 // ns stripe waves.  LDS: [16][64] flush area, then the staged activations.
-template <int T, int D, int LB, bool MS>
+template <int T, int D, int LB, bool MS, int LP>
 __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
                                                     const float *__restrict__ x) {
     extern __shared__ float smem[];
@@ -1526,7 +1536,7 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     // wave index as a scalar: everything derived from it (the row of a step and
     // the buffer descriptor of its loads) stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    B1Pass<T, D, MS> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
+    B1Pass<T, D, MS, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
     stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
     p.run(xs, ss, XS, SS, part);
 }
@@ -2600,8 +2610,10 @@ template <int T, bool WIDE>
 int launch_qgemv1_cfg(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
     const int nt = 64 * c.ns * c.rs;
     const int G = 64 / c.lpr;
-    auto kern = sg.n > 1 ? qgemv1_kernel<T, PREFETCH<T, WIDE>(), WIDE ? 1024 : 512, true>
-                         : qgemv1_kernel<T, PREFETCH<T, WIDE>(), WIDE ? 1024 : 512, false>;
+    constexpr int D = PREFETCH<T, WIDE>(), LB = WIDE ? 1024 : 512;
+    // rows of 64 units or more (lpr 64) get the kernel with the lane count fixed
+    auto kern = sg.n > 1 ? (c.lpr == 64 ? qgemv1_kernel<T, D, LB, true, 64> : qgemv1_kernel<T, D, LB, true, 0>)
+                         : (c.lpr == 64 ? qgemv1_kernel<T, D, LB, false, 64> : qgemv1_kernel<T, D, LB, false, 0>);
     if (allow_lds(kern, c.lds) != hipSuccess) return KQ_ERR_LAUNCH;
     const int64_t slots = ((int64_t)sg.start[sg.n] + G - 1) / G;
     const int64_t need = (slots + c.rs - 1) / c.rs;
