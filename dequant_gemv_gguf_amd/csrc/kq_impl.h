@@ -41,7 +41,7 @@
 // Kernels: qgemv1_kernel (M = 1, persistent, one work-group per compute unit,
 // several matrices of one format per launch), qgemv1_dma_kernel (its Q4_K form
 // with the weight ring in LDS, filled by buffer-to-LDS loads; qgemv1m_dma_kernel
-// the same at M = 2 for short launches),
+// the same at M = 2),
 // qgemv1_mixed_kernel (the same for two formats side by side), qgemvm_kernel (M = 2..8, persistent),
 // qgemv_kernel and qgemv_seg_kernel (non-persistent, activations staged per
 // work-group: small launches at M = 1 and rows too long for the persistent
@@ -2701,20 +2701,19 @@ template <int T, int M> constexpr int MRING() { return (BIG_UNIT<T>() && M > 4) 
 // Batch-M launch over one or more segments (starts padded to the row step).
 // Returns KQ_ERR_ARG when the activations of one 4096-column chunk do not fit
 // in LDS next to the row sums (then the caller uses the LDS kernel).
-// Q4_K at M = 2 on the LDS-ring kernel (8 waves, a ring of 2 steps) for short
-// launches -- at most DMA_M_STEPS row steps per row slot, where it beats the
-// batch-M kernel (70B wk + wq 20.3 -> 17.3 us, wk 10.1 -> 6.5 us); longer ones
-// run faster on the batch-M kernel (w1 28672 x 8192 37.6 vs 40.0 us).
-// KQ_ERR_ARG when the launch is long or does not fit (more than 8 stripes,
-// activations and ring beyond the LDS).
-constexpr int64_t DMA_M_STEPS = 10;
+// Q4_K at M = 2 on the LDS-ring kernel (8 waves, a ring of 2 steps) for rows of
+// 64 units or more whose stripes fill the 8 waves (1, 2, 4 or 8 stripes): it
+// beats the batch-M kernel on short and long launches alike (70B wk + wq 20.3
+// -> 17.3 us, w1 28672 x 8192 36.2 -> 31.7 us, w1 + w3 69.3 -> 63.4 us);
+// with 3 stripes (6 waves busy) or short rows it does not.  KQ_ERR_ARG when
+// the shape does not take it.
 template <int T, int M>
 int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
     constexpr int D = 2, LB = 512;
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);
     const int ns = units > 64 ? (units + 63) / 64 : 1;
-    if (ns > 8) return KQ_ERR_ARG;
+    if (lpr != 64 || 8 % ns) return KQ_ERR_ARG;
     const int rs = 8 / ns;
     if (K / 16 > 2 * 64 * ns * rs) return KQ_ERR_ARG;
     const size_t lds = b1_ring_offset(K, M) + (size_t)(ns * rs) * D * DmaGeom<T>::SLOT;
@@ -2727,9 +2726,7 @@ int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, 
     const int64_t cap = cu_count();
     const int grid = (int)(need < cap ? need : cap);
     if (grid == 0) return KQ_OK;
-    if ((need + grid - 1) / grid > DMA_M_STEPS) return KQ_ERR_ARG;
-    auto kern = sg.n > 1 ? (lpr == 64 ? qgemv1m_dma_kernel<T, D, LB, true, M, 64> : qgemv1m_dma_kernel<T, D, LB, true, M, 0>)
-                         : (lpr == 64 ? qgemv1m_dma_kernel<T, D, LB, false, M, 64> : qgemv1m_dma_kernel<T, D, LB, false, M, 0>);
+    auto kern = sg.n > 1 ? qgemv1m_dma_kernel<T, D, LB, true, M, 64> : qgemv1m_dma_kernel<T, D, LB, false, M, 64>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ns * rs), lds, st, sg, row_bytes, K, lpr, ns, x);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
