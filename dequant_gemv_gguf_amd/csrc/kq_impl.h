@@ -1789,7 +1789,7 @@ __global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t 
 
 // One side of a mixed launch: this work-group's share of the rows of one
 // format (Q4_K through the LDS ring when DMA is set).
-template <int T, int D, bool DMA>
+template <int T, int D, bool DMA, int LP>
 __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int lpr, int ns, int wave, int lane, int wg,
                                         int nwg, const float *__restrict__ x, float *smem) {
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
@@ -1798,28 +1798,28 @@ __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int l
     float *ss = xs + XS;
     if constexpr (DMA && T == T_Q4_K) {
         char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
-        B1Dma<T, D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
+        B1Dma<T, D, true, 1, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
         stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
         XReg<T> xa;
         p.x_from_lds(xa, xs, ss, XS, SS);
         p.run(xa, part);
     } else {
-        B1Pass<T, D, true> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
+        B1Pass<T, D, true, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
         stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
         p.run(xs, ss, XS, SS, part);
     }
 }
 
-template <int TA, int DA, int TB, int DB, int LB, bool DMA>
+template <int TA, int DA, int TB, int DB, int LB, bool DMA, int LP>
 __global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
                                                            int gb, int K, int lpr, int ns,
                                                            const float *__restrict__ x) {
     extern __shared__ float smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if ((int)blockIdx.x < gb)
-        b1_side<TB, DB, DMA>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, x, smem);
+        b1_side<TB, DB, DMA, LP>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, x, smem);
     else
-        b1_side<TA, DA, DMA>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, x, smem);
+        b1_side<TA, DA, DMA, LP>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, x, smem);
 }
 
 // Small grouped launches at M = 1 (the non-persistent counterpart of the
@@ -2941,16 +2941,22 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     const int grid = (int)(ga + gb);
     if (grid == 0) return KQ_OK;
     size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
-    auto kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false>
-                       : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false>;
+    // rows of 64 units or more (lpr 64) get the kernels with the lane count fixed
+    const bool l64 = ca.lpr == 64;
+    auto kern = narrow ? (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 64>
+                              : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 0>)
+                       : (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false, 64>
+                              : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false, 0>);
     if constexpr (TA == T_Q4_K || TB == T_Q4_K) {
         // the Q4_K side through the LDS ring
         B1Cfg cq = ca;
         cq.wide = !narrow;
         if (dma_ok<T_Q4_K>(cq, TA == T_Q4_K ? sa : sb, TA == T_Q4_K ? rba : rbb, K)) {
             lds = std::max(lds, dma_lds<T_Q4_K>(cq, K));
-            kern = narrow ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true>
-                          : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true>;
+            kern = narrow ? (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 64>
+                                 : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 0>)
+                          : (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true, 64>
+                                 : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true, 0>);
         }
     }
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
