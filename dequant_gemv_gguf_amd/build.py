@@ -9,7 +9,11 @@ launchers and kernels of its format or pair).  They are linked with
 build.
 
 All HIP code is compiled with packed fp32 instructions disabled: hipcc would
-otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code."""
+otherwise form v_pk_{add,mul,fma}_f32 from ordinary float code.  The target
+feature has to reach the device compile through -Xclang (the clang driver
+forwards no -Xclang option through -Xarch_device), so the host pass sees it
+too and prints that x86 does not know it; that line is harmless and is
+dropped from the build log."""
 import concurrent.futures
 import os
 import subprocess
@@ -26,6 +30,9 @@ ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+
+# what the host (x86) pass prints for the device-only target feature above
+HOST_FEATURE_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target"
 
 # GGUF type ids of the formats, and the K-quant pairs (lower id first) that
 # kq_impl.h declares mixed launchers for.
@@ -64,7 +71,8 @@ def build(verbose=False, extra=()):
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        return cmd, r.returncode, r.stdout
+        out = "".join(line for line in r.stdout.splitlines(True) if HOST_FEATURE_NOTE not in line)
+        return cmd, r.returncode, out
 
     failed = []
     with concurrent.futures.ThreadPoolExecutor(_jobs()) as pool:

@@ -2702,18 +2702,19 @@ template <int T, int M> constexpr int MRING() { return (BIG_UNIT<T>() && M > 4) 
 // Returns KQ_ERR_ARG when the activations of one 4096-column chunk do not fit
 // in LDS next to the row sums (then the caller uses the LDS kernel).
 // Q4_K at M = 2 on the LDS-ring kernel (8 waves, a ring of 2 steps) for rows of
-// 64 units or more whose stripes fill the 8 waves (1, 2, 4 or 8 stripes): it
-// beats the batch-M kernel on short and long launches alike (70B wk + wq 20.3
-// -> 17.3 us, w1 28672 x 8192 36.2 -> 31.7 us, w1 + w3 69.3 -> 63.4 us);
-// with 3 stripes (6 waves busy) or short rows it does not.  KQ_ERR_ARG when
-// the shape does not take it.
+// 64 units or more in 1 or 2 stripes (K <= 8192; longer rows leave no LDS
+// for the ring beside two staged activation rows): it beats the batch-M
+// kernel on short and long launches alike (70B wk + wq 20.3 -> 17.3 us, w1
+// 28672 x 8192 36.2 -> 31.7 us, w1 + w3 69.3 -> 63.4 us); with 3 stripes (6
+// waves busy) or short rows it does not.  KQ_ERR_ARG when the shape does not
+// take it.
 template <int T, int M>
 int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, hipStream_t st) {
     constexpr int D = 2, LB = 512;
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     const int lpr = lanes_per_row(units);
     const int ns = units > 64 ? (units + 63) / 64 : 1;
-    if (lpr != 64 || 8 % ns) return KQ_ERR_ARG;
+    if (lpr != 64 || ns > 2) return KQ_ERR_ARG;
     const int rs = 8 / ns;
     if (K / 16 > 2 * 64 * ns * rs) return KQ_ERR_ARG;
     const size_t lds = b1_ring_offset(K, M) + (size_t)(ns * rs) * D * DmaGeom<T>::SLOT;

@@ -362,11 +362,11 @@ def test_q4k_lds_ring_shapes(N, K):
     del W
 
 
-# Q4_K at M = 2 with rows of 64 units or more in 1, 2, 4 or 8 stripes runs the
+# Q4_K at M = 2 with rows of 64 units or more in 1 or 2 stripes runs the
 # LDS-ring kernel with both activation rows in registers: a 70B wk + wq group,
-# wo, w1 + w3 with a ragged group, an 8B projection, a 16384-column matrix
-# (4 stripes) and a 3-row matrix; a short-row matrix and a 3-stripe one take
-# the batch-M kernel.  Sampled rows against the oracle and every row bit for
+# wo, w1 + w3 with a ragged group, an 8B projection and a 3-row matrix; a
+# 16384-column matrix (4 stripes: no LDS for the ring beside two staged rows),
+# a short-row matrix and a 3-stripe one take the batch-M kernel.  Sampled rows against the oracle and every row bit for
 # bit against M = 1.
 Q4K_RING_M2 = [([1024, 8192], 8192), ([8192], 8192), ([28672, 28001], 8192), ([4096], 4096), ([2000], 16384),
                ([3], 8192), ([5001], 2048), ([3000], 12288)]
