@@ -50,7 +50,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream", "dequant"])
+    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream", "dequant",
+                                                           "ceiling", "floor", "barrier"])
+    ap.add_argument("--phase-mb", type=float, default=136.0,
+                    help="barrier: weight MB per phase (136 = a 70B layer's 544 MB over its 4 launches)")
+    ap.add_argument("--phases", type=int, default=320, help="barrier: phases per step")
+    ap.add_argument("--x-kb", type=int, default=32, help="barrier: activation KB staged per phase")
     ap.add_argument("--slots", type=int, default=3, help="stream: device slots in the ring")
     ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
     ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
@@ -152,10 +157,117 @@ def summarize_pmc(args):
     return 0
 
 
+PROBE_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqprobe.so")
+
+
+def probe_lib():
+    import dequant_gemv_gguf_amd  # noqa: F401  (fails loudly without the built libraries)
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError("%s is missing: build it first (python __graft_entry__.py build)" % PROBE_LIB)
+    L = ctypes.CDLL(PROBE_LIB)
+    P, I, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    L.kqp_read_stream.argtypes = [P, U64, I, I, I, I, P, P]
+    L.kqp_empty.argtypes = [I, I, P]
+    L.kqp_phased_stream.argtypes = [P, U64, U64, I, P, I, I, I, P, P, P]
+    return L
+
+
+def run_probe(args):
+    """Ceilings and fixed costs the GEMV kernels are judged against:
+    ceiling  HBM read stream (4 GiB) with the kernels' load forms
+    floor    back-to-back launches of an empty kernel
+    barrier  dependent phases of a weight stream: one launch per phase vs one
+             persistent launch with a grid barrier between phases (with and
+             without issuing the next phase's first loads before the wait)"""
+    import torch
+    P = probe_lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(65535 * 16 * 64, dtype=torch.int32, device=dev)
+
+    def chk(r, what):
+        if r != 0:
+            raise RuntimeError("%s failed with status %d" % (what, r))
+
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
+           "data": "synthetic (uninitialised device memory; only the read rate matters)", "compute_units": cus}
+    if args.workload == "ceiling":
+        nbytes = (1 << 32) - 4096
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        rows = []
+        for (mode, waves, depth) in [(0, 16, 2), (0, 8, 4), (1, 16, 2), (1, 8, 4), (1, 16, 3)]:
+            ms = timed(lambda: chk(P.kqp_read_stream(buf.data_ptr(), nbytes, mode, cus, waves, depth,
+                                                     sink.data_ptr(), sp), "kqp_read_stream"), args.steps)
+            rows.append({"loads": "buffer-to-LDS" if mode else "registers", "waves": waves, "depth": depth,
+                         "us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        best = max(r["GBps"] for r in rows)
+        out.update({"metric": "HBM read-stream ceiling (4 GiB, one persistent work-group per CU)", "value": best,
+                    "unit": "GB/s", "pct_of_hbm_peak": round(100 * best / HBM_PEAK_GBS, 2), "variants": rows,
+                    "config": {"workload": "read 4 GiB once, 3-KB spans, non-temporal", "bytes": nbytes}})
+    elif args.workload == "floor":
+        rows = []
+        for (nwg, threads) in [(1, 64), (cus, 1024), (cus, 512)]:
+            ms = timed(lambda: chk(P.kqp_empty(nwg, threads, sp), "kqp_empty"), 2000)
+            rows.append({"workgroups": nwg, "threads": threads, "us_per_launch": round(ms * 1e3, 3)})
+        out.update({"metric": "back-to-back launch floor of an empty kernel", "value": rows[1]["us_per_launch"],
+                    "unit": "us", "higher_is_better": False, "variants": rows,
+                    "config": {"workload": "2000 launches of an empty kernel on one stream"}})
+    else:  # barrier
+        pbytes = int(args.phase_mb * 1e6) // 3072 * 3072
+        total = pbytes * args.phases
+        buf = torch.empty(total, dtype=torch.uint8, device=dev)
+        x = torch.randn(args.x_kb * 256, device=dev)
+        ctr = torch.zeros(2, dtype=torch.int32, device=dev)
+        rows = []
+        for (pers, pref) in [(0, 0), (1, 0), (1, 1), (1, 2), (1, 3)]:
+            def step(pers=pers, pref=pref):
+                chk(P.kqp_phased_stream(buf.data_ptr(), pbytes, pbytes, args.phases, x.data_ptr(), args.x_kb * 1024,
+                                        pers, pref, ctr.data_ptr(), sink.data_ptr(), sp), "kqp_phased_stream")
+            ms = timed(step, args.steps)
+            rows.append({"launch": "persistent, grid barrier" if pers else "one launch per phase",
+                         "prefetch_next_phase": bool(pref & 1),
+                         "barrier": ("device-scope data, no cache maintenance" if pref & 2 else
+                                     "agent-scope release + acquire per work-group") if pers else None,
+                         "ms_per_step": round(ms, 4),
+                         "GBps": round(total / (ms * 1e-3) / 1e9, 1),
+                         "us_per_phase": round(ms * 1e3 / args.phases, 3)})
+        torch.cuda.synchronize()
+        if int(ctr[1].item()) != 0:
+            raise RuntimeError("a grid-barrier wait gave up (ctr[1] = %d)" % int(ctr[1].item()))
+        best = max(r["GBps"] for r in rows)
+        out.update({"metric": "dependent weight-stream phases: launch per phase vs persistent grid barrier",
+                    "value": best, "unit": "GB/s", "pct_of_hbm_peak": round(100 * best / HBM_PEAK_GBS, 2),
+                    "variants": rows,
+                    "config": {"workload": "%d phases of %.1f MB, %d KB activations staged per phase" % (
+                        args.phases, pbytes / 1e6, args.x_kb), "bytes_per_step": total}})
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.workload in ("ceiling", "floor", "barrier"):
+        if args.gpus != 1:
+            print("bench.py: measurement workloads run on one GPU", file=sys.stderr)
+            return 2
+        return run_probe(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on exactly one GPU (no collectives, no sharding); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)

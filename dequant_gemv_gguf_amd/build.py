@@ -25,6 +25,8 @@ CSRC = os.path.join(HERE, "csrc")
 INC = os.path.join(ROOT, "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkqgemv.so")
+# the measurement kernels (include/kqprobe.h), a library of their own
+PROBE_LIB = os.path.join(HERE, "libkqprobe.so")
 ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -43,7 +45,8 @@ PAIRS = ((10, 11), (10, 12), (10, 13), (10, 14), (11, 12), (11, 13), (11, 14),
 
 def units():
     """(object name, source, defines) of every object of the library."""
-    out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", []), ("kq_stream", "kq_stream.cpp", [])]
+    out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", []), ("kq_stream", "kq_stream.cpp", []),
+           ("kq_probe", "kq_probe.hip", [])]
     out += [("kq_type%d" % t, "kq_inst.hip", ["-DKQ_INST_TYPE=%d" % t]) for t in TYPES]
     out += [("kq_mixed%d_%d" % p, "kq_inst.hip", ["-DKQ_INST_A=%d" % p[0], "-DKQ_INST_B=%d" % p[1]])
             for p in PAIRS]
@@ -83,12 +86,14 @@ def build(verbose=False, extra=()):
                 failed.append(cmd)
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
-    tmp = LIB + ".tmp%d" % os.getpid()
-    link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined"] + objs + ["-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    subprocess.check_call(link)
-    os.replace(tmp, LIB)
+    probe = [o for o in objs if o.endswith("kq_probe.o")]
+    for lib, parts in ((LIB, [o for o in objs if o not in probe]), (PROBE_LIB, probe)):
+        tmp = lib + ".tmp%d" % os.getpid()
+        link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined"] + parts + ["-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.check_call(link)
+        os.replace(tmp, lib)
     return LIB
 
 
