@@ -10,7 +10,14 @@ and w3) go through one grouped call -- 320 launches per step, k+q+v as one
 launch with the Q4_K and Q6_K rows side by side (--no-group: one launch per
 matrix).  The metric is packed-weight bytes moved per second
 (algorithmic bytes: every weight byte read once), reported in GB/s, as a
-fraction of the 8 TB/s HBM3E peak and as equivalent tokens/s.
+fraction of the 8 TB/s HBM3E peak and of the read ceiling measured on the
+same GPU, and as equivalent tokens/s.
+
+Before anything is timed, sampled rows of every matrix of the step's last
+layer are checked against the CPU oracle (|dy| <= 1e-4 * sum|w*x| + 1e-6); a
+mismatch ends the run with a non-zero status and no value.  The roofline
+object covers the launch class (wv+wk+wq, wo, w1+w3, w2, ...) that takes the
+most time; every class's rate is reported beside it.
 
 Other workloads (--workload) measure the remaining shapes the same way:
   8b      Llama-3-8B-shaped layers x32
@@ -23,6 +30,11 @@ Other workloads (--workload) measure the remaining shapes the same way:
           (host-to-device link bound; value includes the copies)
   dequant the standalone dequantizer over a 70B layer's matrices to fp32
           (value counts packed bytes read plus fp32 bytes written)
+and the measurement kernels of libkqprobe.so:
+  ceiling HBM read stream of 4 GiB with the GEMV kernels' load forms
+  floor   back-to-back launches of an empty kernel
+  barrier dependent weight-stream phases: a launch per phase vs one
+          persistent launch with grid barriers
 
 Inputs are seeded synthetic data drawn directly in device memory.  Only one
 GPU is supported: the path has no collectives.
@@ -32,6 +44,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -42,7 +55,10 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "achieved weight GB/s (% of 8 TB/s HBM) + equiv tok/s, 70B-layer Q4_K_M GEMV M=1"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqgemv.so")
+PROBE_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqprobe.so")
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+TOL_REL, TOL_ABS = 1e-4, 1e-6
+PROBES = ("ceiling", "floor", "barrier")
 
 
 def parse():
@@ -50,17 +66,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="70b", choices=["70b", "8b", "single", "verify", "moe", "stream", "dequant",
-                                                           "ceiling", "floor", "barrier"])
-    ap.add_argument("--phase-mb", type=float, default=136.0,
-                    help="barrier: weight MB per phase (136 = a 70B layer's 544 MB over its 4 launches)")
-    ap.add_argument("--phases", type=int, default=320, help="barrier: phases per step")
-    ap.add_argument("--x-kb", type=int, default=32, help="barrier: activation KB staged per phase")
+    ap.add_argument("--workload", default="70b",
+                    choices=["70b", "8b", "single", "verify", "moe", "stream", "dequant"] + list(PROBES))
     ap.add_argument("--slots", type=int, default=3, help="stream: device slots in the ring")
     ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
     ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the model's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling and launch-floor measurement")
     ap.add_argument("--no-group", action="store_true",
                     help="one launch per matrix (no grouped calls for matrices sharing an input)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
@@ -70,7 +83,16 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn the counter_collection.csv files of a FETCH_SIZE pass and a "
                          "WRITE_SIZE pass (both run with --copy-calibration) into profiles/traffic_<workload>.json")
-    ap.add_argument("--pmc-command", default="", help="with --summarize-pmc: the command the passes ran")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="no GPU: turn a rocprofv3 kernel_stats.csv into profiles/<--profile-name>.txt")
+    ap.add_argument("--profile-name", default="", help="with --summarize-trace: file name (no extension)")
+    ap.add_argument("--dominant", default="", help="with --summarize-*: the dominant kernel's name (its start)")
+    ap.add_argument("--launch-class", default="", help="with --summarize-pmc: the launch class it serves")
+    ap.add_argument("--pmc-command", default="", help="with --summarize-*: the command the passes ran")
+    ap.add_argument("--phase-mb", type=float, default=136.0,
+                    help="barrier: weight MB per phase (136 = a 70B layer's 544 MB over its 4 launches)")
+    ap.add_argument("--phases", type=int, default=320, help="barrier: phases per step")
+    ap.add_argument("--x-kb", type=int, default=32, help="barrier: activation KB staged per phase")
     return ap.parse_args()
 
 
@@ -97,17 +119,32 @@ def check(status):
 def library_hash():
     """Hash of the built library (its kernels and launch logic): traffic
     counters taken with another build are not reported.  The build is
-    deterministic, so an edit that changes no code keeps the hash."""
+    reproducible (fixed compilation-unit ids), so the same sources give the
+    same hash wherever they are built."""
     h = hashlib.sha256()
     with open(KERNEL_LIB, "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def clocks():
+    """Best-effort GPU clocks from amd-smi (None when unavailable)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = d[0] if isinstance(d, list) else d.get("gpu_data", [d])[0]
+        c = g.get("clock", g)
+        out = {}
+        for key, val in c.items():
+            if isinstance(val, dict) and "clk" in val:
+                v = val["clk"]
+                out[key] = v.get("value", v) if isinstance(v, dict) else v
+        return out or None
+    except Exception:
+        return None
+
+
 CALIB_BYTES = 1 << 30
-# batch-1 launches with a Q4_K pass (the LDS-ring kernel, or the register-ring
-# one for unaligned matrices)
-DOMINANT_KERNELS = ("qgemv1_dma_kernel<12,", "qgemv1_kernel<12,", "qgemv1_mixed_kernel<12,")
 
 
 def pmc_per_dispatch(path, counter):
@@ -124,11 +161,17 @@ def pmc_per_dispatch(path, counter):
     return out
 
 
+def squash(name):
+    return name.replace(" ", "").replace("void", "").replace("kq::", "")
+
+
 def summarize_pmc(args):
     """Traffic of the dominant kernel from a FETCH_SIZE and a WRITE_SIZE pass.
     Each counter is calibrated on the 1 GiB copy the passes ran first: the
     factor is 1 GiB over what the counter read for it."""
-    result = {"kernel": "batch-1 Q4_K launches (M=1)", "library_sha256_16": library_hash(),
+    if not args.dominant or not args.launch_class:
+        raise SystemExit("--summarize-pmc needs --dominant KERNEL_NAME_START and --launch-class CLASS")
+    result = {"kernel": args.dominant, "launch": args.launch_class, "library_sha256_16": library_hash(),
               "workload": args.workload, "command": args.pmc_command}
     per = {}
     for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),
@@ -139,9 +182,9 @@ def summarize_pmc(args):
             raise SystemExit("no copy kernel in %s: run the pass with --copy-calibration" % path)
         ref = max(copies)                              # the 1 GiB copy is the largest one
         factor = CALIB_BYTES / (ref * 1024.0)
-        dom = [v for (n, v) in d.values() if any(k in n.replace(" ", "") for k in DOMINANT_KERNELS)]
+        dom = [v for (n, v) in d.values() if squash(n).startswith(squash(args.dominant))]
         if not dom:
-            raise SystemExit("no dominant-kernel dispatch in %s" % path)
+            raise SystemExit("no dispatch of %s in %s" % (args.dominant, path))
         per[key] = sum(dom) / len(dom) * 1024.0 * factor
         result["%s_kib_copy_1gib" % key] = round(ref, 1)
         result["%s_factor" % key] = round(factor, 4)
@@ -157,7 +200,30 @@ def summarize_pmc(args):
     return 0
 
 
-PROBE_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqprobe.so")
+def summarize_trace(args):
+    """A rocprofv3 kernel_stats.csv as a short text summary in profiles/."""
+    import csv
+    if not args.profile_name:
+        raise SystemExit("--summarize-trace needs --profile-name")
+    with open(args.summarize_trace) as f:
+        rows = list(csv.DictReader(f))
+    lines = ["# rocprofv3 kernel summary", "", "command (from the repository root, one MI355X):",
+             "  " + args.pmc_command, "",
+             "%-80s %7s %11s %10s %10s %6s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
+    for r in rows[:14]:
+        lines.append("%-80s %7s %11.0f %10s %10s %6.2f" % (
+            r["Name"][:80], r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"], float(r["Percentage"])))
+    if args.dominant:
+        dom = [r for r in rows if squash(r["Name"]).startswith(squash(args.dominant))]
+        calls = sum(int(r["Calls"]) for r in dom)
+        total = sum(float(r["TotalDurationNs"]) for r in dom)
+        lines += ["", "dominant kernel %s: %d calls, average %.0f ns" % (args.dominant, calls, total / max(1, calls))]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, args.profile_name + ".txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
 
 
 def probe_lib():
@@ -170,6 +236,42 @@ def probe_lib():
     L.kqp_empty.argtypes = [I, I, P]
     L.kqp_phased_stream.argtypes = [P, U64, U64, I, P, I, I, I, P, P, P]
     return L
+
+
+def timed(torch, stream, fn, reps, warmup):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(max(1, warmup)):
+        fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def chk(r, what):
+    if r != 0:
+        raise RuntimeError("%s failed with status %d" % (what, r))
+
+
+def read_ceiling(torch, stream, P, cus, reps=5):
+    """HBM read ceiling: 4 GiB streamed once through a per-wave LDS ring
+    (8 waves x 4 slots of 3 KB a compute unit, non-temporal), in GB/s."""
+    nbytes = (1 << 32) - 4096
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 16 * 64, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ms = timed(torch, stream, lambda: chk(P.kqp_read_stream(buf.data_ptr(), nbytes, 1, cus, 8, 4, sink.data_ptr(), sp),
+                                          "kqp_read_stream"), reps, 1)
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def launch_floor(torch, stream, P, cus, reps=500):
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    return 1e3 * timed(torch, stream, lambda: chk(P.kqp_empty(cus, 1024, sp), "kqp_empty"), reps, 20)
 
 
 def run_probe(args):
@@ -188,31 +290,17 @@ def run_probe(args):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(65535 * 16 * 64, dtype=torch.int32, device=dev)
 
-    def chk(r, what):
-        if r != 0:
-            raise RuntimeError("%s failed with status %d" % (what, r))
-
-    def timed(fn, reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(max(1, args.warmup)):
-            fn()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
-           "data": "synthetic (uninitialised device memory; only the read rate matters)", "compute_units": cus}
+           "data": "synthetic (uninitialised device memory; only the read rate matters)", "compute_units": cus,
+           "clocks": clocks()}
     if args.workload == "ceiling":
         nbytes = (1 << 32) - 4096
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         rows = []
         for (mode, waves, depth) in [(0, 16, 2), (0, 8, 4), (1, 16, 2), (1, 8, 4), (1, 16, 3)]:
-            ms = timed(lambda: chk(P.kqp_read_stream(buf.data_ptr(), nbytes, mode, cus, waves, depth,
-                                                     sink.data_ptr(), sp), "kqp_read_stream"), args.steps)
+            ms = timed(torch, stream, lambda: chk(P.kqp_read_stream(buf.data_ptr(), nbytes, mode, cus, waves, depth,
+                                                                    sink.data_ptr(), sp), "kqp_read_stream"),
+                       args.steps, args.warmup)
             rows.append({"loads": "buffer-to-LDS" if mode else "registers", "waves": waves, "depth": depth,
                          "us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
         best = max(r["GBps"] for r in rows)
@@ -222,7 +310,7 @@ def run_probe(args):
     elif args.workload == "floor":
         rows = []
         for (nwg, threads) in [(1, 64), (cus, 1024), (cus, 512)]:
-            ms = timed(lambda: chk(P.kqp_empty(nwg, threads, sp), "kqp_empty"), 2000)
+            ms = timed(torch, stream, lambda: chk(P.kqp_empty(nwg, threads, sp), "kqp_empty"), 2000, args.warmup)
             rows.append({"workgroups": nwg, "threads": threads, "us_per_launch": round(ms * 1e3, 3)})
         out.update({"metric": "back-to-back launch floor of an empty kernel", "value": rows[1]["us_per_launch"],
                     "unit": "us", "higher_is_better": False, "variants": rows,
@@ -238,7 +326,7 @@ def run_probe(args):
             def step(pers=pers, pref=pref):
                 chk(P.kqp_phased_stream(buf.data_ptr(), pbytes, pbytes, args.phases, x.data_ptr(), args.x_kb * 1024,
                                         pers, pref, ctr.data_ptr(), sink.data_ptr(), sp), "kqp_phased_stream")
-            ms = timed(step, args.steps)
+            ms = timed(torch, stream, step, args.steps, args.warmup)
             rows.append({"launch": "persistent, grid barrier" if pers else "one launch per phase",
                          "prefetch_next_phase": bool(pref & 1),
                          "barrier": ("device-scope data, no cache maintenance" if pref & 2 else
@@ -259,19 +347,69 @@ def run_probe(args):
     return 0
 
 
+# ---------------------------------------------------------------------------
+# Parity gate: sampled outputs of the timed launches against the oracle
+
+def sample_rows(N, seed, n=14):
+    import numpy as np
+    return np.unique(np.concatenate([[0, N - 1], np.random.default_rng(seed).integers(0, N, n)]))
+
+
+def parity_gate(torch, checks):
+    """Worst |dy| / (1e-4 * sum|w*x| + 1e-6) over sampled outputs of every
+    check (dequant: 0 when bit-exact, inf otherwise) and the outputs checked."""
+    import numpy as np
+    import oracle
+    worst, nrows = 0.0, 0
+    for c in checks:
+        kind = c["kind"]
+        if kind == "gemv":
+            qt, N, K, W, x, y = c["qtype"], c["N"], c["K"], c["W"], c["x"], c["y"]
+            rows = sample_rows(N, N + K)
+            Wr = W[torch.from_numpy(rows).to(W.device)].cpu().numpy()
+            yo, S = oracle.gemv(qt, Wr, len(rows), K, x.cpu().numpy())
+            yg = y[:, torch.from_numpy(rows).to(y.device)].cpu().numpy().astype(np.float64)
+            worst = max(worst, float((np.abs(yg - yo) / (TOL_REL * S + TOL_ABS)).max()))
+            nrows += yg.size
+        elif kind == "dequant":
+            qt, W, out, n = c["qtype"], c["W"], c["out"], c["n"]
+            qk, nb = c["block"]
+            nblk = n // qk
+            pick = sample_rows(nblk, nblk, 30)
+            ok = True
+            Wf = W.view(-1)
+            for b in pick:
+                ref = oracle.dequant(qt, Wf[b * nb:(b + 1) * nb].cpu().numpy(), qk)
+                got = out[b * qk:(b + 1) * qk].cpu().numpy()
+                ok = ok and bool(np.array_equal(got.view(np.uint32), ref.view(np.uint32)))
+            worst = max(worst, 0.0 if ok else float("inf"))
+            nrows += len(pick) * qk
+        else:  # moe: the same sampled rows of every expert
+            qt, E, N, K, W, ids, p, x, xm, y = (c[k] for k in ("qtype", "E", "N", "K", "W", "ids", "p", "x",
+                                                                 "x_mode", "y"))
+            rows = sample_rows(N, N + K, 10)
+            rb = W.shape[1]
+            Wr = W.view(E, N, rb)[:, torch.from_numpy(rows).to(W.device)].contiguous().cpu().numpy()
+            yo, S, _ = oracle.moe(qt, Wr, E, len(rows), K, ids.cpu().numpy(),
+                                  None if p is None else p.cpu().numpy(), x.cpu().numpy(), xm)
+            yg = y[..., torch.from_numpy(rows).to(y.device)].cpu().numpy().astype(np.float64)
+            worst = max(worst, float((np.abs(yg - yo) / (TOL_REL * S + TOL_ABS)).max()))
+            nrows += yg.size
+    return worst, nrows
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         return summarize_pmc(args)
-    if args.workload in ("ceiling", "floor", "barrier"):
-        if args.gpus != 1:
-            print("bench.py: measurement workloads run on one GPU", file=sys.stderr)
-            return 2
-        return run_probe(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on exactly one GPU (no collectives, no sharding); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         return 2
+    if args.workload in PROBES:
+        return run_probe(args)
 
     import numpy as np
     import torch
@@ -285,9 +423,12 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    # ---- build the workload: a list of launches, each a closure + its bytes
-    launches = []          # (fn, weight_bytes, is_dominant)
-    host_sample = []       # (qtype, N, K, device tensor) used for the CPU oracle sample
+    # ---- the workload: launches (closure, weight bytes, class), the checks of
+    # the parity gate (the last layer's matrices: a step leaves their outputs
+    # in place) and the CPU baseline's sample
+    launches = []
+    checks = []
+    host_sample = []
     M = 1
     if args.workload in ("70b", "8b", "verify"):
         spec = kqsynth.LLAMA3_70B if args.workload != "8b" else kqsynth.LLAMA3_8B
@@ -304,8 +445,7 @@ def main():
         ys = {name: torch.empty(M, N, device=dev) for (name, _, N, _) in layer}
         # layer order as a decode step runs it: the three projections of the
         # attention input (any order: v, k, q), o after attention, the two FFN
-        # inputs, the FFN output -- which also keeps every Q4_K matrix
-        # (k, q, o, w1, w3) contiguous for timing the dominant kernel
+        # inputs, the FFN output
         order = {"wv": 0, "wk": 1, "wq": 2, "wo": 3, "w1": 4, "w3": 5, "w2": 6}
         # matrices that read the same activations go through one grouped call
         # (k+q+v, w1+w3); the library runs two formats in one launch
@@ -333,15 +473,18 @@ def main():
                     Ws.append(W)
                     if L == 0:
                         host_sample.append((qt, N, K, W))
+                    if L == layers - 1:
+                        checks.append({"kind": "gemv", "qtype": qt, "N": N, "K": K, "W": W, "x": xs[K],
+                                       "y": ys[name]})
                 qt, K = grp[0][1], grp[0][3]
                 nbytes = sum(N * kq.kq_row_bytes(t, K) for (_, t, N, _) in grp)
-                dominant = any(t == kqsynth.Q4_K for (_, t, _, _) in grp)
+                cls = "+".join(n for (n, _, _, _) in grp)
                 x = xs[K]
                 n_mats += len(grp)
                 if len(grp) == 1:
                     N, y = grp[0][2], ys[grp[0][0]]
                     launches.append(((lambda qt=qt, W=Ws[0], N=N, K=K, x=x, y=y:
-                                      kq.kq_qgemv(qt, W, N, K, x, M, y, stream)), nbytes, dominant))
+                                      kq.kq_qgemv(qt, W, N, K, x, M, y, stream)), nbytes, cls))
                 else:
                     # host arrays marshalled once; the call is the C entry point itself
                     n = len(grp)
@@ -352,7 +495,7 @@ def main():
                     sp = ctypes.c_void_p(stream.cuda_stream)
                     launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=x, Ya=Ya, sp=sp:
                                       check(L_.kq_qgemv_multi(n, Ta, Wa, Na, K, ctypes.c_void_p(x.data_ptr()),
-                                                              M, Ya, sp))), nbytes, dominant))
+                                                              M, Ya, sp))), nbytes, cls))
         workload = {"70b": "llama3-70b decode layer x%d, Q4_K_M mix, M=1" % layers,
                     "8b": "llama3-8b decode layer x%d, Q4_K_M mix, M=1" % layers,
                     "verify": "llama3-70b layer shapes x%d, %s, M=%d" % (layers, args.quant, M)}[args.workload]
@@ -392,6 +535,9 @@ def main():
                         host_sample.append((qt, N, K, W))
                     else:
                         del W
+                    if L == layers - 1:
+                        checks.append({"kind": "gemv", "qtype": qt, "N": N, "K": K,
+                                       "W": Wh.view(N, kq.kq_row_bytes(qt, K)), "x": xs[K], "y": ys[name]})
                     Hs.append(Wh)
                 weights += Hs
                 n, K = len(grp), grp[0][3]
@@ -403,7 +549,7 @@ def main():
                 launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=xs[K], Ya=Ya:
                                   check(L_.kq_stream_qgemv_multi(ctypes.c_void_p(streamer), n, Ta, Wa, Na, K,
                                                                  ctypes.c_void_p(x.data_ptr()), 1, Ya))),
-                                 nbytes, True))
+                                 nbytes, "+".join(t[0] for t in grp)))
         torch.cuda.synchronize()
         workload = "llama3-8b layers x%d streamed from pinned host memory, %d device slots, M=1" % (layers,
                                                                                                    args.slots)
@@ -419,8 +565,9 @@ def main():
         y = torch.empty(1, N, device=dev)
         weights = [kqsynth.device_matrix(qt, N, K, seed=c, device=dev) for c in range(copies)]
         for W in weights:
-            launches.append(((lambda W=W: kq.kq_qgemv(qt, W, N, K, x, 1, y, stream)), nbytes, True))
+            launches.append(((lambda W=W: kq.kq_qgemv(qt, W, N, K, x, 1, y, stream)), nbytes, "q4_k 4096x4096"))
         host_sample.append((qt, N, K, weights[0]))
+        checks.append({"kind": "gemv", "qtype": qt, "N": N, "K": K, "W": weights[-1], "x": x, "y": y})
         workload = "single Q4_K 4096x4096 M=1, rotated over %d copies" % copies
         config = {"workload": workload, "N": N, "K": K, "M": 1, "copies": copies}
     elif args.workload == "dequant":
@@ -436,8 +583,10 @@ def main():
                 W = kqsynth.device_matrix(qt, N, K, seed=1000 * L + i, device=dev)
                 weights.append(W)
                 nbytes = N * kq.kq_row_bytes(qt, K) + 4 * N * K
-                launches.append(((lambda qt=qt, W=W, n=N * K: kq.kq_dequant(qt, W, n, out, stream)), nbytes,
-                                 qt == kqsynth.Q4_K))
+                launches.append(((lambda qt=qt, W=W, n=N * K: kq.kq_dequant(qt, W, n, out, stream)), nbytes, name))
+        qt, N, K = layer[-1][1], layer[-1][2], layer[-1][3]
+        checks.append({"kind": "dequant", "qtype": qt, "W": weights[-1], "out": out, "n": N * K,
+                       "block": kqsynth.BLOCK[qt][:2]})
         workload = "standalone dequant of llama3-70b layer matrices x%d to fp32" % layers
         config = {"workload": workload, "layers": layers, "matrices_per_step": len(launches),
                   "bytes": "packed in + fp32 out"}
@@ -465,6 +614,11 @@ def main():
                 W = kqsynth.device_matrix(qt, EE * N, K, seed=100 * L + len(weights), device=dev)
                 weights.append(W)
                 per_expert = N * kq.kq_row_bytes(qt, K)
+                if L == layers - 1:
+                    y_of = {"gate": yg, "up": yu, "down": yd}[name]
+                    checks.append({"kind": "moe", "qtype": qt, "E": E, "N": N, "K": K, "W": W, "ids": ids,
+                                   "p": p if name == "down" else None, "x": h if name == "down" else x,
+                                   "x_mode": 1 if name == "down" else 0, "y": y_of})
                 if name == "down":
                     fn = (lambda qt=qt, W=W, N=N, K=K, ids=ids, p=p:
                           kq.kq_qmoe_gemv(qt, W, E, N, K, ids, p, T, k, h, 1, yd, ws, None, stream))
@@ -479,9 +633,9 @@ def main():
                         continue
                     fn = (lambda qt=qt, Wg=gate_up[0][0], Wu=gate_up[1][0], N=N, K=K, ids=ids:
                           kq.kq_qmoe_gemv_multi(qt, [Wg, Wu], E, N, K, ids, T, k, x, 0, [yg, yu], None, stream))
-                    launches.append((fn, gate_up[0][1] + gate_up[1][1], True))
+                    launches.append((fn, gate_up[0][1] + gate_up[1][1], "gate+up"))
                     continue
-                launches.append((fn, distinct * per_expert, name != "down"))
+                launches.append((fn, distinct * per_expert, name))
         workload = "qwen3-30b-a3b MoE FFN x%d, top-%d of %d experts, T=%d" % (layers, k, E, T)
         config = {"workload": workload, "layers": layers, "experts": E, "top_k": k, "hidden": H,
                   "expert_ffn": F, "tokens": T, "calls_per_step": len(launches),
@@ -493,25 +647,6 @@ def main():
         for (fn, _, _) in launches:
             fn()
 
-    # The dominant kernel's duration comes from a second pass of the same
-    # steps in which each step issues its dominant launches first, as one
-    # contiguous run between two events, and then the others: an event record
-    # costs the stream a few microseconds, which one bracket per step spreads
-    # over all of the step's dominant launches.
-    if not any(d for (_, _, d) in launches):
-        # no Q4_K launch (an all-Q2_K or all-Q8_0 re-encoding): time them all
-        launches = [(fn, b, True) for (fn, b, _) in launches]
-    dominant_idx = [i for i, (_, _, d) in enumerate(launches) if d]
-    other_idx = [i for i, (_, _, d) in enumerate(launches) if not d]
-
-    def run_step_bracketed(a, b):
-        a.record(stream)
-        for i in dominant_idx:
-            launches[i][0]()
-        b.record(stream)
-        for i in other_idx:
-            launches[i][0]()
-
     log("inputs resident: %.2f GB of packed weights per step, %d launches" % (step_bytes / 1e9, len(launches)))
     if args.copy_calibration:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -519,10 +654,21 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup)):
         run_step()
     torch.cuda.synchronize()
     log("warmup done")
+
+    # ---- parity gate: the outputs the warmup left (the last layer's) against
+    # the oracle, before anything is timed
+    worst, nrows = parity_gate(torch, checks)
+    parity = "pass" if worst <= 1.0 else "fail"
+    log("parity %s: worst |dy|/bound %.3g over %d sampled outputs" % (parity, worst, nrows))
+    if parity != "pass":
+        print(json.dumps({"metric": METRIC if args.workload == "70b" else "achieved weight GB/s (%s)" % args.workload,
+                          "parity": "fail", "max_dy_over_bound": worst, "parity_outputs_checked": nrows,
+                          "config": config}), flush=True)
+        return 3
 
     # ---- timed region: exactly `steps` steps
     # (one event at every step boundary, for the median / p10 / p90 of a step)
@@ -543,25 +689,48 @@ def main():
     def pct(q):
         return step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
 
-    # ---- roofline pass: the same steps, dominant launches bracketed
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), len(dominant_idx))
-             for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for (a, b, _) in pairs:
-        run_step_bracketed(a, b)
-    torch.cuda.synchronize()
-    dom_ms = sum(a.elapsed_time(b) for (a, b, _) in pairs)
-    dom_n = sum(n for (_, _, n) in pairs)
-    dom_bytes_per_launch = (sum(b for (_, b, d) in launches if d) / max(1, sum(1 for (_, _, d) in launches if d)))
-    dom_avg_us = 1e3 * dom_ms / max(1, dom_n)
-    dom_gbs = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9 if dom_n else None
+    # ---- per launch class: the same steps issuing only that class's launches,
+    # back to back between two events (an event between two launches costs the
+    # stream microseconds, so none is recorded inside the run)
+    classes = []
+    for (_, _, c) in launches:
+        if c not in classes:
+            classes.append(c)
+    per_class = []
+    for c in classes:
+        idx = [i for i, (_, _, cc) in enumerate(launches) if cc == c]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            for i in idx:
+                launches[i][0]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        avg_us = 1e3 * a.elapsed_time(b) / (len(idx) * args.steps)
+        nb = sum(launches[i][1] for i in idx) / len(idx)
+        per_class.append({"launch": c, "per_step": len(idx), "bytes_per_launch": int(nb),
+                          "avg_us": round(avg_us, 3), "GBps": round(nb / (avg_us * 1e-6) / 1e9, 1),
+                          "frac": round(nb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    total_cls_us = sum(pc["avg_us"] * pc["per_step"] for pc in per_class)
+    for pc in per_class:
+        pc["share_of_step_time"] = round(pc["avg_us"] * pc["per_step"] / total_cls_us, 3)
+    dom = max(per_class, key=lambda pc: pc["avg_us"] * pc["per_step"])
+
+    # ---- ceilings on the same GPU
+    ceiling = floor_us = None
+    if not args.no_ceiling and args.workload != "stream":
+        P = probe_lib()
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        ceiling = read_ceiling(torch, stream, P, cus)
+        floor_us = launch_floor(torch, stream, P, cus)
 
     traffic = None
     tfile = os.path.join(PROFILES, "traffic_%s.json" % args.workload)
     if os.path.exists(tfile):
         with open(tfile) as f:
             t = json.load(f)
-        if t.get("library_sha256_16") == library_hash():
+        if t.get("library_sha256_16") == library_hash() and t.get("launch") == dom["launch"]:
             traffic = t.get("bytes_per_launch")
 
     out = {
@@ -578,27 +747,36 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded, drawn in device memory)",
         "config": config,
+        "parity": parity,
+        "max_dy_over_bound": round(worst, 4),
+        "parity_outputs_checked": nrows,
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tok_per_s_equiv": round(1e3 / ms_per_step, 2),
         "step_ms_median_p10_p90": [round(pct(0.5), 4), round(pct(0.1), 4), round(pct(0.9), 4)],
         "weight_bytes_per_step": step_bytes,
         "wall_s_timed": round(wall1 - wall0, 3),
         "roofline": {
-            "kernel": (("batch-1 Q4_K launches (M=1: %s)" % ("wk, wq, wo, w1, w3" if args.no_group else
-                                                              "wk+wq beside wv (Q6_K) in one launch, wo, w1+w3"))
-                       if args.workload in ("70b", "8b") else "dominant launches"),
+            "kernel": "%s launch (the launch class with the most step time)" % dom["launch"],
             "bound": "hbm",
-            "achieved": round(dom_gbs, 1) if dom_gbs else None,
+            "achieved": dom["GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dom_gbs / HBM_PEAK_GBS, 4) if dom_gbs else None,
+            "frac": dom["frac"],
             "traffic": traffic,
-            "avg_launch_us": round(dom_avg_us, 3),
-            "algorithmic_bytes_per_launch": int(dom_bytes_per_launch),
-            "launches_timed": dom_n,
-            "timing": "HIP events around each step's dominant launches, issued as one run in a second pass of the same steps",
+            "avg_launch_us": dom["avg_us"],
+            "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
+            "launches_timed": dom["per_step"] * args.steps,
+            "timing": "HIP events around the class's launches of every step, issued back to back in a pass of "
+                      "their own",
         },
+        "launch_classes": per_class,
+        "clocks": clocks(),
     }
+    if ceiling:
+        out["read_ceiling_GBps"] = round(ceiling, 1)
+        out["pct_of_read_ceiling"] = round(100.0 * gbs / ceiling, 2)
+        out["roofline"]["frac_of_read_ceiling"] = round(dom["GBps"] / ceiling, 4)
+        out["launch_floor_us"] = round(floor_us, 3)
     if args.workload == "stream":
         # every weight byte crosses the host link once per step: that link,
         # not HBM, bounds the streamed path
@@ -616,12 +794,12 @@ def main():
         log("timing the CPU oracle on a bounded sample")
         import oracle
         threads = oracle.set_threads(0)
-        done_bytes, t_cpu, passes = 0, 0.0, 0
         hosts = []
         for (qt, N, K, W) in host_sample:
             rb = kq.kq_row_bytes(qt, K)
             xh = np.random.default_rng(0).standard_normal((M, K)).astype(np.float32)
             hosts.append((qt, N, K, rb, W.view(N, rb).cpu().numpy(), xh))
+
         # repeat the layer-0 matrices until the sample holds enough CPU time;
         # all host threads, then one thread on a quarter of that time
         def sample(seconds):

@@ -68,7 +68,10 @@ def build(verbose=False, extra=()):
     for name, src, defs in units():
         o = os.path.join(OBJ, name + ".o")
         objs.append(o)
-        cmds.append([hipcc] + FLAGS + list(extra) + defs + ["-I", INC, "-c", os.path.join(CSRC, src), "-o", o])
+        # a fixed compilation-unit id (clang derives it from the source path
+        # otherwise): the library's bytes do not depend on where it is built
+        cuid = ["-cuid=kq_" + name]
+        cmds.append([hipcc] + FLAGS + cuid + list(extra) + defs + ["-I", INC, "-c", os.path.join(CSRC, src), "-o", o])
 
     def run(cmd):
         if verbose:

@@ -2660,8 +2660,6 @@ int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
-#include "kq_mx.h"
-
 // Batch-1 launch over one or more segments (same format and K): one lane per
 // unit, stripes of 64 units, one work-group per compute unit (persistent).
 template <int T>
@@ -2785,18 +2783,6 @@ int launch_qgemvm_single(const void *W, int64_t row_bytes, int N, int K, const f
 template <int T>
 int launch_qgemv_m(int M, const void *W, int64_t row_bytes, int N, int K, const float *x, float *y,
                    hipStream_t st) {
-    if constexpr (MX_FMT<T>()) {
-        if (mx_rows(K)) {
-            Segs sg = {};
-            sg.W[0] = (const uint8_t *)W;
-            sg.y[0] = y;
-            sg.start[0] = 0;
-            sg.start[1] = (N + MX_G - 1) / MX_G * MX_G;
-            sg.rows[0] = N;
-            sg.n = 1;
-            return launch_mx_m<T, T>(M, Segs{}, sg, K, x, st);
-        }
-    }
     switch (M) {
     case 1: return launch_qgemv1_single<T>(W, row_bytes, N, K, x, y, st);
     case 2: return launch_qgemvm_single<T, 2>(W, row_bytes, N, K, x, y, st);
@@ -2838,15 +2824,6 @@ int launch_group(int M, const std::vector<int> &ids, const void *const *W, const
                  int K, const float *x, float *const *y, hipStream_t st) {
     size_t pos = 0;
     Segs sg;
-    if constexpr (MX_FMT<T>()) {
-        if (mx_rows(K)) {
-            while (next_segs(ids, &pos, W, N, y, MX_G, &sg)) {
-                const int r = launch_mx_m<T, T>(M, Segs{}, sg, K, x, st);
-                if (r) return r;
-            }
-            return KQ_OK;
-        }
-    }
     if (M == 1) {
         B1Cfg c;
         int64_t rows = 0;
@@ -2916,16 +2893,6 @@ template <int T> bool batch1_wide_cfg(int K, B1Cfg *c) {
 template <int TA, int TB>
 int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> &ib, size_t *pb,
                  const void *const *W, const int64_t *N, int K, const float *x, float *const *y, hipStream_t st) {
-    if (mx_rows(K) && (MX_FMT<TA>() || MX_FMT<TB>())) {
-        // rows on the matrix-core path keep its bits: pair them only with each other
-        if constexpr (MX_FMT<TA>() && MX_FMT<TB>()) {
-            Segs sa, sb;
-            next_segs(ia, pa, W, N, y, MX_G, &sa);
-            next_segs(ib, pb, W, N, y, MX_G, &sb);
-            return launch_mx<TA, TB, 1>(sa, sb, K, x, st);
-        }
-        return KQ_ERR_ARG;
-    }
     B1Cfg ca, cb;
     if (!batch1_wide_cfg<TA>(K, &ca) || !batch1_wide_cfg<TB>(K, &cb) || ca.lpr != cb.lpr || ca.ns != cb.ns ||
         ca.rs != cb.rs)

@@ -623,9 +623,7 @@ def test_qmoe_slot_major_path_bits():
     # activation rows too large for the token-major kernel (k = 4 rows of
     # K = 8192 per token): the slot-major kernel serves the call, alone and
     # grouped, and every slot still equals a batch-1 product bit for bit
-    # (Q2_K: a format whose dense rows of any length share the routed
-    # kernels' arithmetic)
-    qtype, E, N, K, T, k = kqsynth.Q2_K, 12, 96, 8192, 2, 4
+    qtype, E, N, K, T, k = kqsynth.Q4_K, 12, 96, 8192, 2, 4
     say("qmoe slot-major", E, N, K, T, k)
     Ws = [moe_inputs(qtype, E, N, K, T, k, 30 + i, 1)[0] for i in range(2)]
     _, ids, p, x = moe_inputs(qtype, E, N, K, T, k, 30, 1)
@@ -711,10 +709,9 @@ def test_maximum_K(qtype, M):
     assert e.value.status == -2
 
 
-def test_qmoe_long_rows_on_the_matrix_core_formats():
-    # Q4_K / Q6_K experts with rows of 4096 columns or more: dense calls on
-    # such rows run on the matrix cores, the routed kernels on the vector
-    # ALU; each is checked against the oracle, slot by slot
+def test_qmoe_long_expert_rows():
+    # Q4_K / Q6_K experts with rows of 4096 columns or more (the routed
+    # kernels' longer K chunks), against the oracle slot by slot
     for qtype, E, N, K, T, k, x_mode in [(kqsynth.Q4_K, 12, 96, 8192, 2, 4, 1), (kqsynth.Q6_K, 6, 40, 4096, 3, 2, 0)]:
         W, ids, p, x = moe_inputs(qtype, E, N, K, T, k, 31, x_mode)
         y, flag = gpu_moe(qtype, W, E, N, K, ids, None, x, x_mode)
