@@ -2888,6 +2888,14 @@ template <int T> bool batch1_wide_cfg(int K, B1Cfg *c) {
     return K / 16 <= 2 * 64 * c->ns * c->rs;
 }
 
+// Ring depth of a side (format T, the other side's format O) of the 16-wave
+// mixed kernel with the register ring and the lane count set at run time:
+// beside a large-unit format's ring Q4_K keeps one step in flight there (two
+// spilled 4-5 registers).
+template <int T, int O> constexpr int MIXED_WIDE_RT_D() {
+    return (T == T_Q4_K && BIG_UNIT<O>()) ? 1 : PREFETCH<T, true>();
+}
+
 // Two K-quant formats (type ids TA < TB) with the same K in one launch: up to
 // MAX_SEGS matrices of each; returns how many of each it served.
 template <int TA, int TB>
@@ -2947,7 +2955,8 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     auto kern = narrow ? (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 64>
                               : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 0>)
                        : (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false, 64>
-                              : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false, 0>);
+                              : qgemv1_mixed_kernel<TA, MIXED_WIDE_RT_D<TA, TB>(), TB, MIXED_WIDE_RT_D<TB, TA>(),
+                                                    1024, false, 0>);
     if constexpr (TA == T_Q4_K || TB == T_Q4_K) {
         // the Q4_K side through the LDS ring
         B1Cfg cq = ca;
