@@ -4,6 +4,8 @@
 // launchers are in kq_impl.h.
 #include "kq_impl.h"
 
+#include <cstring>
+
 #define KQ_VERSION 10000
 
 namespace kq {
@@ -36,6 +38,22 @@ int launch_mixed_t(int ta, int tb, const std::vector<int> &ia, size_t *pa, const
     KQ_PAIR(Q4_K, Q5_K) KQ_PAIR(Q4_K, Q6_K) KQ_PAIR(Q5_K, Q6_K)
 #undef KQ_PAIR
     return KQ_ERR_ARG;
+}
+
+// Whether the current device is a gfx950 (the only target the kernels are
+// built for), looked up once per device.
+constexpr int CHECKED_DEVICES = 64;
+static std::atomic<int> device_state[CHECKED_DEVICES];   // 0 unknown, 1 gfx950, 2 other
+static int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= CHECKED_DEVICES) return KQ_ERR_DEVICE;
+    int st = device_state[dev].load(std::memory_order_acquire);
+    if (!st) {
+        hipDeviceProp_t prop;
+        st = (hipGetDeviceProperties(&prop, dev) == hipSuccess && strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        device_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? KQ_OK : KQ_ERR_DEVICE;
 }
 
 } // namespace kq
@@ -89,6 +107,7 @@ int kq_dequant(int type, const void *src, int64_t n_elems, float *dst, void *str
     if (n_elems == 0) return KQ_OK;
     if (!src || !dst) return KQ_ERR_NULL;
     if (!aligned(src, 16) || !aligned(dst, 16)) return KQ_ERR_ALIGN;
+    if (device_check()) return KQ_ERR_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     return with_type(type, [&](auto tag) { return launch_dequant_t<decltype(tag)::value>(src, n_elems, dst, st); });
 }
@@ -112,6 +131,7 @@ int kq_qgemv(int type, const void *W, int64_t N, int64_t K, const float *x, int 
     if (N == 0) return KQ_OK;
     if (!W || !x || !y) return KQ_ERR_NULL;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return KQ_ERR_ALIGN;
+    if (device_check()) return KQ_ERR_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     return with_type(type, [&](auto tag) {
         return launch_qgemv_m<decltype(tag)::value>(M, W, row_bytes, (int)N, (int)K, x, y, st);
@@ -161,6 +181,7 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W, const int6
     bool any = false;
     for (int t = 0; t < NT; ++t) any = any || !by[t].empty();
     if (!any) return KQ_OK;
+    if (device_check()) return KQ_ERR_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     size_t pos[NT] = {};
     if (M == 1) {
@@ -208,6 +229,7 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, 
     if (!aligned(W_exps, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) ||
         (route_w && (!aligned(route_w, 4) || !aligned(workspace, 16))) || (err_flag && !aligned(err_flag, 4)))
         return KQ_ERR_ALIGN;
+    if (device_check()) return KQ_ERR_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     MoeSet set = {};
     set.W[0] = (const uint8_t *)W_exps;
@@ -257,6 +279,7 @@ int kq_qmoe_gemv_multi(int count, int type, const void *const *W_exps, int64_t E
     }
     set.n = count;
     if (!aligned(x, 16) || !aligned(ids, 4) || (err_flag && !aligned(err_flag, 4))) return KQ_ERR_ALIGN;
+    if (device_check()) return KQ_ERR_DEVICE;
     return with_type(type, [&](auto tag) {
         constexpr int TT = decltype(tag)::value;
         const int rt = launch_qmoe_tok_t<TT>(set, row_bytes, (int)E, (int)N, (int)K, ids, nullptr, T, k, x, x_mode,

@@ -35,8 +35,9 @@
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *    Every call is asynchronous on that stream.
  *  - Argument errors are returned synchronously as a negative kq_status before
- *    any HIP call is made.  A failed launch returns KQ_ERR_LAUNCH.  Faults in
- *    a kernel surface at the caller's next synchronisation.
+ *    any HIP call is made.  A call that would launch on a device other than a
+ *    gfx950 returns KQ_ERR_DEVICE.  A failed launch returns KQ_ERR_LAUNCH.
+ *    Faults in a kernel surface at the caller's next synchronisation.
  *  - The library holds no per-call state (only caches of each device's compute
  *    unit count and of the LDS limits granted to its kernels); calls are
  *    reentrant and thread-safe.
@@ -76,7 +77,8 @@ typedef enum kq_status {
     KQ_ERR_ALIGN = -5,    /* a pointer violates its alignment requirement   */
     KQ_ERR_ARG = -6,      /* any other invalid argument (x_mode, k, E)      */
     KQ_ERR_LAUNCH = -7,   /* the HIP launch itself failed                   */
-    KQ_ERR_DEVICE = -8,   /* no usable gfx950 device                        */
+    KQ_ERR_DEVICE = -8,   /* the current device is not a gfx950 (checked once
+                             per device by the first call that would launch) */
     KQ_ERR_IO = -9,       /* a file could not be opened or mapped (kqgguf.h) */
     KQ_ERR_FORMAT = -10   /* a malformed or unsupported file (kqgguf.h)     */
 } kq_status;
@@ -96,13 +98,21 @@ int kq_block_info(int type, int *block_elems, int *block_bytes);
 int64_t kq_row_bytes(int type, int64_t K);
 
 /* Standalone dequantization: dst[i] = fp32 weight i of the packed blocks at
- * src, for i in [0, n_elems).  n_elems must be a multiple of the block size
- * (0 is allowed and launches nothing).  Every value is the correctly rounded
- * fp32 of the exact weight (the products are exact, one rounding at the final
+ * src, for i in [0, n_elems).  This is the expansion the fused GEMV below
+ * does only in registers (Kortex article, section Key components, item 3),
+ * written out to memory: for checking the formats and for callers that need
+ * dense weights.  n_elems must be a multiple of the block size (0 is allowed
+ * and launches nothing).  Every value is the correctly rounded fp32 of the
+ * exact weight (the products are exact, one rounding at the final
  * subtraction); an exact zero is written as +0.  src: n_elems/QK blocks. */
 int kq_dequant(int type, const void *src, int64_t n_elems, float *dst, void *stream);
 
-/* Fused dequant-GEMV: y[m][o] = sum_i w[o][i] * x[m][i] for m < M, o < N.
+/* Fused dequant-GEMV: y[m][o] = sum_i w[o][i] * x[m][i] for m < M, o < N --
+ * the decode-time matrix-vector product over quantized weights that the
+ * Kortex summary ("Out-of-core LLM inference engine written from scratch in
+ * Rust", section Approach) runs in fused dequant-matmul kernels; M > 1 rows
+ * are the several positions one speculative-verify pass runs through the
+ * weights (same section).
  *   W  N x K matrix of `type` blocks (row-major, K fastest), 16-B aligned.
  *   x  M rows of K fp32, contiguous (row stride K).
  *   y  M rows of N fp32, contiguous (row stride N), overwritten.
@@ -143,7 +153,9 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W,
  * routing-weighted combine is requested (T*k*N*4); 0 on invalid sizes. */
 size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N);
 
-/* Routed-expert GEMV over a stacked expert tensor.
+/* Routed-expert GEMV over a stacked expert tensor: only the experts each
+ * token selected are read (the RunNburn post: only a token's chosen experts
+ * are fetched, and the router's choices are not altered).
  *   W_exps  E matrices of N x K `type` blocks, expert-major, 16-B aligned.
  *   ids     [T][k] int32 expert ids (device memory; never read by the host).
  *   x       x_mode 0: [T][K] fp32, one activation row per token, shared by
@@ -175,6 +187,7 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,
                  const int32_t *ids, const float *route_w, int T, int k,
                  const float *x, int x_mode, float *y, float *workspace,
                  int32_t *err_flag, void *stream);
+
 
 /* Grouped routed-expert GEMV: `count` (1..4) stacked expert tensors of one
  * format and shape that share the routing and the activations -- an MoE
