@@ -38,6 +38,7 @@ from ._binding import (  # noqa: F401
     kq_qgemv_multi,
     kq_qmoe_gemv,
     kq_qmoe_gemv_multi,
+    kq_qmoe_gemv_noalloc,
     kq_qmoe_workspace_bytes,
     kq_row_bytes,
     kq_stream_qgemv,

@@ -52,6 +52,7 @@ def lib():
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
         L.kq_qmoe_gemv_multi.argtypes = [I, I, P, I64, I64, I64, P, I, I, P, I, P, P, P]
+        L.kq_qmoe_gemv_noalloc.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P]
         U64, CP = ctypes.c_uint64, ctypes.c_char_p
         L.kq_gguf_open.argtypes = [CP, ctypes.POINTER(P)]
         L.kq_gguf_close.argtypes = [P]
@@ -171,6 +172,13 @@ def kq_qmoe_gemv(qtype, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, works
     _check("kq_qmoe_gemv", lib().kq_qmoe_gemv(int(qtype), _ptr(W_exps), int(E), int(N), int(K), _ptr(ids),
                                               _ptr(route_w), int(T), int(k), _ptr(x), int(x_mode), _ptr(y),
                                               _ptr(workspace), _ptr(err_flag), _stream(stream, y)))
+
+
+def kq_qmoe_gemv_noalloc(qtype, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, err_flag=None, stream=None):
+    _check("kq_qmoe_gemv_noalloc", lib().kq_qmoe_gemv_noalloc(int(qtype), _ptr(W_exps), int(E), int(N), int(K),
+                                                              _ptr(ids), _ptr(route_w), int(T), int(k), _ptr(x),
+                                                              int(x_mode), _ptr(y), _ptr(err_flag),
+                                                              _stream(stream, y)))
 
 
 def kq_qmoe_gemv_multi(qtype, W_exps, E, N, K, ids, T, k, x, x_mode, ys, err_flag=None, stream=None):

@@ -56,6 +56,40 @@ static int device_check() {
     return st == 1 ? KQ_OK : KQ_ERR_DEVICE;
 }
 
+// Scratch of kq_qmoe_gemv_noalloc: the per-slot results of a routing-weighted
+// sum served by the slot-major kernel, in a static device array instead of
+// caller memory.  The array's name is a host-side stand-in: host code uses
+// only the address hipGetSymbolAddress returns for the current device (each
+// device holds its own copy), looked up once per device on the first call.
+static __device__ __align__(256) float scratch[KQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int SCRATCH_DEVICES = 64;
+inline std::mutex &scratch_mutex() {
+    static std::mutex mu;
+    return mu;
+}
+static std::atomic<float *> scratch_addr[SCRATCH_DEVICES];
+
+// The scratch array's address on the current device (KQ_ERR_DEVICE when it
+// cannot be resolved).
+static int scratch_of_device(float **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return KQ_ERR_DEVICE;
+    float *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mutex());
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *a = nullptr;
+            if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return KQ_ERR_DEVICE;
+            p = static_cast<float *>(a);
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return KQ_OK;
+}
+
 } // namespace kq
 
 using namespace kq;
@@ -215,22 +249,35 @@ size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N) {
     return (size_t)T * (size_t)k * (size_t)N * sizeof(float);
 }
 
-int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, const int32_t *ids,
-                 const float *route_w, int T, int k, const float *x, int x_mode, float *y, float *workspace,
-                 int32_t *err_flag, void *stream) {
-    int64_t row_bytes;
-    int r = check_gemv_shape(type, N, K, &row_bytes);
+// Argument checks of kq_qmoe_gemv (need_ws: a workspace is required when
+// route_w is given), in their order; KQ_OK with *row_bytes set, or N == 0
+// reported through *empty.
+static int qmoe_check(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, const int32_t *ids,
+                      const float *route_w, int T, int k, const float *x, int x_mode, const float *y,
+                      const float *workspace, bool need_ws, const int32_t *err_flag, int64_t *row_bytes, bool *empty) {
+    int r = check_gemv_shape(type, N, K, row_bytes);
     if (r) return r;
     if (T < 1 || T > 8) return KQ_ERR_M;
     if (E < 1 || E >= ((int64_t)1 << 31) || k < 1 || k > 16 || k > E || (x_mode != 0 && x_mode != 1))
         return KQ_ERR_ARG;
+    *empty = N == 0;
     if (N == 0) return KQ_OK;
-    if (!W_exps || !ids || !x || !y || (route_w && !workspace)) return KQ_ERR_NULL;
+    if (!W_exps || !ids || !x || !y || (need_ws && route_w && !workspace)) return KQ_ERR_NULL;
     if (!aligned(W_exps, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) ||
-        (route_w && (!aligned(route_w, 4) || !aligned(workspace, 16))) || (err_flag && !aligned(err_flag, 4)))
+        (route_w && (!aligned(route_w, 4) || (need_ws && !aligned(workspace, 16)))) ||
+        (err_flag && !aligned(err_flag, 4)))
         return KQ_ERR_ALIGN;
+    return KQ_OK;
+}
+
+// The routed-expert product once its arguments are checked: token-major with
+// the sum in the same launch when the activation rows fit, else slot-major
+// through `workspace` and the separate sum.
+static int qmoe_run(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, int64_t row_bytes,
+                    const int32_t *ids, const float *route_w, int T, int k, const float *x, int x_mode, float *y,
+                    float *workspace, int32_t *err_flag, hipStream_t st) {
     if (device_check()) return KQ_ERR_DEVICE;
-    hipStream_t st = (hipStream_t)stream;
+    int r;
     MoeSet set = {};
     set.W[0] = (const uint8_t *)W_exps;
     set.y[0] = y;
@@ -255,6 +302,36 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, 
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + WG_THREADS - 1) / WG_THREADS)), dim3(WG_THREADS),
                        0, st, workspace, route_w, T, k, (int)N, y);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, const int32_t *ids,
+                 const float *route_w, int T, int k, const float *x, int x_mode, float *y, float *workspace,
+                 int32_t *err_flag, void *stream) {
+    int64_t row_bytes;
+    bool empty = false;
+    const int r = qmoe_check(type, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, workspace, true, err_flag,
+                             &row_bytes, &empty);
+    if (r || empty) return r;
+    return qmoe_run(type, W_exps, E, N, K, row_bytes, ids, route_w, T, k, x, x_mode, y, workspace, err_flag,
+                    (hipStream_t)stream);
+}
+
+int kq_qmoe_gemv_noalloc(int type, const void *W_exps, int64_t E, int64_t N, int64_t K, const int32_t *ids,
+                         const float *route_w, int T, int k, const float *x, int x_mode, float *y,
+                         int32_t *err_flag, void *stream) {
+    int64_t row_bytes;
+    bool empty = false;
+    int r = qmoe_check(type, W_exps, E, N, K, ids, route_w, T, k, x, x_mode, y, nullptr, false, err_flag, &row_bytes,
+                       &empty);
+    if (r || empty) return r;
+    float *ws = nullptr;
+    if (route_w) {
+        if (kq_qmoe_workspace_bytes(T, k, N) > KQ_NOALLOC_SCRATCH_BYTES) return KQ_ERR_SHAPE;
+        r = scratch_of_device(&ws);
+        if (r) return r;
+    }
+    return qmoe_run(type, W_exps, E, N, K, row_bytes, ids, route_w, T, k, x, x_mode, y, ws, err_flag,
+                    (hipStream_t)stream);
 }
 
 int kq_qmoe_gemv_multi(int count, int type, const void *const *W_exps, int64_t E, int64_t N, int64_t K,

@@ -188,6 +188,25 @@ int kq_qmoe_gemv(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,
                  const float *x, int x_mode, float *y, float *workspace,
                  int32_t *err_flag, void *stream);
 
+/* Scratch bytes kq_qmoe_gemv_noalloc holds per device (4 MiB). */
+#define KQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* kq_qmoe_gemv without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, results and errors are those
+ * of kq_qmoe_gemv; when a routing-weighted sum needs per-slot scratch it
+ * uses a static device array of KQ_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends (its address is
+ * looked up on the first call on a device: KQ_ERR_DEVICE if that fails).
+ * With route_w non-NULL, T*k*N*4 (kq_qmoe_workspace_bytes) above that size
+ * is refused with KQ_ERR_SHAPE before any HIP call.  The call allocates and
+ * frees nothing.  Every call on a device shares that device's array and
+ * overwrites what it uses before reading it; calls that overlap on one device
+ * (other streams or host threads) race on it and must be serialised by the
+ * caller. */
+int kq_qmoe_gemv_noalloc(int type, const void *W_exps, int64_t E, int64_t N, int64_t K,
+                         const int32_t *ids, const float *route_w, int T, int k,
+                         const float *x, int x_mode, float *y, int32_t *err_flag, void *stream);
 
 /* Grouped routed-expert GEMV: `count` (1..4) stacked expert tensors of one
  * format and shape that share the routing and the activations -- an MoE

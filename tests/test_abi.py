@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
                             "kq_dequant", "kq_qgemv", "kq_qgemv_multi", "kq_qmoe_workspace_bytes",
-                            "kq_qmoe_gemv", "kq_qmoe_gemv_multi",
+                            "kq_qmoe_gemv", "kq_qmoe_gemv_multi", "kq_qmoe_gemv_noalloc",
                             "kq_gguf_open", "kq_gguf_close", "kq_gguf_version", "kq_gguf_alignment",
                             "kq_gguf_tensor_count", "kq_gguf_find_tensor", "kq_gguf_tensor_info",
                             "kq_gguf_upload", "kq_gguf_meta_count", "kq_gguf_meta_key", "kq_gguf_meta_int",
@@ -186,3 +186,22 @@ def test_qmoe_multi_argument_errors():
     assert call(2, W=(ctypes.c_void_p * 2)(FAKE, ODD)) == -5
     assert call(2, x=ctypes.c_void_p(ODD)) == -5
     assert call(2, N=0) == 0                                     # nothing to do: no launch
+
+
+def test_qmoe_noalloc_argument_errors():
+    # the same checks as kq_qmoe_gemv without the workspace, and the scratch
+    # limit (T * k * N * 4 bytes with routing weights) refused before any HIP
+    # call
+    def m(qtype=Q4, W=FAKE, E=8, N=16, K=256, ids=FAKE, rw=None, T=1, k=2, x=FAKE, xm=0, y=FAKE, flag=None):
+        return _status(kq.kq_qmoe_gemv_noalloc, qtype, W, E, N, K, ids, rw, T, k, x, xm, y, flag)
+    assert m(qtype=5) == -1
+    assert m(K=300) == -2
+    assert m(T=0) == -3 and m(T=9) == -3
+    assert m(k=17) == -6 and m(xm=2) == -6
+    assert m(W=None) == -4 and m(ids=None) == -4 and m(x=None) == -4 and m(y=None) == -4
+    assert m(W=ODD) == -5 and m(rw=FAKE + 2) == -5 and m(flag=FAKE + 1) == -5
+    assert m(N=0, W=None, ids=None, x=None, y=None) == 0
+    limit = 4 << 20
+    N = limit // (8 * 16 * 4)
+    assert N * 8 * 16 * 4 == limit
+    assert m(E=16, N=N + 1, T=8, k=16, rw=FAKE) == -2           # one row past the scratch
