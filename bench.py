@@ -269,6 +269,31 @@ def read_ceiling(torch, stream, P, cus, reps=5):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def stream_twins(torch, stream, P, cus, sizes, xbytes=32 * 1024, reps=4):
+    """For each launch size: microseconds of one launch of the plain read
+    stream (kqp_phased_stream, one launch per phase: 16 waves x 2 slots of
+    3 KB a compute unit, buffer-to-LDS, after staging xbytes of activations)
+    moving the same bytes -- what one launch of that size can reach on this
+    GPU with no arithmetic.  Launches rotate over 4 GiB, so no phase finds
+    its bytes in a cache."""
+    nbytes = 1 << 32
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 16 * 64, dtype=torch.int32, device="cuda")
+    x = torch.randn(xbytes // 4, device="cuda")
+    ctr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = []
+    for size in sizes:
+        pbytes = max(3072, int(size) // 3072 * 3072)
+        nph = max(1, min(320, nbytes // pbytes))
+        ms = timed(torch, stream, lambda: chk(P.kqp_phased_stream(buf.data_ptr(), pbytes, pbytes, nph, x.data_ptr(),
+                                                                  xbytes, 0, 0, ctr.data_ptr(), sink.data_ptr(), sp),
+                                              "kqp_phased_stream"), reps, 1)
+        out.append(1e3 * ms / nph * size / pbytes)
+    del buf
+    return out
+
+
 def launch_floor(torch, stream, P, cus, reps=500):
     sp = ctypes.c_void_p(stream.cuda_stream)
     return 1e3 * timed(torch, stream, lambda: chk(P.kqp_empty(cus, 1024, sp), "kqp_empty"), reps, 20)
@@ -724,6 +749,11 @@ def main():
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         ceiling = read_ceiling(torch, stream, P, cus)
         floor_us = launch_floor(torch, stream, P, cus)
+        for pc, us in zip(per_class, stream_twins(torch, stream, P, cus, [pc["bytes_per_launch"] for pc in per_class])):
+            pc["stream_twin_us"] = round(us, 3)
+            pc["frac_of_stream_twin"] = round(us / pc["avg_us"], 4)
+            log("class %s: %.2f us a launch, the plain read stream of its bytes %.2f us" % (
+                pc["launch"], pc["avg_us"], us))
 
     traffic = None
     tfile = os.path.join(PROFILES, "traffic_%s.json" % args.workload)
@@ -776,6 +806,9 @@ def main():
         out["read_ceiling_GBps"] = round(ceiling, 1)
         out["pct_of_read_ceiling"] = round(100.0 * gbs / ceiling, 2)
         out["roofline"]["frac_of_read_ceiling"] = round(dom["GBps"] / ceiling, 4)
+        if "stream_twin_us" in dom:
+            out["roofline"]["stream_twin_us"] = dom["stream_twin_us"]
+            out["roofline"]["frac_of_stream_twin"] = dom["frac_of_stream_twin"]
         out["launch_floor_us"] = round(floor_us, 3)
     if args.workload == "stream":
         # every weight byte crosses the host link once per step: that link,

@@ -531,6 +531,35 @@ def test_qmoe_slot_rows_do_not_depend_on_grouping():
             assert np.array_equal(y[t, j].view(np.uint32), yg[0].view(np.uint32)), (t, j)
 
 
+@pytest.mark.parametrize("case", [(kqsynth.Q4_K, 128, 768, 2048, 8, 8, 0), (kqsynth.Q6_K, 128, 2048, 768, 8, 8, 1),
+                                  (kqsynth.Q4_K, 20, 200, 1024, 8, 8, 0), (kqsynth.Q2_K, 9, 77, 512, 5, 6, 1)],
+                         ids=["gate-up", "down", "few-experts", "ragged"])
+def test_qmoe_tokens_together_equal_one_token_calls(case):
+    # per-slot outputs of T tokens routed together (experts chosen by several
+    # tokens are read once for all of them) equal, bit for bit, those of each
+    # token routed alone, for one tensor and for two in one launch
+    qtype, E, N, K, T, k, x_mode = case
+    say("qmoe tokens together", kqsynth.TYPE_NAMES[qtype], E, N, K, T, k, x_mode)
+    Ws = [moe_inputs(qtype, E, N, K, T, k, 40 + i, x_mode)[0] for i in range(2)]
+    _, ids, _, x = moe_inputs(qtype, E, N, K, T, k, 40, x_mode)
+    ids[T - 1, :] = ids[0, :]                          # two tokens with the same experts
+    Wd = [dev(W.reshape(-1)) for W in Ws]
+    ys = [torch.full((T, k, N), float("nan"), device="cuda") for _ in range(2)]
+    kq.kq_qmoe_gemv_multi(qtype, Wd, E, N, K, dev(ids), T, k, dev(x), x_mode, ys, None)
+    one, _ = gpu_moe(qtype, Wd[0], E, N, K, ids, None, x, x_mode)
+    torch.cuda.synchronize()
+    rows = x.shape[0] // T
+    for t in range(T):
+        xt = x[t * rows:(t + 1) * rows]
+        for i in range(2):
+            yt, _ = gpu_moe(qtype, Wd[i], E, N, K, ids[t:t + 1], None, xt, x_mode)
+            assert np.array_equal(ys[i].cpu().numpy()[t].view(np.uint32), yt[0].view(np.uint32)), (t, i)
+            if i == 0:
+                assert np.array_equal(one[t].view(np.uint32), yt[0].view(np.uint32)), t
+    yo, S, _ = oracle.moe(qtype, Ws[0], E, N, K, ids, None, x, x_mode)
+    check_close(one, yo, S, "tokens together")
+
+
 def fma_f32(a, b, c):
     """fp32 fused multiply-add, exact: a*b + c rounded once to nearest, ties
     to even (subnormals kept), from exact rational arithmetic."""
