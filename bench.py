@@ -31,7 +31,8 @@ Other workloads (--workload) measure the remaining shapes the same way:
   dequant the standalone dequantizer over a 70B layer's matrices to fp32
           (value counts packed bytes read plus fp32 bytes written)
 and the measurement kernels of libkqprobe.so:
-  ceiling HBM read stream of 4 GiB with the GEMV kernels' load forms
+  ceiling HBM read stream of 4 GiB with the GEMV kernels' load forms,
+          12 to 144 KB in flight per compute unit
   floor   back-to-back launches of an empty kernel
   barrier dependent weight-stream phases: a launch per phase vs one
           persistent launch with grid barriers
@@ -322,11 +323,15 @@ def run_probe(args):
         nbytes = (1 << 32) - 4096
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         rows = []
-        for (mode, waves, depth) in [(0, 16, 2), (0, 8, 4), (1, 16, 2), (1, 8, 4), (1, 16, 3)]:
+        # bytes in flight per compute unit = waves x depth x 3 KB, from 12 KB
+        # to 144 KB, through registers and through LDS
+        for (mode, waves, depth) in [(m, w, d) for m in (1, 0) for (w, d) in
+                                     [(4, 1), (8, 1), (4, 2), (16, 1), (8, 2), (8, 3), (16, 2), (8, 4), (16, 3)]]:
             ms = timed(torch, stream, lambda: chk(P.kqp_read_stream(buf.data_ptr(), nbytes, mode, cus, waves, depth,
                                                                     sink.data_ptr(), sp), "kqp_read_stream"),
                        args.steps, args.warmup)
             rows.append({"loads": "buffer-to-LDS" if mode else "registers", "waves": waves, "depth": depth,
+                         "kb_in_flight_per_cu": waves * depth * 3,
                          "us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
         best = max(r["GBps"] for r in rows)
         out.update({"metric": "HBM read-stream ceiling (4 GiB, one persistent work-group per CU)", "value": best,

@@ -170,3 +170,53 @@ def test_mixed_short_rows_persistent(mats):
         Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
         yo, S = oracle.gemv(t, Wr, len(rows), K, x)
         check_close(got[:, rows], yo, S, "matrix %d" % i)
+
+
+# Batch-1 Q6_K launches of long rows (K >= 20480, the 16-wave configuration
+# with one row step in flight per wave): a wave making more than 64 row steps
+# (parked sums flushed mid-run), one step, a ragged row count, and two
+# matrices in one launch; every row bit for bit against row 0 of an M = 2 call
+# (the batch-M kernel) and sampled rows against the oracle.
+Q6K_LONG = [(33000, 20480), (100, 20480), (1025, 28672)]
+
+
+@pytest.mark.parametrize("N,K", Q6K_LONG, ids=["%dx%d" % c for c in Q6K_LONG])
+def test_q6k_long_rows(N, K):
+    qtype = kqsynth.Q6_K
+    say("q6_k long rows", N, K)
+    W = kqsynth.device_matrix(qtype, N, K, seed=N + 3 * K, device="cuda")
+    x = kqsynth.activations(2, K, kqsynth.rng_for(96, N, K))
+    y1 = torch.full((1, N), float("nan"), device="cuda")
+    y2 = torch.full((2, N), float("nan"), device="cuda")
+    kq.kq_qgemv(qtype, W, N, K, torch.from_numpy(np.ascontiguousarray(x[:1])).cuda(), 1, y1)
+    kq.kq_qgemv(qtype, W, N, K, torch.from_numpy(x).cuda(), 2, y2)
+    torch.cuda.synchronize()
+    got = y1.cpu().numpy()
+    assert np.array_equal(got[0].view(np.uint32), y2.cpu().numpy()[0].view(np.uint32))
+    rows = sample_rows(N, N + K)
+    Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yo, S = oracle.gemv(qtype, Wr, len(rows), K, x[:1])
+    say("  worst |dy|/bound", check_close(got[:, rows], yo, S, "Q6_K %dx%d" % (N, K)))
+
+
+def test_q6k_long_rows_grouped():
+    qtype, K, ns = kqsynth.Q6_K, 28672, [300, 700]
+    say("q6_k long rows, two matrices", ns, K)
+    Ws = [kqsynth.device_matrix(qtype, n, K, seed=97 + i, device="cuda") for i, n in enumerate(ns)]
+    x = kqsynth.activations(1, K, kqsynth.rng_for(97))
+    xd = torch.from_numpy(x).cuda()
+    ys = [torch.full((1, n), float("nan"), device="cuda") for n in ns]
+    kq.kq_qgemv_multi([qtype] * len(ns), Ws, ns, K, xd, 1, ys)
+    sep = []
+    for i, n in enumerate(ns):
+        o = torch.empty((1, n), device="cuda")
+        kq.kq_qgemv(qtype, Ws[i], n, K, xd, 1, o)
+        sep.append(o)
+    torch.cuda.synchronize()
+    for i, n in enumerate(ns):
+        got = ys[i].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), sep[i].cpu().numpy().view(np.uint32)), i
+        rows = sample_rows(n, n + i)
+        Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
+        check_close(got[:, rows], yo, S, "matrix %d" % i)
