@@ -88,6 +88,7 @@ def parse():
                     help="no GPU: turn a rocprofv3 kernel_stats.csv into profiles/<--profile-name>.txt")
     ap.add_argument("--profile-name", default="", help="with --summarize-trace: file name (no extension)")
     ap.add_argument("--dominant", default="", help="with --summarize-*: the dominant kernel's name (its start)")
+    ap.add_argument("--bench-line", help="with --summarize-trace: the JSON line the profiled bench run printed")
     ap.add_argument("--launch-class", default="", help="with --summarize-pmc: the launch class it serves")
     ap.add_argument("--pmc-command", default="", help="with --summarize-*: the command the passes ran")
     ap.add_argument("--phase-mb", type=float, default=136.0,
@@ -173,7 +174,7 @@ def summarize_pmc(args):
     if not args.dominant or not args.launch_class:
         raise SystemExit("--summarize-pmc needs --dominant KERNEL_NAME_START and --launch-class CLASS")
     result = {"kernel": args.dominant, "launch": args.launch_class, "library_sha256_16": library_hash(),
-              "workload": args.workload, "command": args.pmc_command}
+              "workload": args.workload, "m": args.m, "command": args.pmc_command}
     per = {}
     for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),
                                ("write", args.summarize_pmc[1], "WRITE_SIZE")):
@@ -219,6 +220,17 @@ def summarize_trace(args):
         calls = sum(int(r["Calls"]) for r in dom)
         total = sum(float(r["TotalDurationNs"]) for r in dom)
         lines += ["", "dominant kernel %s: %d calls, average %.0f ns" % (args.dominant, calls, total / max(1, calls))]
+    if args.bench_line:
+        # the bench line the profiled run printed: its per-class HIP-event averages
+        with open(args.bench_line) as f:
+            b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+        lines += ["", "bench line of the same run (HIP-event averages per launch class; the profiler "
+                  "lengthens launches a little):"]
+        for c in b.get("launch_classes", []):
+            lines.append("  %-10s %4d a step  %9.3f us  %8.1f GB/s  frac %.4f" % (
+                c["launch"], c["per_step"], c["avg_us"], c["GBps"], c["frac"]))
+        lines.append("  ms_per_step %.4f, value %.1f %s, parity %s" % (b["ms_per_step"], b["value"], b["unit"],
+                                                                       b.get("parity")))
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, args.profile_name + ".txt")
     with open(path, "w") as f:
@@ -765,7 +777,8 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as f:
             t = json.load(f)
-        if t.get("library_sha256_16") == library_hash() and t.get("launch") == dom["launch"]:
+        if (t.get("library_sha256_16") == library_hash() and t.get("launch") == dom["launch"]
+                and t.get("m", 1) == args.m):
             traffic = t.get("bytes_per_launch")
 
     out = {
