@@ -146,6 +146,40 @@ def clocks():
         return None
 
 
+def clocks_under_load(torch, run_step, seconds=2.0):
+    """GPU clocks sampled (amd-smi) while the timed step runs again, untimed,
+    for about `seconds`: the graphics clocks while the kernels stream, not
+    at idle.  None when amd-smi gives nothing."""
+    import threading
+    stop = threading.Event()
+
+    def spin():
+        while not stop.is_set():
+            run_step()
+            torch.cuda.synchronize()
+
+    th = threading.Thread(target=spin, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    time.sleep(0.3)
+    samples = []
+    while time.perf_counter() - t0 < seconds:
+        c = clocks()
+        if c:
+            samples.append(c)
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    keys = sorted({k for c in samples for k in c if k.startswith("gfx") or k.startswith("mem")})
+    out = {}
+    for k in keys:
+        vals = [c[k] for c in samples if isinstance(c.get(k), (int, float))]
+        if vals:
+            out[k] = sorted(vals)[len(vals) // 2]
+    return out or None
+
+
 CALIB_BYTES = 1 << 30
 
 
@@ -330,7 +364,7 @@ def run_probe(args):
 
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
            "data": "synthetic (uninitialised device memory; only the read rate matters)", "compute_units": cus,
-           "clocks": clocks()}
+           "clocks_idle_mhz": clocks()}
     if args.workload == "ceiling":
         nbytes = (1 << 32) - 4096
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -818,7 +852,7 @@ def main():
                       "their own",
         },
         "launch_classes": per_class,
-        "clocks": clocks(),
+        "clocks_under_load_mhz": clocks_under_load(torch, run_step) if args.workload != "stream" else None,
     }
     if ceiling:
         out["read_ceiling_GBps"] = round(ceiling, 1)
