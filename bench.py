@@ -36,6 +36,8 @@ and the measurement kernels of libkqprobe.so:
   floor   back-to-back launches of an empty kernel
   barrier dependent weight-stream phases: a launch per phase vs one
           persistent launch with grid barriers
+  stamps  per-work-group timestamps of the 70B wo and w1+w3 launches (the
+          library's Q4_K LDS-ring kernel with stamps at its phase boundaries)
 
 Inputs are seeded synthetic data drawn directly in device memory.  Only one
 GPU is supported: the path has no collectives.
@@ -59,7 +61,7 @@ KERNEL_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqgemv.so")
 PROBE_LIB = os.path.join(ROOT, "dequant_gemv_gguf_amd", "libkqprobe.so")
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 TOL_REL, TOL_ABS = 1e-4, 1e-6
-PROBES = ("ceiling", "floor", "barrier")
+PROBES = ("ceiling", "floor", "barrier", "stamps")
 
 
 def parse():
@@ -282,7 +284,23 @@ def probe_lib():
     L.kqp_read_stream.argtypes = [P, U64, I, I, I, I, P, P]
     L.kqp_empty.argtypes = [I, I, P]
     L.kqp_phased_stream.argtypes = [P, U64, U64, I, P, I, I, I, P, P, P]
+    L.kqp_stamped_q4k.argtypes = [I, P, P, ctypes.c_int64, P, P, P, I, P, P]
     return L
+
+
+def stamp_stats(st, groups):
+    """Phases of one stamped launch (µs; the stamps count a 100 MHz clock)."""
+    import numpy as np
+    t = st[:groups, :4].astype(np.int64)
+    base = t[:, 0].min()
+    rel = (t - base) * 0.01
+    end = rel[:, 3]
+    xcd = st[:groups, 4].astype(np.int64)
+    per_xcd = {int(x): float(np.median(end[xcd == x])) for x in np.unique(xcd)}
+    return {"span": float(end.max()), "start_spread": float(rel[:, 0].max()),
+            "staging": float(np.median(rel[:, 1] - rel[:, 0])), "to_registers": float(np.median(rel[:, 2] - rel[:, 1])),
+            "weight_stream": float(np.median(rel[:, 3] - rel[:, 2])), "end_median": float(np.median(end)),
+            "end_first": float(end.min()), "xcd_end_median": per_xcd}
 
 
 def timed(torch, stream, fn, reps, warmup):
@@ -352,7 +370,8 @@ def run_probe(args):
     floor    back-to-back launches of an empty kernel
     barrier  dependent phases of a weight stream: one launch per phase vs one
              persistent launch with a grid barrier between phases (with and
-             without issuing the next phase's first loads before the wait)"""
+             without issuing the next phase's first loads before the wait)
+    stamps   per-work-group timestamps of the library's Q4_K LDS-ring launches"""
     import torch
     P = probe_lib()
     dev = torch.device("cuda:0")
@@ -391,6 +410,56 @@ def run_probe(args):
         out.update({"metric": "back-to-back launch floor of an empty kernel", "value": rows[1]["us_per_launch"],
                     "unit": "us", "higher_is_better": False, "variants": rows,
                     "config": {"workload": "2000 launches of an empty kernel on one stream"}})
+    elif args.workload == "stamps":
+        # where a launch's time goes: the library's Q4_K LDS-ring launches of a
+        # 70B layer (wo; w1+w3 in one launch) with per-work-group timestamps
+        import numpy as np
+        import kqsynth
+        rows_out = []
+        for (name, Ns, K) in [("wo", [8192], 8192), ("w1+w3", [28672, 28672], 8192)]:
+            nbytes = sum(Ns) * (K // 256) * 144
+            copies = max(2, (2 << 30) // nbytes + 1)
+            Ws = [[kqsynth.device_matrix(kqsynth.Q4_K, n, K, seed=50 * c + i, device=dev) for i, n in enumerate(Ns)]
+                  for c in range(copies)]
+            x = torch.randn(1, K, device=dev)
+            ys = [torch.empty(1, n, device=dev) for n in Ns]
+            reps = max(4, args.steps)
+            stamps = torch.zeros((reps, 4096, 8), dtype=torch.int64, device=dev)
+            cnt = len(Ns)
+            Na = (ctypes.c_int64 * cnt)(*Ns)
+            Ya = (ctypes.c_void_p * cnt)(*[y.data_ptr() for y in ys])
+            grid = ctypes.c_int(0)
+            xp = ctypes.c_void_p(x.data_ptr())
+            Wa = [(ctypes.c_void_p * cnt)(*[W.data_ptr() for W in Wc]) for Wc in Ws]
+
+            def launch(r, c):
+                chk(P.kqp_stamped_q4k(cnt, Wa[c], Na, K, xp, Ya, ctypes.c_void_p(stamps[r].data_ptr()), 4096,
+                                      ctypes.byref(grid), sp), "kqp_stamped_q4k")
+            for c in range(copies):
+                launch(0, c)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for r in range(reps):
+                launch(r, r % copies)
+            b.record(stream)
+            torch.cuda.synchronize()
+            launch_us = 1e3 * a.elapsed_time(b) / reps
+            st = stamps.cpu().numpy()
+            per = [stamp_stats(st[r], grid.value) for r in range(reps)]
+            med = {k: round(float(np.median([p[k] for p in per])), 3) for k in per[0] if k != "xcd_end_median"}
+            xcds = sorted(per[0]["xcd_end_median"])
+            med["xcd_end_median"] = {str(k): round(float(np.median([p["xcd_end_median"].get(k, 0.0) for p in per])),
+                                                    3) for k in xcds}
+            rows_out.append({"launch": name, "bytes": nbytes, "work_groups": grid.value,
+                             "back_to_back_us": round(launch_us, 3), "phases_us_median_of_launches": med})
+            del Ws
+            torch.cuda.empty_cache()
+        out.update({"metric": "per-work-group timestamps of the Q4_K LDS-ring GEMV launches of a 70B layer",
+                    "value": rows_out[-1]["phases_us_median_of_launches"]["span"], "unit": "us",
+                    "higher_is_better": False, "launches": rows_out,
+                    "config": {"workload": "70B wo 8192x8192 and w1+w3 2x28672x8192 Q4_K, M=1, weights rotated "
+                                           "over > 2 GB"}})
     else:  # barrier
         pbytes = int(args.phase_mb * 1e6) // 3072 * 3072
         total = pbytes * args.phases

@@ -46,7 +46,7 @@ PAIRS = ((10, 11), (10, 12), (10, 13), (10, 14), (11, 12), (11, 13), (11, 14),
 def units():
     """(object name, source, defines) of every object of the library."""
     out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", []), ("kq_stream", "kq_stream.cpp", []),
-           ("kq_probe", "kq_probe.hip", [])]
+           ("kq_probe", "kq_probe.hip", []), ("kq_stamps", "kq_stamps.hip", [])]
     out += [("kq_type%d" % t, "kq_inst.hip", ["-DKQ_INST_TYPE=%d" % t]) for t in TYPES]
     out += [("kq_mixed%d_%d" % p, "kq_inst.hip", ["-DKQ_INST_A=%d" % p[0], "-DKQ_INST_B=%d" % p[1]])
             for p in PAIRS]
@@ -89,7 +89,7 @@ def build(verbose=False, extra=()):
                 failed.append(cmd)
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
-    probe = [o for o in objs if o.endswith("kq_probe.o")]
+    probe = [o for o in objs if o.endswith(("kq_probe.o", "kq_stamps.o"))]
     for lib, parts in ((LIB, [o for o in objs if o not in probe]), (PROBE_LIB, probe)):
         tmp = lib + ".tmp%d" % os.getpid()
         link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined"] + parts + ["-o", tmp]

@@ -40,6 +40,16 @@ def test_header_declares_the_boundary():
                             "kq_stream_qgemv_multi", "kq_stream_qgemv"])
 
 
+def test_probe_library_exports_its_header():
+    probe = os.path.join(os.path.dirname(kq.lib_path), "libkqprobe.so")
+    L = ctypes.CDLL(probe)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kqprobe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kqp_[a-z_0-9]+)\s*\(", text)))
+    assert "kqp_stamped_q4k" in names and "kqp_read_stream" in names
+    for name in names:
+        assert hasattr(L, name), name
+
+
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(kq.lib_path)
     for name in declared_functions():
