@@ -220,3 +220,53 @@ def test_q6k_long_rows_grouped():
         Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
         yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
         check_close(got[:, rows], yo, S, "matrix %d" % i)
+
+
+# Batch-1 Q4_K launches on the LDS ring with many row steps per wave: more
+# than 64 (parked sums flushed mid-run), ragged row counts, the w1+w3 row
+# count as one matrix, rows of one stripe, and two matrices in one launch;
+# every row bit for bit against row 0 of an M = 2 call (another kernel) and
+# sampled rows against the oracle, twice in a row.
+Q4K_LONG = [(140001, 8192), (29000, 8192), (57344, 8192), (20001, 4096)]
+
+
+@pytest.mark.parametrize("N,K", Q4K_LONG, ids=["%dx%d" % c for c in Q4K_LONG])
+def test_q4k_long_launches(N, K):
+    qtype = kqsynth.Q4_K
+    say("q4_k long launch", N, K)
+    W = kqsynth.device_matrix(qtype, N, K, seed=N + 5 * K, device="cuda")
+    x = kqsynth.activations(2, K, kqsynth.rng_for(98, N, K))
+    y2 = torch.full((2, N), float("nan"), device="cuda")
+    kq.kq_qgemv(qtype, W, N, K, torch.from_numpy(x).cuda(), 2, y2)
+    for rep in range(2):
+        y1 = torch.full((1, N), float("nan"), device="cuda")
+        kq.kq_qgemv(qtype, W, N, K, torch.from_numpy(np.ascontiguousarray(x[:1])).cuda(), 1, y1)
+        torch.cuda.synchronize()
+        got = y1.cpu().numpy()
+        assert np.array_equal(got[0].view(np.uint32), y2.cpu().numpy()[0].view(np.uint32)), rep
+    rows = sample_rows(N, N + K)
+    Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yo, S = oracle.gemv(qtype, Wr, len(rows), K, x[:1])
+    say("  worst |dy|/bound", check_close(got[:, rows], yo, S, "Q4_K %dx%d" % (N, K)))
+
+
+def test_q4k_long_launch_grouped():
+    qtype, K, ns = kqsynth.Q4_K, 8192, [28672, 28672 - 77]
+    say("q4_k long launch, two matrices", ns, K)
+    Ws = [kqsynth.device_matrix(qtype, n, K, seed=99 + i, device="cuda") for i, n in enumerate(ns)]
+    x = kqsynth.activations(1, K, kqsynth.rng_for(99))
+    xd = torch.from_numpy(x).cuda()
+    for rep in range(2):
+        ys = [torch.full((1, n), float("nan"), device="cuda") for n in ns]
+        kq.kq_qgemv_multi([qtype] * len(ns), Ws, ns, K, xd, 1, ys)
+        torch.cuda.synchronize()
+        if rep == 0:
+            first = [y.cpu().numpy() for y in ys]
+        else:
+            for a, y in zip(first, ys):
+                assert np.array_equal(a.view(np.uint32), y.cpu().numpy().view(np.uint32))
+    for i, n in enumerate(ns):
+        rows = sample_rows(n, n + i)
+        Wr = Ws[i][torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
+        check_close(first[i][:, rows], yo, S, "matrix %d" % i)
