@@ -36,8 +36,8 @@ and the measurement kernels of libkqprobe.so:
   floor   back-to-back launches of an empty kernel
   barrier dependent weight-stream phases: a launch per phase vs one
           persistent launch with grid barriers
-  stamps  per-work-group timestamps of the 70B wo and w1+w3 launches (the
-          library's Q4_K LDS-ring kernel with stamps at its phase boundaries)
+  stamps  per-work-group timestamps of the 70B wo, w1+w3 and w2 launches (the
+          library's batch-1 kernels with stamps at their phase boundaries)
 
 Inputs are seeded synthetic data drawn directly in device memory.  Only one
 GPU is supported: the path has no collectives.
@@ -284,7 +284,7 @@ def probe_lib():
     L.kqp_read_stream.argtypes = [P, U64, I, I, I, I, P, P]
     L.kqp_empty.argtypes = [I, I, P]
     L.kqp_phased_stream.argtypes = [P, U64, U64, I, P, I, I, I, P, P, P]
-    L.kqp_stamped_q4k.argtypes = [I, P, P, ctypes.c_int64, P, P, P, I, P, P]
+    L.kqp_stamped_qgemv1.argtypes = [I, I, P, P, ctypes.c_int64, P, P, P, I, P, P]
     return L
 
 
@@ -371,7 +371,7 @@ def run_probe(args):
     barrier  dependent phases of a weight stream: one launch per phase vs one
              persistent launch with a grid barrier between phases (with and
              without issuing the next phase's first loads before the wait)
-    stamps   per-work-group timestamps of the library's Q4_K LDS-ring launches"""
+    stamps   per-work-group timestamps of the library's persistent batch-1 launches"""
     import torch
     P = probe_lib()
     dev = torch.device("cuda:0")
@@ -416,10 +416,11 @@ def run_probe(args):
         import numpy as np
         import kqsynth
         rows_out = []
-        for (name, Ns, K) in [("wo", [8192], 8192), ("w1+w3", [28672, 28672], 8192)]:
-            nbytes = sum(Ns) * (K // 256) * 144
+        for (name, qt, Ns, K) in [("wo", kqsynth.Q4_K, [8192], 8192), ("w1+w3", kqsynth.Q4_K, [28672, 28672], 8192),
+                                  ("w2", kqsynth.Q6_K, [8192], 28672)]:
+            nbytes = sum(Ns) * kqsynth.row_bytes(qt, K)
             copies = max(2, (2 << 30) // nbytes + 1)
-            Ws = [[kqsynth.device_matrix(kqsynth.Q4_K, n, K, seed=50 * c + i, device=dev) for i, n in enumerate(Ns)]
+            Ws = [[kqsynth.device_matrix(qt, n, K, seed=50 * c + i, device=dev) for i, n in enumerate(Ns)]
                   for c in range(copies)]
             x = torch.randn(1, K, device=dev)
             ys = [torch.empty(1, n, device=dev) for n in Ns]
@@ -433,8 +434,8 @@ def run_probe(args):
             Wa = [(ctypes.c_void_p * cnt)(*[W.data_ptr() for W in Wc]) for Wc in Ws]
 
             def launch(r, c):
-                chk(P.kqp_stamped_q4k(cnt, Wa[c], Na, K, xp, Ya, ctypes.c_void_p(stamps[r].data_ptr()), 4096,
-                                      ctypes.byref(grid), sp), "kqp_stamped_q4k")
+                chk(P.kqp_stamped_qgemv1(qt, cnt, Wa[c], Na, K, xp, Ya, ctypes.c_void_p(stamps[r].data_ptr()), 4096,
+                                         ctypes.byref(grid), sp), "kqp_stamped_qgemv1")
             for c in range(copies):
                 launch(0, c)
             torch.cuda.synchronize()
@@ -455,11 +456,11 @@ def run_probe(args):
                              "back_to_back_us": round(launch_us, 3), "phases_us_median_of_launches": med})
             del Ws
             torch.cuda.empty_cache()
-        out.update({"metric": "per-work-group timestamps of the Q4_K LDS-ring GEMV launches of a 70B layer",
+        out.update({"metric": "per-work-group timestamps of the persistent batch-1 GEMV launches of a 70B layer",
                     "value": rows_out[-1]["phases_us_median_of_launches"]["span"], "unit": "us",
                     "higher_is_better": False, "launches": rows_out,
-                    "config": {"workload": "70B wo 8192x8192 and w1+w3 2x28672x8192 Q4_K, M=1, weights rotated "
-                                           "over > 2 GB"}})
+                    "config": {"workload": "70B wo 8192x8192 and w1+w3 2x28672x8192 Q4_K, w2 8192x28672 Q6_K, "
+                                           "M=1, weights rotated over > 2 GB"}})
     else:  # barrier
         pbytes = int(args.phase_mb * 1e6) // 3072 * 3072
         total = pbytes * args.phases

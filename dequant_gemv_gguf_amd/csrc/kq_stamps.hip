@@ -1,6 +1,7 @@
 // kq_stamps.hip -- the batch-1 Q4_K pass with its weight ring in LDS (the
 // library's qgemv1_dma_kernel: same templates, same launch shape) with
-// timestamps at its phase boundaries, for kqp_stamped_q4k (include/kqprobe.h).
+// timestamps at its phase boundaries, and the register-ring pass the same way
+// for Q6_K, for kqp_stamped_qgemv1 (include/kqprobe.h).
 // It shows where a launch's time goes: how late each work-group starts, its
 // activation staging, the load of its activations into registers, the weight
 // stream, and how far apart the work-groups and the XCDs finish.
@@ -61,16 +62,50 @@ __global__ __launch_bounds__(LB) void stamped_q4k_kernel(const Segs sg, int64_t 
     }
 }
 
+// The body of qgemv1_kernel<T, D, LB, MS, 64> (the register ring) with the
+// same stamps; its activations go to registers inside the pass, so stamp 2
+// equals stamp 1 and the register load counts to the weight stream.
+template <int T, int D, int LB, bool MS>
+__global__ __launch_bounds__(LB) void stamped_reg_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
+                                                         const float *__restrict__ x, uint64_t *stamps) {
+    const uint64_t t0 = now();
+    extern __shared__ float smem[];
+    float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
+    float *xs = smem + 16 * 64;
+    const int XS = x_stride(K), SS = s_stride(K);
+    float *ss = xs + XS;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    B1Pass<T, D, MS, 64> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
+    stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
+    const uint64_t t1 = now();
+    p.run(xs, ss, XS, SS, part);
+    __syncthreads();
+    const uint64_t t3 = now();
+    if (threadIdx.x == 0) {
+        u32 hw;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        uint64_t *o = stamps + 8 * (size_t)blockIdx.x;
+        o[0] = t0;
+        o[1] = t1;
+        o[2] = t1;
+        o[3] = t3;
+        o[4] = xcc_id();
+        o[5] = hw;
+    }
+}
+
 } // namespace kq_stamped
 
 using namespace kq_stamped;
 
-extern "C" int kqp_stamped_q4k(int count, const void *const *W, const int64_t *N, int64_t K, const float *x,
-                               float *const *y, uint64_t *stamps, int max_groups, int *groups, void *stream) {
+extern "C" int kqp_stamped_qgemv1(int type, int count, const void *const *W, const int64_t *N, int64_t K,
+                                  const float *x, float *const *y, uint64_t *stamps, int max_groups, int *groups,
+                                  void *stream) {
     if (!W || !N || !y || !x || !stamps || !groups) return KQ_ERR_NULL;
-    if (count < 1 || count > MAX_SEGS || max_groups < 1) return KQ_ERR_ARG;
+    if ((type != KQ_TYPE_Q4_K && type != KQ_TYPE_Q6_K) || count < 1 || count > MAX_SEGS || max_groups < 1)
+        return KQ_ERR_ARG;
     if (K < 256 || K % 256 || K > (1 << 20)) return KQ_ERR_SHAPE;
-    const int64_t rb = (K / 256) * 144;
+    const int64_t rb = (K / 256) * (type == KQ_TYPE_Q4_K ? 144 : 210);
     Segs sg = {};
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) {
@@ -86,16 +121,35 @@ extern "C" int kqp_stamped_q4k(int count, const void *const *W, const int64_t *N
     sg.start[count] = (int)rows;
     sg.n = count;
     B1Cfg c;
-    if (!batch1_cfg<T_Q4_K>((int)K, rows, &c) || c.lpr != 64 || !dma_ok<T_Q4_K>(c, sg, rb, (int)K))
-        return KQ_ERR_SHAPE;    // not a shape the library serves with this kernel
+    const bool q4 = type == KQ_TYPE_Q4_K;
+    if (q4 ? (!batch1_cfg<T_Q4_K>((int)K, rows, &c) || c.lpr != 64 || !dma_ok<T_Q4_K>(c, sg, rb, (int)K))
+           : (!batch1_cfg<T_Q6_K>((int)K, rows, &c) || c.lpr != 64))
+        return KQ_ERR_SHAPE;    // not a shape the library serves with these kernels
     const int64_t need = (rows + c.rs - 1) / c.rs;
     const int64_t cap = cu_count();
     const int grid = (int)(need < cap ? need : cap);
     if (grid > max_groups) return KQ_ERR_ARG;
     *groups = grid;
-    const size_t lds = dma_lds<T_Q4_K>(c, (int)K);
+    const size_t lds = q4 ? dma_lds<T_Q4_K>(c, (int)K) : c.lds;
     const int nt = 64 * c.ns * c.rs;
     hipStream_t st = (hipStream_t)stream;
+    if (!q4) {
+#define KQS_REG(WW, MSS)                                                                                     \
+    do {                                                                                                     \
+        auto kern = stamped_reg_kernel<T_Q6_K, PREFETCH<T_Q6_K, WW>(), WW ? 1024 : 512, MSS>;                \
+        if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;                                        \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, sg, rb, (int)K, c.lpr, c.ns, x, stamps);     \
+    } while (0)
+        if (c.wide) {
+            if (count > 1) KQS_REG(true, true);
+            else KQS_REG(true, false);
+        } else {
+            if (count > 1) KQS_REG(false, true);
+            else KQS_REG(false, false);
+        }
+#undef KQS_REG
+        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+    }
 #define KQS_LAUNCH(DD, LBB, MSS)                                                                             \
     do {                                                                                                     \
         auto kern = stamped_q4k_kernel<DD, LBB, MSS>;                                                        \

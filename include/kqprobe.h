@@ -75,19 +75,22 @@ int kqp_mfma4(const void *a, const void *b, const float *c, float *d, void *stre
  * times.  sink: nwg * waves * 64 uint32. */
 int kqp_mfma4_rate(int nwg, int waves, int chains, int iters, uint32_t *sink, void *stream);
 
-/* The batch-1 Q4_K GEMV of `count` matrices sharing x (kq_qgemv_multi at
- * M = 1, K a multiple of 256 with rows of at least 64 units), run by the
- * library's weight-ring-in-LDS kernel in the library's launch shape, with
- * timestamps: for each work-group g < *groups, stamps[8 g + 0..3] are the
- * 100 MHz constant-clock times at which its first wave started, finished
- * staging the activations, held its unit's activations in registers, and (all
- * waves) finished; stamps[8 g + 4] its XCD, stamps[8 g + 5] its hardware id
- * register.  y[i] receives the products (the same bits as kq_qgemv_multi).
- * stamps: max_groups * 8 uint64 of device memory; *groups (host) is set to
- * the grid size.  KQ_ERR_SHAPE for shapes the library does not serve with
- * that kernel; KQ_ERR_ARG when the grid exceeds max_groups. */
-int kqp_stamped_q4k(int count, const void *const *W, const int64_t *N, int64_t K, const float *x,
-                    float *const *y, uint64_t *stamps, int max_groups, int *groups, void *stream);
+/* The batch-1 GEMV of `count` matrices of `type` (KQ_TYPE_Q4_K or
+ * KQ_TYPE_Q6_K) sharing x (kq_qgemv_multi at M = 1, K a multiple of 256 with
+ * rows of at least 64 units), run by the library's persistent batch-1 kernel
+ * for that format (Q4_K: the weight ring in LDS; Q6_K: the register ring) in
+ * the library's launch shape, with timestamps: for each work-group
+ * g < *groups, stamps[8 g + 0..3] are the 100 MHz constant-clock times at
+ * which its first wave started, finished staging the activations, held its
+ * unit's activations in registers (Q6_K: the same as the previous, the load
+ * is part of its pass), and (all waves) finished; stamps[8 g + 4] its XCD,
+ * stamps[8 g + 5] its hardware id register.  y[i] receives the products (the
+ * same bits as kq_qgemv_multi).  stamps: max_groups * 8 uint64 of device
+ * memory; *groups (host) is set to the grid size.  KQ_ERR_SHAPE for shapes the
+ * library does not serve with those kernels; KQ_ERR_ARG for another type or
+ * when the grid exceeds max_groups. */
+int kqp_stamped_qgemv1(int type, int count, const void *const *W, const int64_t *N, int64_t K, const float *x,
+                       float *const *y, uint64_t *stamps, int max_groups, int *groups, void *stream);
 
 #ifdef __cplusplus
 }

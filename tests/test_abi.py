@@ -45,7 +45,7 @@ def test_probe_library_exports_its_header():
     L = ctypes.CDLL(probe)
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kqprobe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(kqp_[a-z_0-9]+)\s*\(", text)))
-    assert "kqp_stamped_q4k" in names and "kqp_read_stream" in names
+    assert "kqp_stamped_qgemv1" in names and "kqp_read_stream" in names
     for name in names:
         assert hasattr(L, name), name
 
