@@ -411,8 +411,9 @@ def run_probe(args):
                     "unit": "us", "higher_is_better": False, "variants": rows,
                     "config": {"workload": "2000 launches of an empty kernel on one stream"}})
     elif args.workload == "stamps":
-        # where a launch's time goes: the library's Q4_K LDS-ring launches of a
-        # 70B layer (wo; w1+w3 in one launch) with per-work-group timestamps
+        # where a launch's time goes: the library's batch-1 launches of a 70B
+        # layer (wo and w1+w3 in one launch: the Q4_K LDS ring; w2: the Q6_K
+        # register ring) with per-work-group timestamps
         import numpy as np
         import kqsynth
         rows_out = []
