@@ -1,0 +1,140 @@
+"""GPU parity over a seeded sweep of shapes.  The launcher chooses among its
+kernels by format, row length, row count, M and grouping; the cases here are
+drawn at random (fixed seed) across those choices: every format, K from one
+block to 32768 columns, N from 1 to ~40000 rows, M from 1 to 8, single and
+grouped launches (one format, or several K-quant formats sharing K).  Each
+output is checked on sampled rows against the CPU oracle
+(|dy| <= 1e-4 * sum|w*x| + 1e-6), each row of an M > 1 call bit for bit
+against the M = 1 call on its activation row, and each matrix of a grouped
+launch bit for bit against its own call."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import kqsynth
+import oracle
+
+torch = pytest.importorskip("torch")
+import dequant_gemv_gguf_amd as kq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [kqsynth.Q4_K, kqsynth.Q6_K, kqsynth.Q2_K, kqsynth.Q8_0, kqsynth.Q4_0, kqsynth.Q5_K, kqsynth.Q3_K]
+KQUANTS = [kqsynth.Q2_K, kqsynth.Q3_K, kqsynth.Q4_K, kqsynth.Q5_K, kqsynth.Q6_K]
+TOL_REL, TOL_ABS = 1e-4, 1e-6
+MAX_WEIGHTS = 1 << 28
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def log_uniform(rng, lo, hi):
+    return int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+
+
+def draw_k(rng, qtype):
+    qk = kqsynth.BLOCK[qtype][0]
+    return qk * log_uniform(rng, 1, 32768 // qk)
+
+
+def draw_n(rng, K, hi=40000):
+    return max(1, min(log_uniform(rng, 1, hi), MAX_WEIGHTS // K))
+
+
+def single_cases(seed=2026, count=96):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        qtype = TYPES[i % len(TYPES)]
+        K = draw_k(rng, qtype)
+        out.append((qtype, draw_n(rng, K), K, int(rng.integers(1, 9)), 1000 + i))
+    return out
+
+
+def grouped_cases(seed=2027, count=32):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        mixed = i % 2 == 1
+        K = draw_k(rng, kqsynth.Q4_K)
+        n = int(rng.integers(2, 6))
+        types = [int(rng.choice(KQUANTS)) for _ in range(n)] if mixed else [TYPES[i % len(TYPES)]] * n
+        if not mixed:
+            K = draw_k(rng, types[0])
+        Ns = [0 if rng.random() < 0.1 else draw_n(rng, K, 30000 // n) for _ in range(n)]
+        M = 1 if mixed and i % 4 == 1 else int(rng.integers(1, 9))
+        out.append((types, Ns, K, M, 2000 + i))
+    return out
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sampled_rows(N, seed, n=24):
+    r = np.random.default_rng(seed).integers(0, N, n)
+    return np.unique(np.concatenate([[0, N - 1], r]))
+
+
+def check_rows(qtype, W, N, K, x, y, seed, what):
+    rows = sampled_rows(N, seed)
+    Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yo, S = oracle.gemv(qtype, Wr, len(rows), K, x)
+    err = np.abs(y[:, rows].astype(np.float64) - yo)
+    bound = TOL_REL * S + TOL_ABS
+    assert np.all(err <= bound), "%s: worst |dy|/bound = %.3g" % (what, float((err / bound).max()))
+
+
+def gemv(qtype, W, N, K, x):
+    y = torch.full((x.shape[0], N), float("nan"), device="cuda")
+    kq.kq_qgemv(qtype, W, N, K, dev(x), x.shape[0], y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", single_cases(),
+                         ids=lambda c: "%s-N%d-K%d-M%d" % (kqsynth.TYPE_NAMES[c[0]], c[1], c[2], c[3]))
+def test_sweep_single(case):
+    qtype, N, K, M, seed = case
+    say("sweep", kqsynth.TYPE_NAMES[qtype], "N", N, "K", K, "M", M)
+    W = kqsynth.device_matrix(qtype, N, K, seed=seed, device="cuda")
+    x = kqsynth.activations(M, K, kqsynth.rng_for(seed, M, K))
+    y = gemv(qtype, W, N, K, x)
+    check_rows(qtype, W, N, K, x, y, seed, "N=%d K=%d M=%d" % (N, K, M))
+    if M > 1:
+        for m in sorted({0, M // 2, M - 1}):
+            one = gemv(qtype, W, N, K, x[m:m + 1])
+            assert np.array_equal(one[0].view(np.uint32), y[m].view(np.uint32)), "row %d of M=%d" % (m, M)
+    del W
+
+
+@pytest.mark.parametrize("case", grouped_cases(),
+                         ids=lambda c: "K%d-M%d-" % (c[2], c[3]) + "+".join(
+                             "%s%d" % (kqsynth.TYPE_NAMES[t], n) for t, n in zip(c[0], c[1])))
+def test_sweep_grouped(case):
+    types, Ns, K, M, seed = case
+    say("sweep grouped", [kqsynth.TYPE_NAMES[t] for t in types], Ns, "K", K, "M", M)
+    Ws = [kqsynth.device_matrix(t, max(n, 1), K, seed=seed + i, device="cuda") for i, (t, n) in enumerate(zip(types, Ns))]
+    x = kqsynth.activations(M, K, kqsynth.rng_for(seed, M, K))
+    ys = [torch.full((M, n), float("nan"), device="cuda") if n else None for n in Ns]
+    kq.kq_qgemv_multi(types, [W if n else None for W, n in zip(Ws, Ns)], Ns, K, dev(x), M, ys)
+    torch.cuda.synchronize()
+    for i, (t, n) in enumerate(zip(types, Ns)):
+        if n == 0:
+            continue
+        got = ys[i].cpu().numpy()
+        one = gemv(t, Ws[i], n, K, x)
+        assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), "matrix %d" % i
+        check_rows(t, Ws[i], n, K, x, got, seed + i, "matrix %d" % i)
+    del Ws
