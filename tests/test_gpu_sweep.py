@@ -6,7 +6,11 @@ grouped launches (one format, or several K-quant formats sharing K).  Each
 output is checked on sampled rows against the CPU oracle
 (|dy| <= 1e-4 * sum|w*x| + 1e-6), each row of an M > 1 call bit for bit
 against the M = 1 call on its activation row, and each matrix of a grouped
-launch bit for bit against its own call."""
+launch bit for bit against its own call.  Routed-expert calls (every format,
+E up to 64, T up to 8, k up to 16, shared or per-slot activations, per-slot
+outputs or their routing-weighted sum) are checked in full against the
+oracle, and per-slot outputs bit for bit against the plain GEMV of the
+slot's expert."""
 import math
 import sys
 
@@ -138,3 +142,53 @@ def test_sweep_grouped(case):
         assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), "matrix %d" % i
         check_rows(t, Ws[i], n, K, x, got, seed + i, "matrix %d" % i)
     del Ws
+
+
+# ---- routed experts ------------------------------------------------------------
+
+def moe_cases(seed=2028, count=32):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        qtype = TYPES[i % len(TYPES)]
+        qk = kqsynth.BLOCK[qtype][0]
+        K = qk * log_uniform(rng, 1, 8192 // qk)
+        E = log_uniform(rng, 1, 64)
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.integers(1, 9))
+        # the oracle computes every output: at most ~5e7 multiply-adds a case
+        N = max(1, min(log_uniform(rng, 1, 3000), int(5e7) // (T * k * K)))
+        out.append((qtype, E, N, K, T, k, i % 2, (i // 2) % 2 == 1, 3000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", moe_cases(),
+                         ids=lambda c: "%s-E%d-N%d-K%d-T%d-k%d-x%d-%s" % (
+                             kqsynth.TYPE_NAMES[c[0]], c[1], c[2], c[3], c[4], c[5], c[6], "sum" if c[7] else "slots"))
+def test_sweep_moe(case):
+    qtype, E, N, K, T, k, x_mode, combine, seed = case
+    say("sweep moe", kqsynth.TYPE_NAMES[qtype], "E", E, "N", N, "K", K, "T", T, "k", k, "x_mode", x_mode, combine)
+    W = kqsynth.blocks(qtype, E * N * (K // kqsynth.BLOCK[qtype][0]), kqsynth.rng_for(seed, 1))
+    ids, p = kqsynth.routing(T, k, E, kqsynth.rng_for(seed, 2))
+    x = kqsynth.activations(T * (k if x_mode else 1), K, kqsynth.rng_for(seed, 3))
+    pw = p if combine else None
+    Wd = dev(W.reshape(-1))
+    y = torch.full((T, N) if combine else (T, k, N), float("nan"), device="cuda")
+    ws = torch.empty(kq.kq_qmoe_workspace_bytes(T, k, N) // 4 + 1, device="cuda") if combine else None
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kq.kq_qmoe_gemv(qtype, Wd, E, N, K, dev(ids), None if pw is None else dev(pw), T, k, dev(x), x_mode, y, ws, flag)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    yo, S, oflag = oracle.moe(qtype, W, E, N, K, ids, pw, x, x_mode)
+    assert int(flag.item()) == 0 and oflag == 0
+    err = np.abs(got.astype(np.float64) - yo)
+    bound = TOL_REL * S + TOL_ABS
+    assert np.all(err <= bound), "worst |dy|/bound = %.3g" % float((err / bound).max())
+    if not combine:
+        # a slot's outputs are the bits of the plain GEMV of its expert on its activation row
+        per = N * kqsynth.row_bytes(qtype, K)
+        for t, j in sorted({(0, 0), (T - 1, k - 1), (T // 2, k // 2)}):
+            e = int(ids[t, j])
+            xr = x[t * k + j if x_mode else t][None, :]
+            one = gemv(qtype, Wd[e * per:(e + 1) * per].clone(), N, K, xr)   # a 16-byte aligned copy
+            assert np.array_equal(one[0].view(np.uint32), got[t, j].view(np.uint32)), (t, j)
