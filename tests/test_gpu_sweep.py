@@ -10,7 +10,8 @@ launch bit for bit against its own call.  Routed-expert calls (every format,
 E up to 64, T up to 8, k up to 16, shared or per-slot activations, per-slot
 outputs or their routing-weighted sum) are checked in full against the
 oracle, and per-slot outputs bit for bit against the plain GEMV of the
-slot's expert."""
+slot's expert.  Standalone dequantization of 1 to 300000 blocks of every
+format is checked bit for bit on every block or on sampled ones."""
 import math
 import sys
 
@@ -192,3 +193,28 @@ def test_sweep_moe(case):
             xr = x[t * k + j if x_mode else t][None, :]
             one = gemv(qtype, Wd[e * per:(e + 1) * per].clone(), N, K, xr)   # a 16-byte aligned copy
             assert np.array_equal(one[0].view(np.uint32), got[t, j].view(np.uint32)), (t, j)
+
+
+# ---- standalone dequantization --------------------------------------------------
+
+def dequant_cases(seed=2029, count=21):
+    rng = np.random.default_rng(seed)
+    return [(TYPES[i % len(TYPES)], log_uniform(rng, 1, 300000), 4000 + i) for i in range(count)]
+
+
+@pytest.mark.parametrize("case", dequant_cases(), ids=lambda c: "%s-%d" % (kqsynth.TYPE_NAMES[c[0]], c[1]))
+def test_sweep_dequant(case):
+    qtype, nblocks, seed = case
+    say("sweep dequant", kqsynth.TYPE_NAMES[qtype], nblocks)
+    qk = kqsynth.BLOCK[qtype][0]
+    W = kqsynth.device_matrix(qtype, nblocks, qk, seed=seed, device="cuda")   # nblocks rows of one block
+    n = nblocks * qk
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    kq.kq_dequant(qtype, W, n, out)
+    torch.cuda.synchronize()
+    # every block of a short run, sampled blocks (first and last included) of a long one
+    picks = np.arange(nblocks) if nblocks <= 4096 else sampled_rows(nblocks, seed, 2000)
+    blk = W[torch.from_numpy(picks).cuda()].cpu().numpy()
+    ref = oracle.dequant(qtype, blk, len(picks) * qk).reshape(len(picks), qk)
+    got = out.view(nblocks, qk)[torch.from_numpy(picks).cuda()].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
