@@ -2158,6 +2158,12 @@ __global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
     const int XS = x_stride(K), SS = s_stride(K);
     const int nx = x_mode ? k : 1;                 // activation rows staged
     float *xs = smem, *ss = smem + nx * XS, *res = ss + nx * SS;
+    // the expert of the wave's first slot, read before the staging so that
+    // its latency overlaps the activations' (a vector load: a scalar one
+    // would be waited for with the kernel arguments, before the staging)
+    const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const u32 e_first = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(ids, (u32)(T_ * k) * 4u),
+                                                             wave0 < k ? (u32)(t * k + wave0) * 4u : OOB, 0, 0);
     {
         const int n16 = K >> 4;
         for (int idx = threadIdx.x; idx < nx * n16; idx += blockDim.x) {
@@ -2180,7 +2186,7 @@ __global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
     for (int j = wave; j < k; j += MOEC_WAVES) {
         // slot j's results: LDS for the sum, else its output row
         float *out = rw ? res + j * RT : y + ((int64_t)t * k + j) * N + row0;
-        const int e = ids[t * k + j];
+        const int e = j == wave ? (int)__builtin_amdgcn_readfirstlane(e_first) : ids[t * k + j];
         if (e < 0 || e >= E) {                     // uniform over the wave
             for (int i = lane; i < nrows; i += 64) out[i] = 0.f;
             if (err_flag && lane == 0) *err_flag = 1;
