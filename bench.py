@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the model's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling and launch-floor measurement")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip sampling the clocks under load (for profiled runs: it repeats the step for ~2 s)")
     ap.add_argument("--no-group", action="store_true",
                     help="one launch per matrix (no grouped calls for matrices sharing an input)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
@@ -923,7 +925,8 @@ def main():
                       "their own",
         },
         "launch_classes": per_class,
-        "clocks_under_load_mhz": clocks_under_load(torch, run_step) if args.workload != "stream" else None,
+        "clocks_under_load_mhz": (clocks_under_load(torch, run_step)
+                                  if args.workload != "stream" and not args.no_clocks else None),
     }
     if ceiling:
         out["read_ceiling_GBps"] = round(ceiling, 1)
