@@ -1489,36 +1489,42 @@ template <int T, int D, bool MS, int LP = 0> struct B1Pass {
     }
 };
 
-// Prologue of the batch-1 kernels: the activation loads (at most two groups
-// of 16 per thread), then `issue` (the first row loads), then the LDS writes
-// of the activations and their 16-sums -- waiting for the activations leaves
-// the row loads in flight.
-template <bool DMA = false, class Issue>
-__device__ __forceinline__ void stage_x1(const float *__restrict__ x, int K, float *smem, float *xs, float *ss,
-                                         Issue issue) {
+// Activation staging of the batch-1 kernels in two halves: x1_load issues the
+// activation loads (at most two groups of 16 per thread) as the kernel's first
+// memory accesses, so that they wait only for the kernel arguments they use;
+// the kernel then sets up its row pass and issues the first row loads, and
+// x1_store writes the activations and their 16-sums to LDS -- waiting for the
+// activations leaves the row loads in flight.
+struct X1 {
+    f4 g[2][4];
+};
+__device__ __forceinline__ X1 x1_load(const float *__restrict__ x, int K) {
     const int nthreads = blockDim.x;
     const int n16 = K >> 4;
-    f4 xg[2][4];
+    X1 r;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int idx = threadIdx.x + it * nthreads;
         const f4 *src = reinterpret_cast<const f4 *>(x + 16 * (idx < n16 ? idx : 0));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xg[it][k] = src[k];
+        for (int k = 0; k < 4; ++k) r.g[it][k] = src[k];
     }
-    __builtin_amdgcn_sched_barrier(0);   // keep every activation load ahead of the row loads
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
+    return r;
+}
+template <bool DMA>
+__device__ __forceinline__ void x1_store(const X1 &r, int K, float *smem, float *xs, float *ss) {
+    const int nthreads = blockDim.x;
+    const int n16 = K >> 4;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        // unconditional, so the loads above are not sunk below the row loads:
+        // unconditional, so the loads are not sunk below the row loads:
         // threads without a group write into the (not yet used) flush area
         const int idx = threadIdx.x + it * nthreads;
         const bool ok = idx < n16;
         f4 *dst = reinterpret_cast<f4 *>(ok ? xs + xpad(16 * idx) : smem);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = xg[it][k];
-        (ok ? ss[idx] : smem[16]) = sum16(xg[it][0], xg[it][1], xg[it][2], xg[it][3]);
+        for (int k = 0; k < 4; ++k) dst[k] = r.g[it][k];
+        (ok ? ss[idx] : smem[16]) = sum16(r.g[it][0], r.g[it][1], r.g[it][2], r.g[it][3]);
     }
     wg_sync<DMA>();
 }
@@ -1536,8 +1542,14 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     // wave index as a scalar: everything derived from it (the row of a step and
     // the buffer descriptor of its loads) stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // the activation loads before the pass is set up: they wait only for the
+    // kernel arguments they use, not for the pass's segment lookups
+    const X1 xr = x1_load(x, K);
+    __builtin_amdgcn_sched_barrier(0);
     B1Pass<T, D, MS, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
-    stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
+    p.issue_first();
+    __builtin_amdgcn_sched_barrier(0);
+    x1_store<false>(xr, K, smem, xs, ss);
     p.run(xs, ss, XS, SS, part);
 }
 
@@ -1725,14 +1737,19 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t r
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
+    // the activation loads before the pass is set up (as in qgemv1_kernel)
+    const X1 xr = x1_load(x, K);
+    __builtin_amdgcn_sched_barrier(0);
     B1Dma<T, D, MS, 1, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
-    stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
+    p.issue_first();
+    __builtin_amdgcn_sched_barrier(0);
+    x1_store<true>(xr, K, smem, xs, ss);
     XReg<T> xa;
     p.x_from_lds(xa, xs, ss, XS, SS);
     p.run(xa, part);
 }
 
-// Prologue of the M-row LDS-ring kernel: stage_x1 for M activation rows (row
+// Prologue of the M-row LDS-ring kernel: x1_load + x1_store for M activation rows (row
 // m at xs + m * (XS + SS), its 16-sums right after it), every activation load
 // ahead of `issue`.
 template <int M, class Issue>
@@ -1791,7 +1808,7 @@ __global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t 
 // format (Q4_K through the LDS ring when DMA is set).
 template <int T, int D, bool DMA, int LP>
 __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int lpr, int ns, int wave, int lane, int wg,
-                                        int nwg, const float *__restrict__ x, float *smem) {
+                                        int nwg, const X1 &xr, float *smem) {
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
     const int XS = x_stride(K), SS = s_stride(K);
@@ -1799,13 +1816,17 @@ __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int l
     if constexpr (DMA && T == T_Q4_K) {
         char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
         B1Dma<T, D, true, 1, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
-        stage_x1<true>(x, K, smem, xs, ss, [&] { p.issue_first(); });
+        p.issue_first();
+        __builtin_amdgcn_sched_barrier(0);
+        x1_store<true>(xr, K, smem, xs, ss);
         XReg<T> xa;
         p.x_from_lds(xa, xs, ss, XS, SS);
         p.run(xa, part);
     } else {
         B1Pass<T, D, true, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
-        stage_x1(x, K, smem, xs, ss, [&] { p.issue_first(); });
+        p.issue_first();
+        __builtin_amdgcn_sched_barrier(0);
+        x1_store<false>(xr, K, smem, xs, ss);
         p.run(xs, ss, XS, SS, part);
     }
 }
@@ -1816,10 +1837,14 @@ __global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t
                                                            const float *__restrict__ x) {
     extern __shared__ float smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // both sides stage the same activations: load them before either side
+    // sets up its pass
+    const X1 xr = x1_load(x, K);
+    __builtin_amdgcn_sched_barrier(0);
     if ((int)blockIdx.x < gb)
-        b1_side<TB, DB, DMA, LP>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, x, smem);
+        b1_side<TB, DB, DMA, LP>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, xr, smem);
     else
-        b1_side<TA, DA, DMA, LP>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, x, smem);
+        b1_side<TA, DA, DMA, LP>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, xr, smem);
 }
 
 // Small grouped launches at M = 1 (the non-persistent counterpart of the
