@@ -1498,8 +1498,7 @@ template <int T, int D, bool MS, int LP = 0> struct B1Pass {
 struct X1 {
     f4 g[2][4];
 };
-__device__ __forceinline__ X1 x1_load(const float *__restrict__ x, int K) {
-    const int nthreads = blockDim.x;
+__device__ __forceinline__ X1 x1_load(const float *__restrict__ x, int K, int nthreads) {
     const int n16 = K >> 4;
     X1 r;
 #pragma unroll
@@ -1512,8 +1511,7 @@ __device__ __forceinline__ X1 x1_load(const float *__restrict__ x, int K) {
     return r;
 }
 template <bool DMA>
-__device__ __forceinline__ void x1_store(const X1 &r, int K, float *smem, float *xs, float *ss) {
-    const int nthreads = blockDim.x;
+__device__ __forceinline__ void x1_store(const X1 &r, int K, int nthreads, float *smem, float *xs, float *ss) {
     const int n16 = K >> 4;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -1532,8 +1530,8 @@ __device__ __forceinline__ void x1_store(const X1 &r, int K, float *smem, float 
 // Batch-1 kernel: one persistent work-group per compute unit, RS row slots of
 // ns stripe waves.  LDS: [16][64] flush area, then the staged activations.
 template <int T, int D, int LB, bool MS, int LP>
-__global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
-                                                    const float *__restrict__ x) {
+__global__ __launch_bounds__(LB) void qgemv1_kernel(const float *__restrict__ x, int K, int nthreads, const Segs sg,
+                                                    int64_t row_bytes, int lpr, int ns) {
     extern __shared__ float smem[];
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
@@ -1544,12 +1542,12 @@ __global__ __launch_bounds__(LB) void qgemv1_kernel(const Segs sg, int64_t row_b
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // the activation loads before the pass is set up: they wait only for the
     // kernel arguments they use, not for the pass's segment lookups
-    const X1 xr = x1_load(x, K);
+    const X1 xr = x1_load(x, K, nthreads);
     __builtin_amdgcn_sched_barrier(0);
     B1Pass<T, D, MS, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
     p.issue_first();
     __builtin_amdgcn_sched_barrier(0);
-    x1_store<false>(xr, K, smem, xs, ss);
+    x1_store<false>(xr, K, nthreads, smem, xs, ss);
     p.run(xs, ss, XS, SS, part);
 }
 
@@ -1728,8 +1726,8 @@ __host__ __device__ constexpr size_t b1_ring_offset(int K, int M = 1) {
 }
 
 template <int T, int D, int LB, bool MS, int LP>
-__global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
-                                                        const float *__restrict__ x) {
+__global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const float *__restrict__ x, int K, int nthreads,
+                                                        const Segs sg, int64_t row_bytes, int lpr, int ns) {
     extern __shared__ float smem[];
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
@@ -1738,12 +1736,12 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const Segs sg, int64_t r
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
     // the activation loads before the pass is set up (as in qgemv1_kernel)
-    const X1 xr = x1_load(x, K);
+    const X1 xr = x1_load(x, K, nthreads);
     __builtin_amdgcn_sched_barrier(0);
     B1Dma<T, D, MS, 1, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
     p.issue_first();
     __builtin_amdgcn_sched_barrier(0);
-    x1_store<true>(xr, K, smem, xs, ss);
+    x1_store<true>(xr, K, nthreads, smem, xs, ss);
     XReg<T> xa;
     p.x_from_lds(xa, xs, ss, XS, SS);
     p.run(xa, part);
@@ -1808,7 +1806,7 @@ __global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t 
 // format (Q4_K through the LDS ring when DMA is set).
 template <int T, int D, bool DMA, int LP>
 __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int lpr, int ns, int wave, int lane, int wg,
-                                        int nwg, const X1 &xr, float *smem) {
+                                        int nwg, const X1 &xr, int nthreads, float *smem) {
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
     const int XS = x_stride(K), SS = s_stride(K);
@@ -1818,7 +1816,7 @@ __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int l
         B1Dma<T, D, true, 1, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg, ring);
         p.issue_first();
         __builtin_amdgcn_sched_barrier(0);
-        x1_store<true>(xr, K, smem, xs, ss);
+        x1_store<true>(xr, K, nthreads, smem, xs, ss);
         XReg<T> xa;
         p.x_from_lds(xa, xs, ss, XS, SS);
         p.run(xa, part);
@@ -1826,25 +1824,25 @@ __device__ __forceinline__ void b1_side(const Segs &sg, int64_t rb, int K, int l
         B1Pass<T, D, true, LP> p(sg, rb, K, lpr, ns, wave, lane, wg, nwg);
         p.issue_first();
         __builtin_amdgcn_sched_barrier(0);
-        x1_store<false>(xr, K, smem, xs, ss);
+        x1_store<false>(xr, K, nthreads, smem, xs, ss);
         p.run(xs, ss, XS, SS, part);
     }
 }
 
 template <int TA, int DA, int TB, int DB, int LB, bool DMA, int LP>
-__global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
-                                                           int gb, int K, int lpr, int ns,
-                                                           const float *__restrict__ x) {
+__global__ __launch_bounds__(LB) void qgemv1_mixed_kernel(const float *__restrict__ x, int K, int nthreads,
+                                                           const Segs sa, int64_t rba, const Segs sb, int64_t rbb,
+                                                           int gb, int lpr, int ns) {
     extern __shared__ float smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // both sides stage the same activations: load them before either side
     // sets up its pass
-    const X1 xr = x1_load(x, K);
+    const X1 xr = x1_load(x, K, nthreads);
     __builtin_amdgcn_sched_barrier(0);
     if ((int)blockIdx.x < gb)
-        b1_side<TB, DB, DMA, LP>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, xr, smem);
+        b1_side<TB, DB, DMA, LP>(sb, rbb, K, lpr, ns, wave, lane, blockIdx.x, gb, xr, nthreads, smem);
     else
-        b1_side<TA, DA, DMA, LP>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, xr, smem);
+        b1_side<TA, DA, DMA, LP>(sa, rba, K, lpr, ns, wave, lane, blockIdx.x - gb, gridDim.x - gb, xr, nthreads, smem);
 }
 
 // Small grouped launches at M = 1 (the non-persistent counterpart of the
@@ -2650,7 +2648,7 @@ int launch_qgemv1_cfg(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     const int64_t need = (slots + c.rs - 1) / c.rs;
     const int64_t cap = cu_count();
     const int grid = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), c.lds, st, sg, row_bytes, K, c.lpr, c.ns, x);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), c.lds, st, x, K, nt, sg, row_bytes, c.lpr, c.ns);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
@@ -2687,7 +2685,7 @@ int launch_qgemv1_dma(const B1Cfg &c, const Segs &sg, int64_t row_bytes, int K, 
     const int64_t need = (slots + c.rs - 1) / c.rs;
     const int64_t cap = cu_count();
     const int grid = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, sg, row_bytes, K, c.lpr, c.ns, x);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, x, K, nt, sg, row_bytes, c.lpr, c.ns);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
@@ -3001,8 +2999,8 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
         }
     }
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ca.ns * ca.rs), lds, st, sa, rba, sb, rbb, (int)gb, K, ca.lpr,
-                       ca.ns, x);
+    const int nt = 64 * ca.ns * ca.rs;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, x, K, nt, sa, rba, sb, rbb, (int)gb, ca.lpr, ca.ns);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 

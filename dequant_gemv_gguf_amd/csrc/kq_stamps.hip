@@ -40,12 +40,12 @@ __global__ __launch_bounds__(LB) void stamped_q4k_kernel(const Segs sg, int64_t 
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K) + (size_t)wave * D * DmaGeom<T>::SLOT;
-    const X1 xr = x1_load(x, K);
+    const X1 xr = x1_load(x, K, (int)blockDim.x);
     __builtin_amdgcn_sched_barrier(0);
     B1Dma<T, D, MS, 1, 64> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
     p.issue_first();
     __builtin_amdgcn_sched_barrier(0);
-    x1_store<true>(xr, K, smem, xs, ss);
+    x1_store<true>(xr, K, (int)blockDim.x, smem, xs, ss);
     const uint64_t t1 = now();
     XReg<T> xa;
     p.x_from_lds(xa, xs, ss, XS, SS);
@@ -79,12 +79,12 @@ __global__ __launch_bounds__(LB) void stamped_reg_kernel(const Segs sg, int64_t 
     const int XS = x_stride(K), SS = s_stride(K);
     float *ss = xs + XS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const X1 xr = x1_load(x, K);
+    const X1 xr = x1_load(x, K, (int)blockDim.x);
     __builtin_amdgcn_sched_barrier(0);
     B1Pass<T, D, MS, 64> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x);
     p.issue_first();
     __builtin_amdgcn_sched_barrier(0);
-    x1_store<false>(xr, K, smem, xs, ss);
+    x1_store<false>(xr, K, (int)blockDim.x, smem, xs, ss);
     const uint64_t t1 = now();
     p.run(xs, ss, XS, SS, part);
     __syncthreads();
