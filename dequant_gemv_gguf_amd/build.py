@@ -31,12 +31,14 @@ ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         # the first four dwords of every kernel's arguments (the batch-1
-         # kernels put the activation pointer, K and the thread count there)
-         # arrive in SGPRs at wave launch, so the activation loads need no
-         # scalar load first; a kernel keeps a prologue that loads them itself
-         # where the firmware does not preload
-         "-mllvm", "-amdgpu-kernarg-preload-count=4",
+         # the first dwords of every kernel's arguments (the batch-1 kernels
+         # put the activation pointer, K and the thread count there, the
+         # routed-expert kernel the activation and expert-id pointers, K, k,
+         # the activation mode and the token count) arrive in SGPRs at wave
+         # launch, so the first loads need no scalar load before them; a
+         # kernel keeps a prologue that loads them itself where the firmware
+         # does not preload
+         "-mllvm", "-amdgpu-kernarg-preload-count=8",
          "-Wall", "-Wno-unused-function"]
 
 # what the host (x86) pass prints for the device-only target feature above

@@ -2167,12 +2167,13 @@ constexpr int MOEC_WAVES = 8;
 constexpr int MOEC_R = 1;          // rows per lane group per step (1: measured best, few VGPRs)
 template <int T>
 __global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
-    const MoeSet set, int64_t row_bytes, int E, int N, int K, int lpr, int RT, const int32_t *__restrict__ ids,
-    const float *__restrict__ rw, int k, const float *__restrict__ x, int x_mode, int32_t *err_flag) {
+    const float *__restrict__ x, const int32_t *__restrict__ ids, int K, int k, int x_mode, int T_, const MoeSet set,
+    int64_t row_bytes, int E, int N, int lpr, int RT, const float *__restrict__ rw, int32_t *err_flag) {
+    // (the arguments the first loads need come first: they are preloaded into
+    // SGPRs, so the expert ids and activations are requested at once)
     typedef Fmt<T> F;
     typedef typename RawOf<T>::type Raw;
     extern __shared__ float smem[];
-    const int T_ = gridDim.y / set.n;
     const int ti = blockIdx.y / T_, t = blockIdx.y - ti * T_;
     const uint8_t *__restrict__ W = set.W[ti];
     float *__restrict__ y = set.y[ti];
@@ -2189,7 +2190,7 @@ __global__ __launch_bounds__(64 * MOEC_WAVES) void qmoe_tok_kernel(
                                                              wave0 < k ? (u32)(t * k + wave0) * 4u : OOB, 0, 0);
     {
         const int n16 = K >> 4;
-        for (int idx = threadIdx.x; idx < nx * n16; idx += blockDim.x) {
+        for (int idx = threadIdx.x; idx < nx * n16; idx += 64 * MOEC_WAVES) {
             const int m = idx / n16, j = idx - m * n16;
             const f4 *src = reinterpret_cast<const f4 *>(x + (int64_t)(x_mode ? t * k + m : t) * K + 16 * j);
             const f4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
@@ -3053,8 +3054,8 @@ int launch_qmoe_tok_t(const MoeSet &set, int64_t row_bytes, int E, int N, int K,
     if (lds > MOEC_LDS_MAX) return KQ_ERR_ARG;
     auto kern = qmoe_tok_kernel<T>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3((N + RT - 1) / RT, (unsigned)per_tile), dim3(64 * MOEC_WAVES), lds, st, set,
-                       row_bytes, E, N, K, lpr, RT, ids, rw, k, x, x_mode, err);
+    hipLaunchKernelGGL(kern, dim3((N + RT - 1) / RT, (unsigned)per_tile), dim3(64 * MOEC_WAVES), lds, st, x, ids, K,
+                       k, x_mode, T_, set, row_bytes, E, N, lpr, RT, rw, err);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
