@@ -2578,11 +2578,13 @@ inline int cu_count() {
 // narrow one when it still holds at least two row slots (32-weight formats:
 // one), which measured faster for Q6_K and Q8_0; with long rows the wide
 // one's extra waves win.  Q4_K and Q2_K (ring of 4) and Q3_K take the narrow
-// one only for launches of at most 8 row steps per wide row slot (a 8192 x
-// 8192 matrix, an 8B model's projections), where having every step's loads
-// in flight early matters more than the wide one's extra waves (Q3_K 28672 x
-// 8192: +12 % wide; Q2_K 14336 x 4096: +11 % narrow; Q5_K and Q6_K measured
-// better narrow throughout).
+// one only for launches of at most 8 row steps per wide row slot (an 8B
+// model's projections), where having every step's loads in flight early
+// matters more than the wide one's extra waves (Q3_K 28672 x 8192: +12 %
+// wide; Q2_K 14336 x 4096: +11 % narrow; Q5_K and Q6_K measured better narrow
+// throughout); rows of two or more stripes only up to 3 row steps outside a
+// two-format launch (8192 x 8192 Q4_K: 10.6 -> 10.1 us wide, Q2_K 9.6 -> 9.0,
+// since the activations load first).
 // PREFETCH is the number of row steps each wave keeps in flight; it must
 // divide every lanes-per-row value (16, 32, 64).
 template <int T, bool WIDE> constexpr int PREFETCH() {
@@ -2593,7 +2595,7 @@ template <int T> constexpr int NARROW_MAX_STRIPES() {
 }
 // formats that take the narrow configuration only for short launches
 template <int T> constexpr bool NARROW_SHORT_ONLY() { return T == T_Q4_K || T == T_Q3_K || T == T_Q2_K; }
-constexpr int64_t SHORT_LAUNCH_STEPS = 8;
+constexpr int64_t SHORT_LAUNCH_STEPS = 8, SHORT_MULTI_STRIPE_STEPS = 3;
 
 struct B1Cfg {
     int lpr, ns, rs;
@@ -2616,7 +2618,7 @@ template <int T> constexpr int64_t rba_of(int K) { return Fmt<T>::BYTES * (int64
 
 // Batch-1 configuration for a launch over `rows` rows of K columns; false:
 // use the LDS kernel.
-template <int T> bool batch1_cfg(int K, int64_t rows, B1Cfg *c) {
+template <int T> bool batch1_cfg(int K, int64_t rows, B1Cfg *c, bool mixed = false) {
     const int units = (K / Fmt<T>::QK) * Fmt<T>::UPB;
     c->lpr = lanes_per_row(units);
     c->ns = units > 64 ? (units + 63) / 64 : 1;
@@ -2626,7 +2628,10 @@ template <int T> bool batch1_cfg(int K, int64_t rows, B1Cfg *c) {
         // row steps per row slot of the wide configuration
         const int64_t slots = (rows + 64 / c->lpr - 1) / (64 / c->lpr);
         const int64_t per_round = (int64_t)cu_count() * (16 / c->ns);
-        c->wide = (slots + per_round - 1) / per_round > SHORT_LAUNCH_STEPS;
+        const int64_t steps = (slots + per_round - 1) / per_round;
+        // rows of two or more stripes take the wide configuration from
+        // SHORT_MULTI_STRIPE_STEPS on, except in a two-format launch
+        c->wide = steps > SHORT_LAUNCH_STEPS || (!mixed && c->ns >= 2 && steps > SHORT_MULTI_STRIPE_STEPS);
     }
     const int maxw = c->wide ? 16 : 8;
     if (c->ns > maxw || c->lds > 150 * 1024) return false;
@@ -2946,7 +2951,7 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     // the 8-wave configuration when each format would take it for its own rows
     // (short launches of Q4_K, Q3_K and Q2_K; rows of few stripes otherwise)
     B1Cfg na, nb;
-    const bool narrow = batch1_cfg<TA>(K, sa.start[sa.n], &na) && batch1_cfg<TB>(K, sb.start[sb.n], &nb) &&
+    const bool narrow = batch1_cfg<TA>(K, sa.start[sa.n], &na, true) && batch1_cfg<TB>(K, sb.start[sb.n], &nb, true) &&
                         !na.wide && !nb.wide && na.rs == nb.rs;
     if (narrow) ca = na;
     const int64_t rba = Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK), rbb = Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK);
