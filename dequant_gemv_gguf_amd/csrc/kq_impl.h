@@ -1747,15 +1747,14 @@ __global__ __launch_bounds__(LB) void qgemv1_dma_kernel(const float *__restrict_
     p.run(xa, part);
 }
 
-// Prologue of the M-row LDS-ring kernel: x1_load + x1_store for M activation rows (row
-// m at xs + m * (XS + SS), its 16-sums right after it), every activation load
-// ahead of `issue`.
-template <int M, class Issue>
-__device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, float *smem, float *xs, int XS, int SS,
-                                         Issue issue) {
-    const int nthreads = blockDim.x;
+// x1_load / x1_store for M activation rows (row m at xs + m * (XS + SS), its
+// 16-sums right after it), for the M-row LDS-ring kernel.
+template <int M> struct XM {
+    f4 g[M][2][4];
+};
+template <int M> __device__ __forceinline__ XM<M> xm_load(const float *__restrict__ x, int K, int nthreads) {
     const int n16 = K >> 4;
-    f4 xg[M][2][4];
+    XM<M> r;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -1763,11 +1762,13 @@ __device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, flo
             const int idx = threadIdx.x + it * nthreads;
             const f4 *src = reinterpret_cast<const f4 *>(x + (int64_t)m * K + 16 * (idx < n16 ? idx : 0));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) xg[m][it][k] = src[k];
+            for (int k = 0; k < 4; ++k) r.g[m][it][k] = src[k];
         }
-    __builtin_amdgcn_sched_barrier(0);
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
+    return r;
+}
+template <int M>
+__device__ __forceinline__ void xm_store(const XM<M> &r, int K, int nthreads, float *smem, float *xs, int XS, int SS) {
+    const int n16 = K >> 4;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -1777,8 +1778,8 @@ __device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, flo
             float *xm = xs + m * (XS + SS);
             f4 *dst = reinterpret_cast<f4 *>(ok ? xm + xpad(16 * idx) : smem);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dst[k] = xg[m][it][k];
-            (ok ? xm[XS + idx] : smem[16]) = sum16(xg[m][it][0], xg[m][it][1], xg[m][it][2], xg[m][it][3]);
+            for (int k = 0; k < 4; ++k) dst[k] = r.g[m][it][k];
+            (ok ? xm[XS + idx] : smem[16]) = sum16(r.g[m][it][0], r.g[m][it][1], r.g[m][it][2], r.g[m][it][3]);
         }
     wg_sync<true>();
 }
@@ -1786,16 +1787,22 @@ __device__ __forceinline__ void stage_xm(const float *__restrict__ x, int K, flo
 // The LDS-ring kernel at M > 1 (used for Q4_K at M = 2): 8 waves, both
 // activation rows in registers, the same per-row sums as at M = 1.
 template <int T, int D, int LB, bool MS, int M, int LP>
-__global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const Segs sg, int64_t row_bytes, int K, int lpr, int ns,
-                                                         const float *__restrict__ x) {
+__global__ __launch_bounds__(LB) void qgemv1m_dma_kernel(const float *__restrict__ x, int K, int nthreads,
+                                                         const Segs sg, int64_t row_bytes, int lpr, int ns) {
     extern __shared__ float smem[];
     float (*part)[64] = reinterpret_cast<float (*)[64]>(smem);
     float *xs = smem + 16 * 64;
     const int XS = x_stride(K), SS = s_stride(K);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     char *ring = reinterpret_cast<char *>(smem) + b1_ring_offset(K, M) + (size_t)wave * D * DmaGeom<T>::SLOT;
+    // the activation loads first, then the pass and its first row loads (as
+    // in qgemv1_dma_kernel)
+    const XM<M> xr = xm_load<M>(x, K, nthreads);
+    __builtin_amdgcn_sched_barrier(0);
     B1Dma<T, D, MS, M, LP> p(sg, row_bytes, K, lpr, ns, wave, lane, blockIdx.x, gridDim.x, ring);
-    stage_xm<M>(x, K, smem, xs, XS, SS, [&] { p.issue_first(); });
+    p.issue_first();
+    __builtin_amdgcn_sched_barrier(0);
+    xm_store<M>(xr, K, nthreads, smem, xs, XS, SS);
     XRegM<T, M> xa;
 #pragma unroll
     for (int m = 0; m < M; ++m) p.x_from_lds(xa.r[m], xs + m * (XS + SS), xs + m * (XS + SS) + XS, XS, SS);
@@ -2764,7 +2771,8 @@ int launch_qgemvm_dma(const Segs &sg, int64_t row_bytes, int K, const float *x, 
     if (grid == 0) return KQ_OK;
     auto kern = sg.n > 1 ? qgemv1m_dma_kernel<T, D, LB, true, M, 64> : qgemv1m_dma_kernel<T, D, LB, false, M, 64>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * ns * rs), lds, st, sg, row_bytes, K, lpr, ns, x);
+    const int nt = 64 * ns * rs;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nt), lds, st, x, K, nt, sg, row_bytes, lpr, ns);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
