@@ -48,6 +48,10 @@ def lib():
         L.kq_dequant.argtypes = [I, P, I64, P, P]
         L.kq_qgemv.argtypes = [I, P, I64, I64, P, I, P, P]
         L.kq_qgemv_multi.argtypes = [I, P, P, P, I64, P, I, P, P]
+        L.kq_qgemv_mc_workspace_bytes.argtypes = [I64]
+        L.kq_qgemv_mc_workspace_bytes.restype = ctypes.c_size_t
+        L.kq_qgemv_mc_multi.argtypes = [I, P, P, P, I64, P, I, P, P, P]
+        L.kq_qgemv_mc.argtypes = [I, P, I64, I64, P, I, P, P, P]
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
@@ -161,6 +165,33 @@ def kq_qgemv_multi(types, Ws, Ns, K, x, M, ys, stream=None):
     like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
     _check("kq_qgemv_multi", lib().kq_qgemv_multi(count, Ta, Wa, Na, int(K), _ptr(x), int(M), Ya,
                                                   _stream(stream, like)))
+
+
+def kq_qgemv_mc_workspace_bytes(K):
+    return int(lib().kq_qgemv_mc_workspace_bytes(int(K)))
+
+
+def kq_qgemv_mc(qtype, W, N, K, x, M, y, workspace, stream=None):
+    _check("kq_qgemv_mc", lib().kq_qgemv_mc(int(qtype), _ptr(W), int(N), int(K), _ptr(x), int(M), _ptr(y),
+                                            _ptr(workspace), _stream(stream, y)))
+
+
+def kq_qgemv_mc_multi(types, Ws, Ns, K, x, M, ys, workspace, stream=None):
+    """As kq_qgemv_multi, on the matrix-core kernels, with a workspace of
+    kq_qgemv_mc_workspace_bytes(K) bytes."""
+    count = len(Ws)
+    if isinstance(types, int):
+        types = [types] * count
+    if len(types) != count or len(Ns) != count or len(ys) != count:
+        raise ValueError("kq_qgemv_mc_multi: types, Ws, Ns and ys must have the same length")
+    n = max(count, 1)
+    Ta = (ctypes.c_int * n)(*[int(t) for t in types])
+    Wa = (ctypes.c_void_p * n)(*[_addr(w) for w in Ws])
+    Na = (ctypes.c_int64 * n)(*[int(v) for v in Ns])
+    Ya = (ctypes.c_void_p * n)(*[_addr(y) for y in ys])
+    like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
+    _check("kq_qgemv_mc_multi", lib().kq_qgemv_mc_multi(count, Ta, Wa, Na, int(K), _ptr(x), int(M), Ya,
+                                                        _ptr(workspace), _stream(stream, like)))
 
 
 def kq_qmoe_workspace_bytes(T, k, N):

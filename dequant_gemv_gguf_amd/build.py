@@ -54,6 +54,7 @@ PAIRS = ((10, 11), (10, 12), (10, 13), (10, 14), (11, 12), (11, 13), (11, 14),
 def units():
     """(object name, source, defines) of every object of the library."""
     out = [("kqgemv", "kqgemv.hip", []), ("kq_gguf", "kq_gguf.cpp", []), ("kq_stream", "kq_stream.cpp", []),
+           ("kq_mc", "kq_mc.hip", []),
            ("kq_probe", "kq_probe.hip", []), ("kq_stamps", "kq_stamps.hip", [])]
     out += [("kq_type%d" % t, "kq_inst.hip", ["-DKQ_INST_TYPE=%d" % t]) for t in TYPES]
     out += [("kq_mixed%d_%d" % p, "kq_inst.hip", ["-DKQ_INST_A=%d" % p[0], "-DKQ_INST_B=%d" % p[1]])

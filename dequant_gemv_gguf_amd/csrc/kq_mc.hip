@@ -1,0 +1,400 @@
+// kq_mc.hip -- the matrix-core form of the fused dequant-GEMV for the few
+// positions of a speculative-verify pass (Kortex summary, "Out-of-core LLM
+// inference engine written from scratch in Rust", section Approach: the draft
+// tokens are checked in one pass over the weights), for Q4_K and Q6_K rows.
+// Entry points kq_qgemv_mc / kq_qgemv_mc_multi in include/kqgemv.h.
+//
+// At M positions the vector kernels spend M fused multiply-adds per weight on
+// the vector ALU; here the multiply-accumulate goes to the matrix cores and
+// the vector ALU keeps only the unpack and the scales:
+//
+//  * A 16-row tile of W is the B operand (16 columns) of the 16x16x32 f16
+//    instruction (Q4_K: one 32-weight sub-block per instruction) or of the
+//    16x16x16 f16 one (Q6_K: one 16-weight sub-block).  Lane l holds row
+//    l % 16 of the tile at the k positions of lane group g = l / 16; the
+//    quants are fp16 subnormal patterns (q * 2^-24, or 16q * 2^-24 for a
+//    nibble left in place), made with one mask per two weights, as in the
+//    vector kernels.  Q6_K subtracts its offset 32 on the patterns (exact).
+//  * The A operand (16 rows) is the activations: row 2p + l holds limb l
+//    (high, low fp16) of position p, so M = 8 fills it.  Per 256 columns and
+//    position the activations are scaled by 2^e so that their largest
+//    magnitude lies in [2^14, 2^15), then split x * 2^e = hi + lo (22 bits);
+//    the scale is undone exactly on the block's sum.  A preparation launch
+//    writes them, with the 32-column sums that Q4_K's min term needs, into
+//    the caller's workspace in the exact register layout (one 16-byte load
+//    per lane and instruction).
+//  * Slot s of lane group g is column 16 * (s / 4) + 4g + (0, 2, 1, 3)[s % 4]
+//    of a 32-column sub-block: the byte order that the masks produce from a
+//    dword of quants, and a layout in which the first and last four slots
+//    are each one Q6_K scale group (the 16x16x16 instruction takes either
+//    half).
+//  * Output element r of lane (n, g) is row n of the tile at A row 4g + r:
+//    the lane sums the two limbs of positions 2g and 2g + 1 and applies its
+//    own row's sub-block scale (and, Q4_K, min).  Each output element depends
+//    only on its own A row, so a position's result does not depend on M.
+//
+// Work: one persistent work-group of 8 waves per compute unit holds up to 16
+// row tiles (interleaved over the grid); wave w takes the 256-column blocks
+// b = w (mod 8) of every tile, keeps one block's activation operands in
+// registers for all its tiles (the next block's are loaded meanwhile) and the
+// next (tile, block) weights in flight; per-tile sums of the 8 waves are added
+// in wave order through LDS at the end.  Rows are summed as
+//   y = sum over waves w (ascending) of sum over the wave's blocks (ascending)
+//       of [u * (sum over sub-blocks of scale * (dot_hi + dot_lo)) - min terms]
+// with u = 2^(24 - e) -- a fixed order for given K, whatever N, M, tiling or
+// grouping; it is not the vector kernels' order, so these results are within
+// the GEMV tolerance of those, not bit-identical to them.
+#include "kq_impl.h"
+
+namespace kq {
+namespace mc {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+constexpr int THREADS = 512;                  // 8 waves
+constexpr int TW_MAX = 16;                    // row tiles per work-group
+// Workspace per 256 columns: A operands [8 sub-blocks][64 lanes][8 halves],
+// then the 32-column sums [4 lane groups][8 sub-blocks][2 positions] and the
+// unscale factors 2^(24 - e) [4 lane groups][2 positions].
+constexpr int A_BYTES = 8 * 64 * 16, SX_OFF = A_BYTES, U_OFF = SX_OFF + 4 * 8 * 2 * 4;
+constexpr int BLK_BYTES = U_OFF + 4 * 2 * 4;  // 8480
+
+__device__ __forceinline__ int sig(int s) { return (s & 1) * 2 + ((s >> 1) & 1); }   // 0, 2, 1, 3
+
+// ---- preparation: thread (block b, position p, sub-block J) of 32 columns.
+// The 8 threads of one (b, p) are consecutive lanes.
+__global__ __launch_bounds__(256) void mc_prep_kernel(const float *__restrict__ x, int K, int M,
+                                                      uint8_t *__restrict__ ws) {
+    const int tid = blockIdx.x * 256 + threadIdx.x;
+    const int nb = K >> 8;
+    const int b = tid >> 6, p = (tid >> 3) & 7, J = tid & 7;
+    const bool live = b < nb, act = live && p < M;
+    f4 v[8];
+    {
+        const f4 *src = reinterpret_cast<const f4 *>(x + (act ? (int64_t)p * K + 256 * b + 32 * J : 0));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = act ? src[k] : (f4){0.f, 0.f, 0.f, 0.f};
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    // m * 2^e in [2^14, 2^15) for a normal m; e kept where 2^e and 2^(24-e)
+    // are normal floats
+    const int E = (int)(__builtin_bit_cast(u32, m) >> 23);
+    int e = m == 0.f ? 0 : 141 - E;
+    e = e < -100 ? -100 : (e > 126 ? 126 : e);
+    const float s = __builtin_bit_cast(float, (u32)(e + 127) << 23);
+    const float u24 = __builtin_bit_cast(float, (u32)(151 - e) << 23);
+    if (!live) return;
+    uint8_t *blk = ws + (int64_t)b * BLK_BYTES;
+    h8 *A = reinterpret_cast<h8 *>(blk) + J * 64;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        h8 hi, lo;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            const int k = 16 * (sl >> 2) + 4 * g + sig(sl & 3);
+            const float a = v[k >> 2][k & 3] * s;
+            const _Float16 h = (_Float16)a;
+            hi[sl] = h;
+            lo[sl] = (_Float16)(a - (float)h);
+        }
+        A[16 * g + 2 * p] = hi;
+        A[16 * g + 2 * p + 1] = lo;
+    }
+    const float s32 = sum16(v[0], v[1], v[2], v[3]) + sum16(v[4], v[5], v[6], v[7]);
+    reinterpret_cast<float *>(blk + SX_OFF)[((p >> 1) * 8 + J) * 2 + (p & 1)] = s32;
+    if (J == 0) reinterpret_cast<float *>(blk + U_OFF)[(p >> 1) * 2 + (p & 1)] = act ? u24 : 0.f;
+}
+
+// Matrices of one format served by one launch.
+struct McSegs {
+    const uint8_t *W[MAX_SEGS];
+    float *y[MAX_SEGS];
+    int rows[MAX_SEGS];
+    int tstart[MAX_SEGS + 1];   // first tile of each matrix; tstart[n] = tiles
+    int n;
+};
+
+// One block's activation operands as a lane uses them.
+struct BlkX {
+    h8 a[8];
+    f4 sx[4];    // Q4_K: 32-column sums of positions 2g, 2g + 1, by sub-block
+    f2 u;        // 2^(24 - e) of positions 2g, 2g + 1
+};
+template <int T> __device__ __forceinline__ void load_blk(BlkX &bx, const uint8_t *__restrict__ ws, int b, int lane,
+                                                          bool ok) {
+    const uint8_t *blk = ws + (int64_t)(ok ? b : 0) * BLK_BYTES;
+    const h8 *A = reinterpret_cast<const h8 *>(blk) + lane;
+#pragma unroll
+    for (int J = 0; J < 8; ++J) bx.a[J] = A[J * 64];
+    const int g = lane >> 4;
+    if constexpr (T == T_Q4_K) {
+        const f4 *sx = reinterpret_cast<const f4 *>(blk + SX_OFF) + g * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bx.sx[i] = sx[i];
+    }
+    bx.u = reinterpret_cast<const f2 *>(blk + U_OFF)[g];
+}
+
+struct Q4Raw { u4 h; u32 q[8]; };
+struct Q6Raw { u32 ql[8], qh[4]; u4 sc; u32 dw; };
+template <int T> struct McRaw;
+template <> struct McRaw<T_Q4_K> { typedef Q4Raw type; };
+template <> struct McRaw<T_Q6_K> { typedef Q6Raw type; };
+
+// Loads of lane (n, g) for one block of its row at byte `o` of the buffer.
+// Q6_K blocks may start 2 bytes off a dword: the memory system serves the
+// unaligned dword loads, and every field read lies inside the block (d is
+// read as the upper half of the dword ending at the block's last byte).
+__device__ __forceinline__ void load_raw(Q4Raw &r, rsrc_t rs, u32 o, int g) {
+    r.h = ld16(rs, o);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        r.q[2 * c] = ld4(rs, o + 16 + 32 * c + 4 * g);
+        r.q[2 * c + 1] = ld4(rs, o + 32 + 32 * c + 4 * g);
+    }
+}
+__device__ __forceinline__ void load_raw(Q6Raw &r, rsrc_t rs, u32 o, int g) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const u32 base = o + 64 * hh + 16 * q2 + 4 * g;
+            r.ql[(hh * 2 + q2) * 2] = ld4(rs, base);
+            r.ql[(hh * 2 + q2) * 2 + 1] = ld4(rs, base + 32);
+            r.qh[hh * 2 + q2] = ld4(rs, o + 128 + 32 * hh + 16 * q2 + 4 * g);
+        }
+    r.sc = ld16(rs, o + 192);
+    r.dw = ld4(rs, o + 206);
+}
+
+__device__ __forceinline__ f4 mma32(h8 a, u4 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, b), (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma16(h4 a, u32 b0, u32 b1) {
+    const hf2 x0 = __builtin_bit_cast(hf2, b0), x1 = __builtin_bit_cast(hf2, b1);
+    const h4 b = {x0.x, x0.y, x1.x, x1.y};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// The block's contribution to positions 2g, 2g + 1 of lane n's row.
+__device__ __forceinline__ f2 item_value(const Q4Raw &r, const BlkX &bx) {
+    const u32 h0 = r.h.x, h1 = r.h.y, h2 = r.h.z, h3 = r.h.w;
+    const float d = half_lo(h0), dmin = half_lo(h0 >> 16);
+    const u32 sc_lo = h1 & 0x3F3F3F3Fu, m_lo = h2 & 0x3F3F3F3Fu;
+    const u32 sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+    const u32 m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+    float aq0 = 0.f, aq1 = 0.f, am0 = 0.f, am1 = 0.f;
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        const u32 D0 = r.q[2 * (J >> 1)], D1 = r.q[2 * (J >> 1) + 1];
+        const u32 msk = (J & 1) ? 0x00F000F0u : 0x000F000Fu;
+        const u4 bw = {D0 & msk, (D0 >> 8) & msk, D1 & msk, (D1 >> 8) & msk};
+        const f4 D = mma32(bx.a[J], bw);
+        const u32 scw = J < 4 ? sc_lo : sc_hi, mw = J < 4 ? m_lo : m_hi;
+        const float sc = (float)((scw >> (8 * (J & 3))) & 0xFFu), mn = (float)((mw >> (8 * (J & 3))) & 0xFFu);
+        const float dsc = ((J & 1) ? d * 0.0625f : d) * sc;
+        const float dm = dmin * mn;
+        aq0 = __builtin_fmaf(dsc, D[0] + D[1], aq0);
+        aq1 = __builtin_fmaf(dsc, D[2] + D[3], aq1);
+        const f4 sxv = bx.sx[J >> 1];
+        am0 = __builtin_fmaf(dm, (J & 1) ? sxv.z : sxv.x, am0);
+        am1 = __builtin_fmaf(dm, (J & 1) ? sxv.w : sxv.y, am1);
+    }
+    return (f2){__builtin_fmaf(aq0, bx.u.x, -am0), __builtin_fmaf(aq1, bx.u.y, -am1)};
+}
+
+__device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
+    const float d = half_lo(r.dw >> 16);
+    const hf2 off_lo = {(_Float16)(32.f / 16777216.f), (_Float16)(32.f / 16777216.f)};
+    const hf2 off_hi = {(_Float16)(512.f / 16777216.f), (_Float16)(512.f / 16777216.f)};
+    float aq0 = 0.f, aq1 = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const u32 A = r.ql[(hh * 2 + q2) * 2], B = r.ql[(hh * 2 + q2) * 2 + 1], H = r.qh[hh * 2 + q2];
+            const u32 A8 = A >> 8, B8 = B >> 8;
+            const u32 H4l = H << 4, H4r = H >> 4, H2l = H << 2, H6r = H >> 6;
+            u32 w[4][2];
+            w[0][0] = (A & 0x000F000Fu) | (H4l & 0x00300030u);
+            w[0][1] = (A8 & 0x000F000Fu) | (H4r & 0x00300030u);
+            w[1][0] = (B & 0x000F000Fu) | (H2l & 0x00300030u);
+            w[1][1] = (B8 & 0x000F000Fu) | (H6r & 0x00300030u);
+            w[2][0] = (A & 0x00F000F0u) | (H4l & 0x03000300u);
+            w[2][1] = (A8 & 0x00F000F0u) | (H4r & 0x03000300u);
+            w[3][0] = (B & 0x00F000F0u) | (H2l & 0x03000300u);
+            w[3][1] = (B8 & 0x00F000F0u) | (H6r & 0x03000300u);
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const hf2 off = gg < 2 ? off_lo : off_hi;
+                const u32 b0 = __builtin_bit_cast(u32, __builtin_bit_cast(hf2, w[gg][0]) - off);
+                const u32 b1 = __builtin_bit_cast(u32, __builtin_bit_cast(hf2, w[gg][1]) - off);
+                const h8 a8 = bx.a[4 * hh + gg];
+                const h4 a = q2 ? (h4){a8[4], a8[5], a8[6], a8[7]} : (h4){a8[0], a8[1], a8[2], a8[3]};
+                const f4 D = mma16(a, b0, b1);
+                const int j16 = 8 * hh + 2 * gg + q2;
+                const u32 scw = r.sc[j16 >> 2];
+                const float sc = (float)(int)(signed char)(scw >> (8 * (j16 & 3)));
+                const float dsc = (gg < 2 ? d : d * 0.0625f) * sc;
+                aq0 = __builtin_fmaf(dsc, D[0] + D[1], aq0);
+                aq1 = __builtin_fmaf(dsc, D[2] + D[3], aq1);
+            }
+        }
+    return (f2){aq0 * bx.u.x, aq1 * bx.u.y};
+}
+
+// Buffer over tile t's rows and the lane's byte offset of block b in it (OOB
+// past the matrix or for a missing item).
+struct TileAt {
+    rsrc_t rs;
+    u32 o;
+};
+template <int T>
+__device__ __forceinline__ TileAt tile_at(const McSegs &sg, int64_t row_bytes, int t, int b, int n, bool ok) {
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
+    const int row0 = (t - sg.tstart[s]) * 16;
+    const int left = sg.rows[s] - row0;
+    const int nr = !ok ? 0 : (left < 16 ? left : 16);
+    const uintptr_t base = (uintptr_t)(sg.W[s] + (int64_t)row0 * row_bytes);
+    const u32 delta = (u32)(base & 3u);
+    TileAt ta;
+    ta.rs = make_rsrc((const void *)(base - delta), nr ? delta + (u32)(nr * row_bytes) : 0u);
+    ta.o = n < nr ? delta + (u32)(n * row_bytes) + (u32)b * Fmt<T>::BYTES : OOB;
+    return ta;
+}
+
+template <int T>
+__global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
+                                                     int64_t row_bytes) {
+    extern __shared__ float part[];   // [tile][wave][lane][2]
+    typedef typename McRaw<T>::type Raw;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int nwg = gridDim.x, wg = blockIdx.x;
+    const int tiles = sg.tstart[sg.n];
+    const int tw = wg < tiles ? (tiles - wg + nwg - 1) / nwg : 0;
+    const int nb = K >> 8;
+    const int nbw = wave < nb ? (nb - wave + 7) / 8 : 0;
+
+    f2 acc[TW_MAX];
+#pragma unroll
+    for (int i = 0; i < TW_MAX; ++i) acc[i] = (f2){0.f, 0.f};
+
+    BlkX cur_x, nxt_x;
+    Raw cur;
+    {
+        load_blk<T>(nxt_x, ws, wave, lane, nbw > 0);
+        const TileAt ta = tile_at<T>(sg, row_bytes, wg, wave, n, nbw > 0 && tw > 0);
+        load_raw(cur, ta.rs, ta.o, g);
+    }
+    for (int bi = 0; bi < nbw; ++bi) {
+        const int b = wave + 8 * bi;
+        cur_x = nxt_x;
+        load_blk<T>(nxt_x, ws, b + 8, lane, bi + 1 < nbw);
+#pragma unroll
+        for (int ti = 0; ti < TW_MAX; ++ti) {
+            if (ti < tw) {
+                // the next item: tile ti + 1 of this block, else tile 0 of the next
+                const bool same = ti + 1 < tw;
+                const bool ok = same || bi + 1 < nbw;
+                const TileAt ta = tile_at<T>(sg, row_bytes, wg + (same ? ti + 1 : 0) * nwg, same ? b : b + 8, n, ok);
+                Raw nxt;
+                load_raw(nxt, ta.rs, ta.o, g);
+                const f2 v = item_value(cur, cur_x);
+                acc[ti] += v;
+                cur = nxt;
+            }
+        }
+    }
+    // per-tile sums of the eight waves, added in wave order
+#pragma unroll
+    for (int ti = 0; ti < TW_MAX; ++ti)
+        if (ti < tw) reinterpret_cast<f2 *>(part)[(ti * 8 + wave) * 64 + lane] = acc[ti];
+    __syncthreads();
+    for (int ti = wave; ti < tw; ti += 8) {
+        f2 s = (f2){0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 8; ++w) s += reinterpret_cast<const f2 *>(part)[(ti * 8 + w) * 64 + lane];
+        const int t = wg + ti * nwg;
+        int sgi = 0;
+#pragma unroll
+        for (int i = 1; i < MAX_SEGS; ++i) sgi += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
+        const int row = (t - sg.tstart[sgi]) * 16 + n;
+        if (row < sg.rows[sgi]) {
+            float *y = sg.y[sgi];
+            const int64_t rows = sg.rows[sgi];
+            if (2 * g < M) y[(int64_t)(2 * g) * rows + row] = s.x;
+            if (2 * g + 1 < M) y[(int64_t)(2 * g + 1) * rows + row] = s.y;
+        }
+    }
+}
+
+template <int T>
+int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *ws, hipStream_t st) {
+    const int64_t tiles = sg.tstart[sg.n];
+    if (tiles == 0) return KQ_OK;
+    int64_t nwg = std::min<int64_t>(tiles, cu_count());
+    nwg = std::max<int64_t>(nwg, (tiles + TW_MAX - 1) / TW_MAX);
+    const int64_t tw = (tiles + nwg - 1) / nwg;
+    const size_t lds = (size_t)tw * 8 * 64 * sizeof(f2);
+    auto kern = mc_kernel<T>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+} // namespace mc
+
+size_t mc_workspace_bytes(int64_t K) {
+    if (K <= 0 || K % 256 || K > ((int64_t)1 << 20)) return 0;
+    return (size_t)(K / 256) * mc::BLK_BYTES;
+}
+
+// The grouped matrix-core GEMV once its arguments are checked: one
+// preparation launch for x, then one launch per format over its matrices (up
+// to 8 per launch).
+int mc_run(int count, const int *types, const void *const *W, const int64_t *N, int K, const float *x, int M,
+           float *const *y, void *workspace, hipStream_t st) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int nb = K / 256;
+    hipLaunchKernelGGL(mc::mc_prep_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, x, K, M, ws);
+    if (hipGetLastError() != hipSuccess) return KQ_ERR_LAUNCH;
+    for (const int type : {KQ_TYPE_Q4_K, KQ_TYPE_Q6_K}) {
+        const int64_t rb = kq_row_bytes_(type, K);
+        mc::McSegs sg = {};
+        auto flush = [&]() -> int {
+            if (sg.n == 0) return KQ_OK;
+            const int r = type == KQ_TYPE_Q4_K ? mc::launch_mc<T_Q4_K>(sg, rb, K, M, ws, st)
+                                               : mc::launch_mc<T_Q6_K>(sg, rb, K, M, ws, st);
+            sg = mc::McSegs{};
+            return r;
+        };
+        for (int i = 0; i < count; ++i) {
+            if (types[i] != type || N[i] == 0) continue;
+            if (sg.n == MAX_SEGS) {
+                const int r = flush();
+                if (r) return r;
+            }
+            sg.W[sg.n] = static_cast<const uint8_t *>(W[i]);
+            sg.y[sg.n] = y[i];
+            sg.rows[sg.n] = (int)N[i];
+            sg.tstart[sg.n + 1] = sg.tstart[sg.n] + (int)((N[i] + 15) / 16);
+            ++sg.n;
+        }
+        const int r = flush();
+        if (r) return r;
+    }
+    return KQ_OK;
+}
+
+} // namespace kq

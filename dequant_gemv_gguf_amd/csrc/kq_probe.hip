@@ -230,6 +230,21 @@ __global__ __launch_bounds__(64) void mfma4_kernel(const h4 *a, const h4 *b, con
     d[l] = __builtin_amdgcn_mfma_f32_4x4x4f16(a[l], b[l], c[l], 0, 0, 0);
 }
 
+// ---- the 16x16x32 and 16x16x16 f16 matrix instructions on one wave: D =
+// A.B + C for 64 lanes' operands as given (each lane: 8 or 4 halves of A and
+// of B, 4 floats of C), so that their lane layouts can be read off on the host.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(64) void mfma16_kernel(const h8 *a, const h8 *b, const f4 *c, f4 *d, int k32) {
+    const int l = threadIdx.x;
+    if (k32) {
+        d[l] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[l], b[l], c[l], 0, 0, 0);
+    } else {
+        const h8 av = a[l], bv = b[l];
+        const h4 a4 = {av[0], av[1], av[2], av[3]}, b4 = {bv[0], bv[1], bv[2], bv[3]};
+        d[l] = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, c[l], 0, 0, 0);
+    }
+}
+
 // Issue rate of that instruction: `chains` independent accumulators per wave,
 // `iters` instructions each, waves * nwg waves.
 template <int CH>
@@ -312,6 +327,14 @@ int kqp_mfma4(const void *a, const void *b, const float *c, float *d, void *stre
     if (((uintptr_t)a | (uintptr_t)b) & 7 || ((uintptr_t)c | (uintptr_t)d) & 15) return KQ_ERR_ALIGN;
     hipLaunchKernelGGL(mfma4_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const h4 *)a, (const h4 *)b,
                        (const f4 *)c, (f4 *)d);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+int kqp_mfma16(const void *a, const void *b, const float *c, float *d, int k32, void *stream) {
+    if (!a || !b || !c || !d) return KQ_ERR_NULL;
+    if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c | (uintptr_t)d) & 15) return KQ_ERR_ALIGN;
+    hipLaunchKernelGGL(mfma16_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const h8 *)a, (const h8 *)b,
+                       (const f4 *)c, (f4 *)d, k32);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 

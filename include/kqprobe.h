@@ -70,6 +70,12 @@ int kqp_phased_stream(const void *src, uint64_t phase_stride, uint64_t phase_byt
  * 8-B aligned; c, d: 256 floats, 16-B aligned. */
 int kqp_mfma4(const void *a, const void *b, const float *c, float *d, void *stream);
 
+/* The 16x16x32 (k32 != 0) or 16x16x16 (k32 == 0) f16 matrix instruction on
+ * one wave: lane l passes a[l] (8 halves; the first 4 for 16x16x16), b[l]
+ * likewise and c[l] (4 floats), and receives d[l] (4 floats).  a, b: 64 x 8
+ * fp16; c, d: 64 x 4 fp32; all 16-byte aligned device memory. */
+int kqp_mfma16(const void *a, const void *b, const float *c, float *d, int k32, void *stream);
+
 /* Issue rate of the same instruction: nwg work-groups of `waves` waves, each
  * wave `chains` (1, 2, 4 or 8) independent accumulators advanced `iters`
  * times.  sink: nwg * waves * 64 uint32. */
