@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--slots", type=int, default=3, help="stream: device slots in the ring")
     ap.add_argument("--m", type=int, default=1, help="activation rows (verify) or tokens (moe)")
     ap.add_argument("--quant", default="mix", choices=["mix", "q2_k", "q8_0"], help="verify: re-encoding")
+    ap.add_argument("--mc", action="store_true",
+                    help="verify / 70b (Q4_K_M mix): every call on the matrix-core GEMV (kq_qgemv_mc_multi)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the model's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling and launch-floor measurement")
@@ -609,6 +611,12 @@ def main():
             else:
                 groups.append([t])
         L_ = kq.lib()
+        if args.mc and args.quant != "mix":
+            print("bench.py: --mc serves Q4_K and Q6_K matrices (the mix) only", file=sys.stderr)
+            return 2
+        # one workspace per activation width (the calls run in order on one stream)
+        mc_ws = {K: torch.empty(kq.kq_qgemv_mc_workspace_bytes(K), dtype=torch.uint8, device=dev)
+                 for K in xs} if args.mc else {}
         weights = []
         n_mats = 0
         for L in range(layers):
@@ -630,7 +638,18 @@ def main():
                 cls = "+".join(n for (n, _, _, _) in grp)
                 x = xs[K]
                 n_mats += len(grp)
-                if len(grp) == 1:
+                if args.mc:
+                    n = len(grp)
+                    Ta = (ctypes.c_int * n)(*[t for (_, t, _, _) in grp])
+                    Wa = (ctypes.c_void_p * n)(*[W.data_ptr() for W in Ws])
+                    Na = (ctypes.c_int64 * n)(*[N for (_, _, N, _) in grp])
+                    Ya = (ctypes.c_void_p * n)(*[ys[name].data_ptr() for (name, _, _, _) in grp])
+                    sp = ctypes.c_void_p(stream.cuda_stream)
+                    wp = ctypes.c_void_p(mc_ws[K].data_ptr())
+                    launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=x, Ya=Ya, wp=wp, sp=sp:
+                                      check(L_.kq_qgemv_mc_multi(n, Ta, Wa, Na, K, ctypes.c_void_p(x.data_ptr()),
+                                                                 M, Ya, wp, sp))), nbytes, cls))
+                elif len(grp) == 1:
                     N, y = grp[0][2], ys[grp[0][0]]
                     launches.append(((lambda qt=qt, W=Ws[0], N=N, K=K, x=x, y=y:
                                       kq.kq_qgemv(qt, W, N, K, x, M, y, stream)), nbytes, cls))
@@ -648,9 +667,12 @@ def main():
         workload = {"70b": "llama3-70b decode layer x%d, Q4_K_M mix, M=1" % layers,
                     "8b": "llama3-8b decode layer x%d, Q4_K_M mix, M=1" % layers,
                     "verify": "llama3-70b layer shapes x%d, %s, M=%d" % (layers, args.quant, M)}[args.workload]
+        if args.mc:
+            workload += ", matrix-core GEMV"
         config = {"workload": workload, "layers": layers, "hidden": spec["hidden"], "ffn": spec["ffn"],
                   "kv_dim": spec["kv"], "M": M, "matrices_per_step": n_mats, "calls_per_step": len(launches),
-                  "grouped": ", ".join("+".join(t[0] for t in g) for g in groups if len(g) > 1) or "none"}
+                  "grouped": ", ".join("+".join(t[0] for t in g) for g in groups if len(g) > 1) or "none",
+                  "gemv": "matrix-core (kq_qgemv_mc_multi)" if args.mc else "vector (kq_qgemv / kq_qgemv_multi)"}
     elif args.workload == "stream":
         spec = kqsynth.LLAMA3_8B
         layers = args.layers or spec["layers"]

@@ -128,20 +128,6 @@ struct BlkX {
     f4 sx[4];    // Q4_K: 32-column sums of positions 2g, 2g + 1, by sub-block
     f2 u;        // 2^(24 - e) of positions 2g, 2g + 1
 };
-template <int T> __device__ __forceinline__ void load_blk(BlkX &bx, const uint8_t *__restrict__ ws, int b, int lane,
-                                                          bool ok) {
-    const uint8_t *blk = ws + (int64_t)(ok ? b : 0) * BLK_BYTES;
-    const h8 *A = reinterpret_cast<const h8 *>(blk) + lane;
-#pragma unroll
-    for (int J = 0; J < 8; ++J) bx.a[J] = A[J * 64];
-    const int g = lane >> 4;
-    if constexpr (T == T_Q4_K) {
-        const f4 *sx = reinterpret_cast<const f4 *>(blk + SX_OFF) + g * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bx.sx[i] = sx[i];
-    }
-    bx.u = reinterpret_cast<const f2 *>(blk + U_OFF)[g];
-}
 
 struct Q4Raw { u4 h; u32 q[8]; };
 struct Q6Raw { u32 ql[8], qh[4]; u4 sc; u32 dw; };
@@ -149,30 +135,112 @@ template <int T> struct McRaw;
 template <> struct McRaw<T_Q4_K> { typedef Q4Raw type; };
 template <> struct McRaw<T_Q6_K> { typedef Q6Raw type; };
 
-// Loads of lane (n, g) for one block of its row at byte `o` of the buffer.
-// Q6_K blocks may start 2 bytes off a dword: the memory system serves the
-// unaligned dword loads, and every field read lies inside the block (d is
-// read as the upper half of the dword ending at the block's last byte).
-__device__ __forceinline__ void load_raw(Q4Raw &r, rsrc_t rs, u32 o, int g) {
-    r.h = ld16(rs, o);
+// LDS staging of one (tile, block) item: the 16 rows' blocks copied by NLD
+// buffer-to-LDS loads of 16 bytes per lane (1 KB per instruction), row r at
+// r * RS.  Q4_K blocks (144 B) are 16-byte aligned and copied exactly; a
+// Q6_K block (210 B, 2-byte aligned) is copied as the 14 aligned 16-byte
+// pieces that cover it, its first byte `delta` bytes into the row.
+template <int T> struct Geo;
+template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NLD = 3, SLOT = 3072, D = 3; };
+template <> struct Geo<T_Q6_K> { static constexpr int RS = 224, PC = 14, NLD = 4, SLOT = 4096, D = 2; };
+constexpr int BLD = 9, BSLOT = BLD * 1024;   // a block's activation operands: 9 loads
+
+#define MC_LDS __attribute__((address_space(3)))
+
+// The buffer over tile t's rows, aligned down to 16 bytes (dt: the tile's
+// first byte in it); nr = 0 (nothing read) for a missing item.
+struct TileBuf {
+    rsrc_t rs;
+    u32 dt;
+    int nr;
+};
+__device__ __forceinline__ TileBuf tile_buf(const McSegs &sg, int64_t row_bytes, int t, bool ok) {
+    int s = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        r.q[2 * c] = ld4(rs, o + 16 + 32 * c + 4 * g);
-        r.q[2 * c + 1] = ld4(rs, o + 32 + 32 * c + 4 * g);
+    for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
+    const int row0 = (t - sg.tstart[s]) * 16;
+    const int left = sg.rows[s] - row0;
+    // (all of it is uniform over the wave: kept in scalar registers, so the
+    // loads need no loop over distinct descriptors)
+    TileBuf tb;
+    tb.nr = __builtin_amdgcn_readfirstlane((!ok || left <= 0) ? 0 : (left < 16 ? left : 16));
+    const uint64_t base = (uint64_t)(uintptr_t)(sg.W[s] + (int64_t)row0 * row_bytes);
+    tb.dt = __builtin_amdgcn_readfirstlane((u32)(base & 15u));
+    const u32 lo = __builtin_amdgcn_readfirstlane((u32)(base & ~(uint64_t)15));
+    const u32 hi = __builtin_amdgcn_readfirstlane((u32)(base >> 32));
+    const u32 size = __builtin_amdgcn_readfirstlane(tb.nr ? tb.dt + (u32)(tb.nr * row_bytes) : 0u);
+    tb.rs = make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), size);
+    return tb;
+}
+
+// Copies item (tile t, block b) into an LDS slot (every lane takes part; the
+// NLD loads are issued whatever `ok`, so the wait counts below hold).
+template <int T>
+__device__ __forceinline__ void issue_item(const McSegs &sg, int64_t row_bytes, int t, int b, bool ok, char *slot,
+                                           int lane) {
+    typedef Geo<T> G;
+    const TileBuf tb = tile_buf(sg, row_bytes, t, ok);
+#pragma unroll
+    for (int k = 0; k < G::NLD; ++k) {
+        const int p = 64 * k + lane;
+        const int r = p / G::PC, pc = p - r * G::PC;
+        const u32 first = tb.dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
+        const u32 o = (p < 16 * G::PC && r < tb.nr) ? (first & ~15u) + 16u * pc : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tb.rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0, 2 /* nt */);
     }
 }
-__device__ __forceinline__ void load_raw(Q6Raw &r, rsrc_t rs, u32 o, int g) {
+
+// Copies block b's activation operands (workspace layout) into an LDS slot.
+__device__ __forceinline__ void issue_blk(rsrc_t wsr, int b, bool ok, char *slot, int lane) {
+#pragma unroll
+    for (int k = 0; k < BLD; ++k) {
+        const u32 o = 1024u * k + 16u * lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (MC_LDS void *)(slot + 1024 * k), 16,
+                                                 (ok && o < (u32)BLK_BYTES) ? (u32)b * BLK_BYTES + o : OOB, 0, 0, 0);
+    }
+}
+
+template <int T> __device__ __forceinline__ void read_blk(BlkX &bx, const char *slot, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int J = 0; J < 8; ++J) bx.a[J] = *reinterpret_cast<const h8 *>(slot + (J * 64 + lane) * 16);
+    if constexpr (T == T_Q4_K) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bx.sx[i] = *reinterpret_cast<const f4 *>(slot + SX_OFF + g * 64 + 16 * i);
+    }
+    bx.u = *reinterpret_cast<const f2 *>(slot + U_OFF + g * 8);
+}
+
+// Lane (n, g)'s fields of its row's block from the item's LDS slot.
+__device__ __forceinline__ void read_raw(Q4Raw &r, const char *slot, int n, int g, u32) {
+    const char *row = slot + n * 144;
+    r.h = *reinterpret_cast<const u4 *>(row);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        r.q[2 * c] = *reinterpret_cast<const u32 *>(row + 16 + 32 * c + 4 * g);
+        r.q[2 * c + 1] = *reinterpret_cast<const u32 *>(row + 32 + 32 * c + 4 * g);
+    }
+}
+// the dword at byte `off` of a row whose block starts at an even, possibly
+// not 4-aligned, byte
+__device__ __forceinline__ u32 lds_dword(const char *row, u32 off) {
+    const u32 a = off & ~3u;
+    return realign(*reinterpret_cast<const u32 *>(row + a + 4), *reinterpret_cast<const u32 *>(row + a), off & 3u);
+}
+__device__ __forceinline__ void read_raw(Q6Raw &r, const char *slot, int n, int g, u32 delta) {
+    const char *row = slot + n * 224;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-            const u32 base = o + 64 * hh + 16 * q2 + 4 * g;
-            r.ql[(hh * 2 + q2) * 2] = ld4(rs, base);
-            r.ql[(hh * 2 + q2) * 2 + 1] = ld4(rs, base + 32);
-            r.qh[hh * 2 + q2] = ld4(rs, o + 128 + 32 * hh + 16 * q2 + 4 * g);
+            const u32 base = delta + 64 * hh + 16 * q2 + 4 * g;
+            r.ql[(hh * 2 + q2) * 2] = lds_dword(row, base);
+            r.ql[(hh * 2 + q2) * 2 + 1] = lds_dword(row, base + 32);
+            r.qh[hh * 2 + q2] = lds_dword(row, delta + 128 + 32 * hh + 16 * q2 + 4 * g);
         }
-    r.sc = ld16(rs, o + 192);
-    r.dw = ld4(rs, o + 206);
+    r.sc = (u4){lds_dword(row, delta + 192), lds_dword(row, delta + 196), lds_dword(row, delta + 200),
+                lds_dword(row, delta + 204)};
+    r.dw = lds_dword(row, delta + 206);
 }
 
 __device__ __forceinline__ f4 mma32(h8 a, u4 b) {
@@ -251,33 +319,12 @@ __device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
     return (f2){aq0 * bx.u.x, aq1 * bx.u.y};
 }
 
-// Buffer over tile t's rows and the lane's byte offset of block b in it (OOB
-// past the matrix or for a missing item).
-struct TileAt {
-    rsrc_t rs;
-    u32 o;
-};
-template <int T>
-__device__ __forceinline__ TileAt tile_at(const McSegs &sg, int64_t row_bytes, int t, int b, int n, bool ok) {
-    int s = 0;
-#pragma unroll
-    for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
-    const int row0 = (t - sg.tstart[s]) * 16;
-    const int left = sg.rows[s] - row0;
-    const int nr = !ok ? 0 : (left < 16 ? left : 16);
-    const uintptr_t base = (uintptr_t)(sg.W[s] + (int64_t)row0 * row_bytes);
-    const u32 delta = (u32)(base & 3u);
-    TileAt ta;
-    ta.rs = make_rsrc((const void *)(base - delta), nr ? delta + (u32)(nr * row_bytes) : 0u);
-    ta.o = n < nr ? delta + (u32)(n * row_bytes) + (u32)b * Fmt<T>::BYTES : OOB;
-    return ta;
-}
-
 template <int T>
 __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
                                                      int64_t row_bytes) {
-    extern __shared__ float part[];   // [tile][wave][lane][2]
+    typedef Geo<T> G;
     typedef typename McRaw<T>::type Raw;
+    extern __shared__ __align__(16) char smem[];   // per wave: D item slots, a block slot; at the end the sums
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
     const int nwg = gridDim.x, wg = blockIdx.x;
@@ -285,46 +332,72 @@ __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__
     const int tw = wg < tiles ? (tiles - wg + nwg - 1) / nwg : 0;
     const int nb = K >> 8;
     const int nbw = wave < nb ? (nb - wave + 7) / 8 : 0;
+    char *ring = smem + wave * (G::D * G::SLOT + BSLOT);
+    char *bslot = ring + G::D * G::SLOT;
+    const rsrc_t wsr = make_rsrc(ws, (u32)nb * BLK_BYTES);
 
     f2 acc[TW_MAX];
 #pragma unroll
     for (int i = 0; i < TW_MAX; ++i) acc[i] = (f2){0.f, 0.f};
 
-    BlkX cur_x, nxt_x;
-    Raw cur;
-    {
-        load_blk<T>(nxt_x, ws, wave, lane, nbw > 0);
-        const TileAt ta = tile_at<T>(sg, row_bytes, wg, wave, n, nbw > 0 && tw > 0);
-        load_raw(cur, ta.rs, ta.o, g);
-    }
+    // Every item issues the item D - 1 ahead (past the end: nothing read, the
+    // same number of loads), so before computing an item at most (D - 1) NLD
+    // later loads may be outstanding; a block's operands were issued one
+    // block (tw items) before they are read.
+    int iti = 0, ibi = 0, islot = 0, cslot = 0;
+    auto issue = [&]() {
+        issue_item<T>(sg, row_bytes, wg + iti * nwg, wave + 8 * ibi, ibi < nbw, ring + islot * G::SLOT, lane);
+        if (++iti == tw) {
+            iti = 0;
+            ++ibi;
+        }
+        if (++islot == G::D) islot = 0;
+    };
+    issue_blk(wsr, wave, nbw > 0, bslot, lane);
+#pragma unroll
+    for (int d = 0; d < G::D - 1; ++d) issue();
     for (int bi = 0; bi < nbw; ++bi) {
+        if (tw >= G::D - 1)
+            wait_vm<(G::D - 1) * G::NLD>();
+        else
+            wait_vm<G::NLD>();
+        BlkX cx;
+        read_blk<T>(cx, bslot, lane);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_blk(wsr, wave + 8 * (bi + 1), bi + 1 < nbw, bslot, lane);
         const int b = wave + 8 * bi;
-        cur_x = nxt_x;
-        load_blk<T>(nxt_x, ws, b + 8, lane, bi + 1 < nbw);
 #pragma unroll
         for (int ti = 0; ti < TW_MAX; ++ti) {
             if (ti < tw) {
-                // the next item: tile ti + 1 of this block, else tile 0 of the next
-                const bool same = ti + 1 < tw;
-                const bool ok = same || bi + 1 < nbw;
-                const TileAt ta = tile_at<T>(sg, row_bytes, wg + (same ? ti + 1 : 0) * nwg, same ? b : b + 8, n, ok);
-                Raw nxt;
-                load_raw(nxt, ta.rs, ta.o, g);
-                const f2 v = item_value(cur, cur_x);
-                acc[ti] += v;
-                cur = nxt;
+                // the slot refilled now held the previous item: its reads are done
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue();
+                wait_vm<(G::D - 1) * G::NLD>();
+                u32 delta = 0;
+                if constexpr (T == T_Q6_K) {
+                    const TileBuf tb = tile_buf(sg, row_bytes, wg + ti * nwg, true);
+                    delta = (tb.dt + (u32)(n * row_bytes) + (u32)b * Fmt<T>::BYTES) & 15u;
+                }
+                Raw r;
+                read_raw(r, ring + cslot * G::SLOT, n, g, delta);
+                if (++cslot == G::D) cslot = 0;
+                acc[ti] += item_value(r, cx);
             }
         }
     }
-    // per-tile sums of the eight waves, added in wave order
+    // every copy into LDS has landed before the slots are reused for the sums
+    wait_vm<0>();
+    __syncthreads();
+    f2 *part = reinterpret_cast<f2 *>(smem);   // [tile][wave][lane]
 #pragma unroll
     for (int ti = 0; ti < TW_MAX; ++ti)
-        if (ti < tw) reinterpret_cast<f2 *>(part)[(ti * 8 + wave) * 64 + lane] = acc[ti];
+        if (ti < tw) part[(ti * 8 + wave) * 64 + lane] = acc[ti];
     __syncthreads();
+    // per-tile sums of the eight waves, added in wave order
     for (int ti = wave; ti < tw; ti += 8) {
         f2 s = (f2){0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 8; ++w) s += reinterpret_cast<const f2 *>(part)[(ti * 8 + w) * 64 + lane];
+        for (int w = 0; w < 8; ++w) s += part[(ti * 8 + w) * 64 + lane];
         const int t = wg + ti * nwg;
         int sgi = 0;
 #pragma unroll
@@ -346,7 +419,7 @@ int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *
     int64_t nwg = std::min<int64_t>(tiles, cu_count());
     nwg = std::max<int64_t>(nwg, (tiles + TW_MAX - 1) / TW_MAX);
     const int64_t tw = (tiles + nwg - 1) / nwg;
-    const size_t lds = (size_t)tw * 8 * 64 * sizeof(f2);
+    const size_t lds = std::max<size_t>((size_t)8 * (Geo<T>::D * Geo<T>::SLOT + BSLOT), (size_t)tw * 8 * 64 * sizeof(f2));
     auto kern = mc_kernel<T>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
