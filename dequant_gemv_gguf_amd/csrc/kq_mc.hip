@@ -140,10 +140,14 @@ template <> struct McRaw<T_Q6_K> { typedef Q6Raw type; };
 // r * RS.  Q4_K blocks (144 B) are 16-byte aligned and copied exactly; a
 // Q6_K block (210 B, 2-byte aligned) is copied as the 14 aligned 16-byte
 // pieces that cover it, its first byte `delta` bytes into the row.
+// The last of the NLD loads runs on its first REM lanes only (a lane that is
+// switched off writes nothing to LDS), so the slots hold exactly the pieces.
 template <int T> struct Geo;
-template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NLD = 3, SLOT = 3072, D = 3; };
-template <> struct Geo<T_Q6_K> { static constexpr int RS = 224, PC = 14, NLD = 4, SLOT = 4096, D = 2; };
-constexpr int BLD = 9, BSLOT = BLD * 1024;   // a block's activation operands: 9 loads
+template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NLD = 3, REM = 16, SLOT = 2304, D = 4; };
+// (Q6_K rows take 15 pieces in LDS, the last one not read: a row stride of
+// 240 bytes spreads the 16 rows' fields over the LDS banks two lanes a bank)
+template <> struct Geo<T_Q6_K> { static constexpr int RS = 240, PC = 15, NLD = 4, REM = 48, SLOT = 3840, D = 3; };
+constexpr int BLD = 9, BREM = 18, BSLOT = BLK_BYTES;   // a block's activation operands: 9 loads
 
 #define MC_LDS __attribute__((address_space(3)))
 
@@ -185,18 +189,23 @@ __device__ __forceinline__ void issue_item(const McSegs &sg, int64_t row_bytes, 
         const int p = 64 * k + lane;
         const int r = p / G::PC, pc = p - r * G::PC;
         const u32 first = tb.dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
-        const u32 o = (p < 16 * G::PC && r < tb.nr) ? (first & ~15u) + 16u * pc : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(tb.rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0, 2 /* nt */);
+        const u32 o = (r < tb.nr && 16 * pc < 16 + Fmt<T>::BYTES) ? (first & ~15u) + 16u * pc : OOB;
+        if (k < G::NLD - 1 || lane < G::REM)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(tb.rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0,
+                                                     2 /* nt */);
     }
 }
 
 // Copies block b's activation operands (workspace layout) into an LDS slot.
-__device__ __forceinline__ void issue_blk(rsrc_t wsr, int b, bool ok, char *slot, int lane) {
+// The operand rows of positions >= M are not read (the copy writes zeros).
+__device__ __forceinline__ void issue_blk(rsrc_t wsr, int b, bool ok, int M, char *slot, int lane) {
 #pragma unroll
     for (int k = 0; k < BLD; ++k) {
         const u32 o = 1024u * k + 16u * lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (MC_LDS void *)(slot + 1024 * k), 16,
-                                                 (ok && o < (u32)BLK_BYTES) ? (u32)b * BLK_BYTES + o : OOB, 0, 0, 0);
+        const bool used = o >= (u32)A_BYTES || (int)(lane & 15) < 2 * M;
+        if (k < BLD - 1 || lane < BREM)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (MC_LDS void *)(slot + 1024 * k), 16,
+                                                     (ok && used) ? (u32)b * BLK_BYTES + o : OOB, 0, 0, 0);
     }
 }
 
@@ -213,7 +222,7 @@ template <int T> __device__ __forceinline__ void read_blk(BlkX &bx, const char *
 
 // Lane (n, g)'s fields of its row's block from the item's LDS slot.
 __device__ __forceinline__ void read_raw(Q4Raw &r, const char *slot, int n, int g, u32) {
-    const char *row = slot + n * 144;
+    const char *row = slot + n * Geo<T_Q4_K>::RS;
     r.h = *reinterpret_cast<const u4 *>(row);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -221,34 +230,34 @@ __device__ __forceinline__ void read_raw(Q4Raw &r, const char *slot, int n, int 
         r.q[2 * c + 1] = *reinterpret_cast<const u32 *>(row + 32 + 32 * c + 4 * g);
     }
 }
-// the dword at byte `off` of a row whose block starts at an even, possibly
-// not 4-aligned, byte
-__device__ __forceinline__ u32 lds_dword(const char *row, u32 off) {
-    const u32 a = off & ~3u;
-    return realign(*reinterpret_cast<const u32 *>(row + a + 4), *reinterpret_cast<const u32 *>(row + a), off & 3u);
-}
+// A row's block starts `delta` bytes into its LDS row (delta even, possibly
+// not a multiple of 4): each field is read as the two aligned dwords around
+// it and realigned.  d (bytes 208-209) is the half of the dword at 208 that
+// the block's alignment selects.
 __device__ __forceinline__ void read_raw(Q6Raw &r, const char *slot, int n, int g, u32 delta) {
-    const char *row = slot + n * 224;
+    const char *row = slot + n * Geo<T_Q6_K>::RS + (delta & ~3u);
+    const u32 sh = delta & 3u;
+    auto fld = [&](int off) {
+        return realign(*reinterpret_cast<const u32 *>(row + off + 4), *reinterpret_cast<const u32 *>(row + off), sh);
+    };
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-            const u32 base = delta + 64 * hh + 16 * q2 + 4 * g;
-            r.ql[(hh * 2 + q2) * 2] = lds_dword(row, base);
-            r.ql[(hh * 2 + q2) * 2 + 1] = lds_dword(row, base + 32);
-            r.qh[hh * 2 + q2] = lds_dword(row, delta + 128 + 32 * hh + 16 * q2 + 4 * g);
+            const int base = 64 * hh + 16 * q2 + 4 * g;
+            r.ql[(hh * 2 + q2) * 2] = fld(base);
+            r.ql[(hh * 2 + q2) * 2 + 1] = fld(base + 32);
+            r.qh[hh * 2 + q2] = fld(128 + 32 * hh + 16 * q2 + 4 * g);
         }
-    r.sc = (u4){lds_dword(row, delta + 192), lds_dword(row, delta + 196), lds_dword(row, delta + 200),
-                lds_dword(row, delta + 204)};
-    r.dw = lds_dword(row, delta + 206);
+    r.sc = (u4){fld(192), fld(196), fld(200), fld(204)};
+    r.dw = *reinterpret_cast<const u32 *>(row + 208) >> (8 * sh);
 }
 
 __device__ __forceinline__ f4 mma32(h8 a, u4 b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, b), (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
-__device__ __forceinline__ f4 mma16(h4 a, u32 b0, u32 b1) {
-    const hf2 x0 = __builtin_bit_cast(hf2, b0), x1 = __builtin_bit_cast(hf2, b1);
-    const h4 b = {x0.x, x0.y, x1.x, x1.y};
+__device__ __forceinline__ f4 mma16(h4 a, hf2 b0, hf2 b1) {
+    const h4 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
@@ -280,12 +289,15 @@ __device__ __forceinline__ f2 item_value(const Q4Raw &r, const BlkX &bx) {
 }
 
 __device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
-    const float d = half_lo(r.dw >> 16);
+    const float d = half_lo(r.dw);
     const hf2 off_lo = {(_Float16)(32.f / 16777216.f), (_Float16)(32.f / 16777216.f)};
     const hf2 off_hi = {(_Float16)(512.f / 16777216.f), (_Float16)(512.f / 16777216.f)};
     float aq0 = 0.f, aq1 = 0.f;
+    // per half of the block: its 8 sub-blocks' products (independent
+    // instructions back to back), then their scales
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < 2; ++hh) {
+        f4 D[8];
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
             const u32 A = r.ql[(hh * 2 + q2) * 2], B = r.ql[(hh * 2 + q2) * 2 + 1], H = r.qh[hh * 2 + q2];
@@ -303,23 +315,29 @@ __device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const hf2 off = gg < 2 ? off_lo : off_hi;
-                const u32 b0 = __builtin_bit_cast(u32, __builtin_bit_cast(hf2, w[gg][0]) - off);
-                const u32 b1 = __builtin_bit_cast(u32, __builtin_bit_cast(hf2, w[gg][1]) - off);
+                const hf2 b0 = __builtin_bit_cast(hf2, w[gg][0]) - off;
+                const hf2 b1 = __builtin_bit_cast(hf2, w[gg][1]) - off;
                 const h8 a8 = bx.a[4 * hh + gg];
-                const h4 a = q2 ? (h4){a8[4], a8[5], a8[6], a8[7]} : (h4){a8[0], a8[1], a8[2], a8[3]};
-                const f4 D = mma16(a, b0, b1);
-                const int j16 = 8 * hh + 2 * gg + q2;
-                const u32 scw = r.sc[j16 >> 2];
-                const float sc = (float)(int)(signed char)(scw >> (8 * (j16 & 3)));
-                const float dsc = (gg < 2 ? d : d * 0.0625f) * sc;
-                aq0 = __builtin_fmaf(dsc, D[0] + D[1], aq0);
-                aq1 = __builtin_fmaf(dsc, D[2] + D[3], aq1);
+                const h4 a = q2 ? __builtin_shufflevector(a8, a8, 4, 5, 6, 7) : __builtin_shufflevector(a8, a8, 0, 1, 2, 3);
+                D[2 * gg + q2] = mma16(a, b0, b1);
             }
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int j16 = 8 * hh + j;   // scale index 8h + 2g + q2
+            const u32 scw = r.sc[j16 >> 2];
+            const float sc = (float)(int)(signed char)(scw >> (8 * (j16 & 3)));
+            const float dsc = ((j >> 1) < 2 ? d : d * 0.0625f) * sc;
+            aq0 = __builtin_fmaf(dsc, D[j][0] + D[j][1], aq0);
+            aq1 = __builtin_fmaf(dsc, D[j][2] + D[j][3], aq1);
+        }
+    }
     return (f2){aq0 * bx.u.x, aq1 * bx.u.y};
 }
 
-template <int T>
+// TWC: the most tiles a work-group of the launch holds (the tile loop is
+// unrolled that far).
+template <int T, int TWC>
 __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
                                                      int64_t row_bytes) {
     typedef Geo<T> G;
@@ -336,9 +354,9 @@ __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__
     char *bslot = ring + G::D * G::SLOT;
     const rsrc_t wsr = make_rsrc(ws, (u32)nb * BLK_BYTES);
 
-    f2 acc[TW_MAX];
+    f2 acc[TWC];
 #pragma unroll
-    for (int i = 0; i < TW_MAX; ++i) acc[i] = (f2){0.f, 0.f};
+    for (int i = 0; i < TWC; ++i) acc[i] = (f2){0.f, 0.f};
 
     // Every item issues the item D - 1 ahead (past the end: nothing read, the
     // same number of loads), so before computing an item at most (D - 1) NLD
@@ -353,31 +371,32 @@ __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__
         }
         if (++islot == G::D) islot = 0;
     };
-    issue_blk(wsr, wave, nbw > 0, bslot, lane);
+    issue_blk(wsr, wave, nbw > 0, M, bslot, lane);
 #pragma unroll
     for (int d = 0; d < G::D - 1; ++d) issue();
     for (int bi = 0; bi < nbw; ++bi) {
+        // (the block's copy was followed by min(tw, D - 1) items' loads at least)
         if (tw >= G::D - 1)
             wait_vm<(G::D - 1) * G::NLD>();
+        else if (tw >= 2)
+            wait_vm<2 * G::NLD>();
         else
             wait_vm<G::NLD>();
         BlkX cx;
         read_blk<T>(cx, bslot, lane);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_blk(wsr, wave + 8 * (bi + 1), bi + 1 < nbw, bslot, lane);
+        issue_blk(wsr, wave + 8 * (bi + 1), bi + 1 < nbw, M, bslot, lane);
         const int b = wave + 8 * bi;
 #pragma unroll
-        for (int ti = 0; ti < TW_MAX; ++ti) {
+        for (int ti = 0; ti < TWC; ++ti) {
             if (ti < tw) {
                 // the slot refilled now held the previous item: its reads are done
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 issue();
                 wait_vm<(G::D - 1) * G::NLD>();
-                u32 delta = 0;
-                if constexpr (T == T_Q6_K) {
-                    const TileBuf tb = tile_buf(sg, row_bytes, wg + ti * nwg, true);
-                    delta = (tb.dt + (u32)(n * row_bytes) + (u32)b * Fmt<T>::BYTES) & 15u;
-                }
+                // (a tile's first row starts 16-byte aligned: 16 rows into a
+                // 16-byte aligned matrix)
+                const u32 delta = T == T_Q6_K ? ((u32)(n * row_bytes) + (u32)b * Fmt<T>::BYTES) & 15u : 0u;
                 Raw r;
                 read_raw(r, ring + cslot * G::SLOT, n, g, delta);
                 if (++cslot == G::D) cslot = 0;
@@ -390,7 +409,7 @@ __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__
     __syncthreads();
     f2 *part = reinterpret_cast<f2 *>(smem);   // [tile][wave][lane]
 #pragma unroll
-    for (int ti = 0; ti < TW_MAX; ++ti)
+    for (int ti = 0; ti < TWC; ++ti)
         if (ti < tw) part[(ti * 8 + wave) * 64 + lane] = acc[ti];
     __syncthreads();
     // per-tile sums of the eight waves, added in wave order
@@ -420,10 +439,15 @@ int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *
     nwg = std::max<int64_t>(nwg, (tiles + TW_MAX - 1) / TW_MAX);
     const int64_t tw = (tiles + nwg - 1) / nwg;
     const size_t lds = std::max<size_t>((size_t)8 * (Geo<T>::D * Geo<T>::SLOT + BSLOT), (size_t)tw * 8 * 64 * sizeof(f2));
-    auto kern = mc_kernel<T>;
-    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
-    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+    auto run = [&](auto kern) {
+        if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
+        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+    };
+    if (tw <= 2) return run(mc_kernel<T, 2>);
+    if (tw <= 4) return run(mc_kernel<T, 4>);
+    if (tw <= 8) return run(mc_kernel<T, 8>);
+    return run(mc_kernel<T, TW_MAX>);
 }
 
 } // namespace mc
