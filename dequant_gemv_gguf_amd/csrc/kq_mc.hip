@@ -335,17 +335,16 @@ __device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
     return (f2){aq0 * bx.u.x, aq1 * bx.u.y};
 }
 
-// TWC: the most tiles a work-group of the launch holds (the tile loop is
-// unrolled that far).
+// One work-group's share (work-group wg of the nwg that serve sg): TWC is the
+// most tiles a work-group of the launch holds (the tile loop is unrolled that
+// far).  smem: per wave D item slots and a block slot; at the end the sums.
 template <int T, int TWC>
-__global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
-                                                     int64_t row_bytes) {
+__device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, int M, const McSegs &sg,
+                                        int64_t row_bytes, int wg, int nwg, char *smem) {
     typedef Geo<T> G;
     typedef typename McRaw<T>::type Raw;
-    extern __shared__ __align__(16) char smem[];   // per wave: D item slots, a block slot; at the end the sums
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
-    const int nwg = gridDim.x, wg = blockIdx.x;
     const int tiles = sg.tstart[sg.n];
     const int tw = wg < tiles ? (tiles - wg + nwg - 1) / nwg : 0;
     const int nb = K >> 8;
@@ -431,6 +430,73 @@ __global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__
     }
 }
 
+template <int T, int TWC>
+__global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
+                                                     int64_t row_bytes) {
+    extern __shared__ __align__(16) char smem[];
+    mc_body<T, TWC>(ws, K, M, sg, row_bytes, blockIdx.x, gridDim.x, smem);
+}
+
+// Q4_K and Q6_K matrices in one launch (a layer's k and q beside v): the
+// first gb work-groups serve the Q6_K tiles, the others the Q4_K tiles.
+template <int TWA, int TWB>
+__global__ __launch_bounds__(THREADS) void mc_mixed_kernel(const uint8_t *__restrict__ ws, int K, int M,
+                                                           const McSegs sa, int64_t rba, const McSegs sb,
+                                                           int64_t rbb, int gb) {
+    extern __shared__ __align__(16) char smem[];
+    if ((int)blockIdx.x < gb)
+        mc_body<T_Q6_K, TWB>(ws, K, M, sb, rbb, blockIdx.x, gb, smem);
+    else
+        mc_body<T_Q4_K, TWA>(ws, K, M, sa, rba, blockIdx.x - gb, gridDim.x - gb, smem);
+}
+
+template <int T> constexpr size_t ring_lds() { return (size_t)8 * (Geo<T>::D * Geo<T>::SLOT + BSLOT); }
+
+// The split of the grid between the Q6_K (gb work-groups) and Q4_K tiles for
+// which the slowest work-group finishes first; a Q6_K tile is taken to cost
+// 1.8 Q4_K tiles (its bytes and its slower unpack).  0: none fits.
+inline int mixed_split(int64_t ta, int64_t tb, int G, int64_t *twa, int64_t *twb) {
+    int best = 0;
+    double bc = 0;
+    for (int gb = 1; gb < G; ++gb) {
+        if (gb > tb || G - gb > ta) continue;
+        const int64_t b = (tb + gb - 1) / gb, a = (ta + G - gb - 1) / (G - gb);
+        if (a > TW_MAX || b > TW_MAX) continue;
+        const double c = std::max(1.8 * (double)b, (double)a);
+        if (!best || c < bc) {
+            best = gb;
+            bc = c;
+            *twa = a;
+            *twb = b;
+        }
+    }
+    return best;
+}
+
+template <int TWA, int TWB>
+int launch_mixed_tw(const McSegs &sa, int64_t rba, const McSegs &sb, int64_t rbb, int K, int M, const uint8_t *ws,
+                    int gb, int G, size_t lds, hipStream_t st) {
+    auto kern = mc_mixed_kernel<TWA, TWB>;
+    if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(THREADS), lds, st, ws, K, M, sa, rba, sb, rbb, gb);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
+}
+
+// KQ_ERR_ARG when the two do not share one launch well (then separately).
+inline int launch_mc_mixed(const McSegs &sa, int64_t rba, const McSegs &sb, int64_t rbb, int K, int M,
+                           const uint8_t *ws, hipStream_t st) {
+    const int G = cu_count();
+    int64_t twa = 0, twb = 0;
+    const int gb = mixed_split(sa.tstart[sa.n], sb.tstart[sb.n], G, &twa, &twb);
+    if (!gb) return KQ_ERR_ARG;
+    const size_t lds = std::max({ring_lds<T_Q4_K>(), ring_lds<T_Q6_K>(), (size_t)std::max(twa, twb) * 8 * 64 * sizeof(f2)});
+    if (twa <= 4)
+        return twb <= 2 ? launch_mixed_tw<4, 2>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st)
+                        : launch_mixed_tw<4, TW_MAX>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st);
+    return twb <= 2 ? launch_mixed_tw<TW_MAX, 2>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st)
+                    : launch_mixed_tw<TW_MAX, TW_MAX>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st);
+}
+
 template <int T>
 int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *ws, hipStream_t st) {
     const int64_t tiles = sg.tstart[sg.n];
@@ -438,7 +504,7 @@ int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *
     int64_t nwg = std::min<int64_t>(tiles, cu_count());
     nwg = std::max<int64_t>(nwg, (tiles + TW_MAX - 1) / TW_MAX);
     const int64_t tw = (tiles + nwg - 1) / nwg;
-    const size_t lds = std::max<size_t>((size_t)8 * (Geo<T>::D * Geo<T>::SLOT + BSLOT), (size_t)tw * 8 * 64 * sizeof(f2));
+    const size_t lds = std::max<size_t>(ring_lds<T>(), (size_t)tw * 8 * 64 * sizeof(f2));
     auto run = [&](auto kern) {
         if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
@@ -458,39 +524,45 @@ size_t mc_workspace_bytes(int64_t K) {
 }
 
 // The grouped matrix-core GEMV once its arguments are checked: one
-// preparation launch for x, then one launch per format over its matrices (up
-// to 8 per launch).
+// preparation launch for x, then the matrices: Q4_K and Q6_K ones together in
+// one launch when each format has at most 8 and the grid splits well between
+// them, otherwise one launch per format and up to 8 matrices.
 int mc_run(int count, const int *types, const void *const *W, const int64_t *N, int K, const float *x, int M,
            float *const *y, void *workspace, hipStream_t st) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     const int nb = K / 256;
     hipLaunchKernelGGL(mc::mc_prep_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, x, K, M, ws);
     if (hipGetLastError() != hipSuccess) return KQ_ERR_LAUNCH;
-    for (const int type : {KQ_TYPE_Q4_K, KQ_TYPE_Q6_K}) {
-        const int64_t rb = kq_row_bytes_(type, K);
+    std::vector<int> by[2];
+    for (int i = 0; i < count; ++i) {
+        if (N[i] == 0) continue;
+        by[types[i] == KQ_TYPE_Q4_K ? 0 : 1].push_back(i);
+    }
+    const int64_t rb[2] = {kq_row_bytes_(KQ_TYPE_Q4_K, K), kq_row_bytes_(KQ_TYPE_Q6_K, K)};
+    auto segs = [&](int f, size_t from, size_t to) {
         mc::McSegs sg = {};
-        auto flush = [&]() -> int {
-            if (sg.n == 0) return KQ_OK;
-            const int r = type == KQ_TYPE_Q4_K ? mc::launch_mc<T_Q4_K>(sg, rb, K, M, ws, st)
-                                               : mc::launch_mc<T_Q6_K>(sg, rb, K, M, ws, st);
-            sg = mc::McSegs{};
-            return r;
-        };
-        for (int i = 0; i < count; ++i) {
-            if (types[i] != type || N[i] == 0) continue;
-            if (sg.n == MAX_SEGS) {
-                const int r = flush();
-                if (r) return r;
-            }
+        for (size_t j = from; j < to; ++j) {
+            const int i = by[f][j];
             sg.W[sg.n] = static_cast<const uint8_t *>(W[i]);
             sg.y[sg.n] = y[i];
             sg.rows[sg.n] = (int)N[i];
             sg.tstart[sg.n + 1] = sg.tstart[sg.n] + (int)((N[i] + 15) / 16);
             ++sg.n;
         }
-        const int r = flush();
-        if (r) return r;
+        return sg;
+    };
+    if (!by[0].empty() && !by[1].empty() && by[0].size() <= (size_t)MAX_SEGS && by[1].size() <= (size_t)MAX_SEGS) {
+        const int r = mc::launch_mc_mixed(segs(0, 0, by[0].size()), rb[0], segs(1, 0, by[1].size()), rb[1], K, M,
+                                          ws, st);
+        if (r != KQ_ERR_ARG) return r;
     }
+    for (int f = 0; f < 2; ++f)
+        for (size_t j = 0; j < by[f].size(); j += MAX_SEGS) {
+            const mc::McSegs sg = segs(f, j, std::min(by[f].size(), j + MAX_SEGS));
+            const int r = f == 0 ? mc::launch_mc<T_Q4_K>(sg, rb[0], K, M, ws, st)
+                                 : mc::launch_mc<T_Q6_K>(sg, rb[1], K, M, ws, st);
+            if (r) return r;
+        }
     return KQ_OK;
 }
 

@@ -186,3 +186,24 @@ def test_mc_argument_errors_launch_nothing():
     assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 2, P(y), P(ws) + 4, None) == -5
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_mc_two_formats_in_one_launch(M):
+    # a layer's k, q (Q4_K) and v (Q6_K) at 70B shapes: one launch serves both
+    # formats; each matrix keeps its separate-call bits
+    K = 8192
+    mats = [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)]
+    x = kqsynth.activations(M, K, kqsynth.rng_for(21, M, K))
+    xd = dev(x)
+    Ws = [kqsynth.device_matrix(qt, N, K, seed=77 + i, device="cuda") for i, (qt, N) in enumerate(mats)]
+    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N in mats]
+    kq.kq_qgemv_mc_multi([qt for qt, _ in mats], Ws, [N for _, N in mats], K, xd, M, ys, workspace(K))
+    torch.cuda.synchronize()
+    for (qt, N), W, y in zip(mats, Ws, ys):
+        alone = mc_gemv(qt, W, N, K, xd)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), alone.view(np.uint32)), kqsynth.TYPE_NAMES[qt]
+        rows = np.unique(np.concatenate([[0, 15, 16, N - 1], np.random.default_rng(N + M).integers(0, N, 30)]))
+        Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
+        yo, S = oracle.gemv(qt, Wr, len(rows), K, x)
+        check_close(y.cpu().numpy()[:, rows], yo, S, "two formats %s N=%d" % (kqsynth.TYPE_NAMES[qt], N))
