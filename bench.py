@@ -614,9 +614,6 @@ def main():
         if args.mc and args.quant != "mix":
             print("bench.py: --mc serves Q4_K and Q6_K matrices (the mix) only", file=sys.stderr)
             return 2
-        # one workspace per activation width (the calls run in order on one stream)
-        mc_ws = {K: torch.empty(kq.kq_qgemv_mc_workspace_bytes(K), dtype=torch.uint8, device=dev)
-                 for K in xs} if args.mc else {}
         weights = []
         n_mats = 0
         for L in range(layers):
@@ -645,10 +642,9 @@ def main():
                     Na = (ctypes.c_int64 * n)(*[N for (_, _, N, _) in grp])
                     Ya = (ctypes.c_void_p * n)(*[ys[name].data_ptr() for (name, _, _, _) in grp])
                     sp = ctypes.c_void_p(stream.cuda_stream)
-                    wp = ctypes.c_void_p(mc_ws[K].data_ptr())
-                    launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=x, Ya=Ya, wp=wp, sp=sp:
+                    launches.append(((lambda n=n, Ta=Ta, Wa=Wa, Na=Na, K=K, x=x, Ya=Ya, sp=sp:
                                       check(L_.kq_qgemv_mc_multi(n, Ta, Wa, Na, K, ctypes.c_void_p(x.data_ptr()),
-                                                                 M, Ya, wp, sp))), nbytes, cls))
+                                                                 M, Ya, sp))), nbytes, cls))
                 elif len(grp) == 1:
                     N, y = grp[0][2], ys[grp[0][0]]
                     launches.append(((lambda qt=qt, W=Ws[0], N=N, K=K, x=x, y=y:

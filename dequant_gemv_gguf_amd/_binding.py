@@ -48,10 +48,8 @@ def lib():
         L.kq_dequant.argtypes = [I, P, I64, P, P]
         L.kq_qgemv.argtypes = [I, P, I64, I64, P, I, P, P]
         L.kq_qgemv_multi.argtypes = [I, P, P, P, I64, P, I, P, P]
-        L.kq_qgemv_mc_workspace_bytes.argtypes = [I64]
-        L.kq_qgemv_mc_workspace_bytes.restype = ctypes.c_size_t
-        L.kq_qgemv_mc_multi.argtypes = [I, P, P, P, I64, P, I, P, P, P]
-        L.kq_qgemv_mc.argtypes = [I, P, I64, I64, P, I, P, P, P]
+        L.kq_qgemv_mc_multi.argtypes = [I, P, P, P, I64, P, I, P, P]
+        L.kq_qgemv_mc.argtypes = [I, P, I64, I64, P, I, P, P]
         L.kq_qmoe_workspace_bytes.argtypes = [I, I, I64]
         L.kq_qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.kq_qmoe_gemv.argtypes = [I, P, I64, I64, I64, P, P, I, I, P, I, P, P, P, P]
@@ -167,18 +165,13 @@ def kq_qgemv_multi(types, Ws, Ns, K, x, M, ys, stream=None):
                                                   _stream(stream, like)))
 
 
-def kq_qgemv_mc_workspace_bytes(K):
-    return int(lib().kq_qgemv_mc_workspace_bytes(int(K)))
-
-
-def kq_qgemv_mc(qtype, W, N, K, x, M, y, workspace, stream=None):
+def kq_qgemv_mc(qtype, W, N, K, x, M, y, stream=None):
     _check("kq_qgemv_mc", lib().kq_qgemv_mc(int(qtype), _ptr(W), int(N), int(K), _ptr(x), int(M), _ptr(y),
-                                            _ptr(workspace), _stream(stream, y)))
+                                            _stream(stream, y)))
 
 
-def kq_qgemv_mc_multi(types, Ws, Ns, K, x, M, ys, workspace, stream=None):
-    """As kq_qgemv_multi, on the matrix-core kernels, with a workspace of
-    kq_qgemv_mc_workspace_bytes(K) bytes."""
+def kq_qgemv_mc_multi(types, Ws, Ns, K, x, M, ys, stream=None):
+    """As kq_qgemv_multi, on the matrix-core kernels."""
     count = len(Ws)
     if isinstance(types, int):
         types = [types] * count
@@ -191,7 +184,7 @@ def kq_qgemv_mc_multi(types, Ws, Ns, K, x, M, ys, workspace, stream=None):
     Ya = (ctypes.c_void_p * n)(*[_addr(y) for y in ys])
     like = next((y for y in ys if y is not None and not isinstance(y, int)), None)
     _check("kq_qgemv_mc_multi", lib().kq_qgemv_mc_multi(count, Ta, Wa, Na, int(K), _ptr(x), int(M), Ya,
-                                                        _ptr(workspace), _stream(stream, like)))
+                                                        _stream(stream, like)))
 
 
 def kq_qmoe_workspace_bytes(T, k, N):

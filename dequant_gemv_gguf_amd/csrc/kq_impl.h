@@ -3097,12 +3097,10 @@ int launch_dequant_t(const void *src, int64_t n, float *dst, hipStream_t st) {
     X int launch_mixed<A, B>(const std::vector<int> &, size_t *, const std::vector<int> &, size_t *,              \
                              const void *const *, const int64_t *, int, const float *, float *const *, hipStream_t);
 
-// The matrix-core GEMV of the verify pass (kq_mc.hip): workspace bytes for
-// K columns (0 if K is not a positive multiple of 256 up to 2^20), and the
-// grouped call once its arguments are checked (Q4_K and Q6_K matrices only).
-size_t mc_workspace_bytes(int64_t K);
+// The matrix-core GEMV of the verify pass (kq_mc.hip): the grouped call once
+// its arguments are checked (Q4_K and Q6_K matrices only).
 int mc_run(int count, const int *types, const void *const *W, const int64_t *N, int K, const float *x, int M,
-           float *const *y, void *workspace, hipStream_t st);
+           float *const *y, hipStream_t st);
 
 KQ_TYPE_LAUNCHERS(extern template, T_Q4_0)
 KQ_TYPE_LAUNCHERS(extern template, T_Q8_0)

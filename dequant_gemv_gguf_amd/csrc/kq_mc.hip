@@ -18,11 +18,11 @@
 //  * The A operand (16 rows) is the activations: row 2p + l holds limb l
 //    (high, low fp16) of position p, so M = 8 fills it.  Per 256 columns and
 //    position the activations are scaled by 2^e so that their largest
-//    magnitude lies in [2^14, 2^15), then split x * 2^e = hi + lo (22 bits);
-//    the scale is undone exactly on the block's sum.  A preparation launch
-//    writes them, with the 32-column sums that Q4_K's min term needs, into
-//    the caller's workspace in the exact register layout (one 16-byte load
-//    per lane and instruction).
+//    magnitude lies in [2^14, 2^15), then split x * 2^e = hi + lo (about 21
+//    bits); the scale is undone exactly on the block's sum.  Each wave makes
+//    the operands of the blocks it serves from the activations it copies into
+//    LDS (the 32-column sums of Q4_K's min term come from one more matrix
+//    instruction per sub-block).
 //  * Slot s of lane group g is column 16 * (s / 4) + 4g + (0, 2, 1, 3)[s % 4]
 //    of a 32-column sub-block: the byte order that the masks produce from a
 //    dword of quants, and a layout in which the first and last four slots
@@ -55,63 +55,6 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int THREADS = 512;                  // 8 waves
 constexpr int TW_MAX = 16;                    // row tiles per work-group
-// Workspace per 256 columns: A operands [8 sub-blocks][64 lanes][8 halves],
-// then the 32-column sums [4 lane groups][8 sub-blocks][2 positions] and the
-// unscale factors 2^(24 - e) [4 lane groups][2 positions].
-constexpr int A_BYTES = 8 * 64 * 16, SX_OFF = A_BYTES, U_OFF = SX_OFF + 4 * 8 * 2 * 4;
-constexpr int BLK_BYTES = U_OFF + 4 * 2 * 4;  // 8480
-
-__device__ __forceinline__ int sig(int s) { return (s & 1) * 2 + ((s >> 1) & 1); }   // 0, 2, 1, 3
-
-// ---- preparation: thread (block b, position p, sub-block J) of 32 columns.
-// The 8 threads of one (b, p) are consecutive lanes.
-__global__ __launch_bounds__(256) void mc_prep_kernel(const float *__restrict__ x, int K, int M,
-                                                      uint8_t *__restrict__ ws) {
-    const int tid = blockIdx.x * 256 + threadIdx.x;
-    const int nb = K >> 8;
-    const int b = tid >> 6, p = (tid >> 3) & 7, J = tid & 7;
-    const bool live = b < nb, act = live && p < M;
-    f4 v[8];
-    {
-        const f4 *src = reinterpret_cast<const f4 *>(x + (act ? (int64_t)p * K + 256 * b + 32 * J : 0));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = act ? src[k] : (f4){0.f, 0.f, 0.f, 0.f};
-    }
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    // m * 2^e in [2^14, 2^15) for a normal m; e kept where 2^e and 2^(24-e)
-    // are normal floats
-    const int E = (int)(__builtin_bit_cast(u32, m) >> 23);
-    int e = m == 0.f ? 0 : 141 - E;
-    e = e < -100 ? -100 : (e > 126 ? 126 : e);
-    const float s = __builtin_bit_cast(float, (u32)(e + 127) << 23);
-    const float u24 = __builtin_bit_cast(float, (u32)(151 - e) << 23);
-    if (!live) return;
-    uint8_t *blk = ws + (int64_t)b * BLK_BYTES;
-    h8 *A = reinterpret_cast<h8 *>(blk) + J * 64;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        h8 hi, lo;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-            const int k = 16 * (sl >> 2) + 4 * g + sig(sl & 3);
-            const float a = v[k >> 2][k & 3] * s;
-            const _Float16 h = (_Float16)a;
-            hi[sl] = h;
-            lo[sl] = (_Float16)(a - (float)h);
-        }
-        A[16 * g + 2 * p] = hi;
-        A[16 * g + 2 * p + 1] = lo;
-    }
-    const float s32 = sum16(v[0], v[1], v[2], v[3]) + sum16(v[4], v[5], v[6], v[7]);
-    reinterpret_cast<float *>(blk + SX_OFF)[((p >> 1) * 8 + J) * 2 + (p & 1)] = s32;
-    if (J == 0) reinterpret_cast<float *>(blk + U_OFF)[(p >> 1) * 2 + (p & 1)] = act ? u24 : 0.f;
-}
 
 // Matrices of one format served by one launch.
 struct McSegs {
@@ -143,11 +86,12 @@ template <> struct McRaw<T_Q6_K> { typedef Q6Raw type; };
 // The last of the NLD loads runs on its first REM lanes only (a lane that is
 // switched off writes nothing to LDS), so the slots hold exactly the pieces.
 template <int T> struct Geo;
-template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NLD = 3, REM = 16, SLOT = 2304, D = 4; };
+// NP of the PC pieces of a row are read.
+template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NP = 9, NLD = 3, REM = 16, SLOT = 2304, D = 4; };
 // (Q6_K rows take 15 pieces in LDS, the last one not read: a row stride of
 // 240 bytes spreads the 16 rows' fields over the LDS banks two lanes a bank)
-template <> struct Geo<T_Q6_K> { static constexpr int RS = 240, PC = 15, NLD = 4, REM = 48, SLOT = 3840, D = 3; };
-constexpr int BLD = 9, BREM = 18, BSLOT = BLK_BYTES;   // a block's activation operands: 9 loads
+template <> struct Geo<T_Q6_K> { static constexpr int RS = 240, PC = 15, NP = 14, NLD = 4, REM = 48, SLOT = 3840, D = 3; };
+constexpr int BLD = 8, BSLOT = BLD * 1024;   // a block's activations: one 1-KB load per position
 
 #define MC_LDS __attribute__((address_space(3)))
 
@@ -189,35 +133,101 @@ __device__ __forceinline__ void issue_item(const McSegs &sg, int64_t row_bytes, 
         const int p = 64 * k + lane;
         const int r = p / G::PC, pc = p - r * G::PC;
         const u32 first = tb.dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
-        const u32 o = (r < tb.nr && 16 * pc < 16 + Fmt<T>::BYTES) ? (first & ~15u) + 16u * pc : OOB;
+        const u32 o = (r < tb.nr && pc < G::NP) ? (first & ~15u) + 16u * pc : OOB;
         if (k < G::NLD - 1 || lane < G::REM)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(tb.rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0,
                                                      2 /* nt */);
     }
 }
 
-// Copies block b's activation operands (workspace layout) into an LDS slot.
-// The operand rows of positions >= M are not read (the copy writes zeros).
-__device__ __forceinline__ void issue_blk(rsrc_t wsr, int b, bool ok, int M, char *slot, int lane) {
+// Copies the activations of block b (columns 256b .. 256b + 255 of the M
+// rows of x) into an LDS slot, row p at p * 1 KB; rows p >= M are not read
+// (the copy writes zeros), so every block issues the same BLD loads.
+__device__ __forceinline__ void issue_blk(rsrc_t xr, int K, int b, bool ok, int M, char *slot, int lane) {
 #pragma unroll
-    for (int k = 0; k < BLD; ++k) {
-        const u32 o = 1024u * k + 16u * lane;
-        const bool used = o >= (u32)A_BYTES || (int)(lane & 15) < 2 * M;
-        if (k < BLD - 1 || lane < BREM)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (MC_LDS void *)(slot + 1024 * k), 16,
-                                                     (ok && used) ? (u32)b * BLK_BYTES + o : OOB, 0, 0, 0);
-    }
+    for (int p = 0; p < BLD; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (MC_LDS void *)(slot + 1024 * p), 16,
+                                                 (ok && p < M) ? 4u * ((u32)p * K + 256u * b) + 16u * lane : OOB, 0,
+                                                 0, 0);
 }
 
-template <int T> __device__ __forceinline__ void read_blk(BlkX &bx, const char *slot, int lane) {
-    const int g = lane >> 4;
-#pragma unroll
-    for (int J = 0; J < 8; ++J) bx.a[J] = *reinterpret_cast<const h8 *>(slot + (J * 64 + lane) * 16);
-    if constexpr (T == T_Q4_K) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bx.sx[i] = *reinterpret_cast<const f4 *>(slot + SX_OFF + g * 64 + 16 * i);
+// two floats to fp16, rounded toward zero, in one instruction
+__device__ __forceinline__ hf2 pkrtz(float a, float b) {
+    return __builtin_bit_cast(hf2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float swap1(float v) {   // lane l ^ 1
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ u32 swap1u(u32 v) {
+    return (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float max_lanes16_32(float v) {   // max over lanes l, l ^ 16, l ^ 32, l ^ 48
+    {
+        const u32 b = __builtin_bit_cast(u32, v);
+        const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        v = fmaxf(__builtin_bit_cast(float, (u32)p[0]), __builtin_bit_cast(float, (u32)p[1]));
     }
-    bx.u = *reinterpret_cast<const f2 *>(slot + U_OFF + g * 8);
+    {
+        const u32 b = __builtin_bit_cast(u32, v);
+        const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        v = fmaxf(__builtin_bit_cast(float, (u32)p[0]), __builtin_bit_cast(float, (u32)p[1]));
+    }
+    return v;
+}
+
+// The block's matrix operands from its activations in LDS.  Lane (i, g)
+// (i = 2p + limb) reads the four activations of position p at the columns of
+// its lane group in one 16-column half of every sub-block (limb 0 the first,
+// limb 1 the second), splits them into both limbs, and swaps with lane i ^ 1
+// the limb the other one needs.  Scale: the largest magnitude of position
+// p's 256 activations (over the 8 lanes that hold them) times 2^e in
+// [2^14, 2^15).  The 32-column sums (Q4_K) come from one more matrix
+// instruction per sub-block with all-ones weights.
+template <int T> __device__ __forceinline__ void conv_blk(BlkX &bx, const f4 (&v)[8], int lane) {
+    const int limb = lane & 1;
+    float m = 0.f;
+#pragma unroll
+    for (int J = 0; J < 8; ++J)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[J].x), fabsf(v[J].y)), fmaxf(fabsf(v[J].z), fabsf(v[J].w))));
+    m = fmaxf(m, swap1(m));
+    m = max_lanes16_32(m);
+    const int E = (int)(__builtin_bit_cast(u32, m) >> 23);
+    int e = m == 0.f ? 0 : 141 - E;
+    e = e < -100 ? -100 : (e > 126 ? 126 : e);
+    const float s = __builtin_bit_cast(float, (u32)(e + 127) << 23);
+    const float u24 = __builtin_bit_cast(float, (u32)(151 - e) << 23);
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        const float a0 = v[J].x * s, a1 = v[J].y * s, a2 = v[J].z * s, a3 = v[J].w * s;
+        // slots (0, 1), (2, 3) of a half hold columns (0, 2), (1, 3)
+        const hf2 h01 = pkrtz(a0, a2), h23 = pkrtz(a1, a3);
+        const hf2 l01 = pkrtz(a0 - (float)h01.x, a2 - (float)h01.y);
+        const hf2 l23 = pkrtz(a1 - (float)h23.x, a3 - (float)h23.y);
+        const u32 H01 = __builtin_bit_cast(u32, h01), H23 = __builtin_bit_cast(u32, h23);
+        const u32 L01 = __builtin_bit_cast(u32, l01), L23 = __builtin_bit_cast(u32, l23);
+        const u32 r0 = swap1u(limb ? H01 : L01), r1 = swap1u(limb ? H23 : L23);
+        const u4 w = limb ? (u4){r0, r1, L01, L23} : (u4){H01, H23, r0, r1};
+        bx.a[J] = __builtin_bit_cast(h8, w);
+    }
+    // the unscale factors of positions 2g, 2g + 1 (lanes 4g and 4g + 2 hold them)
+    const int g = lane >> 4;
+    const float ua = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (4 * g), __builtin_bit_cast(int, u24)));
+    const float ub =
+        __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (4 * g + 2), __builtin_bit_cast(int, u24)));
+    bx.u = (f2){ua, ub};
+    if constexpr (T == T_Q4_K) {
+        const u4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        const float ka = ua * 0x1p-24f, kb = ub * 0x1p-24f;
+        f4 D[8];
+#pragma unroll
+        for (int J = 0; J < 8; ++J)
+            D[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bx.a[J], __builtin_bit_cast(h8, ones),
+                                                          (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            bx.sx[c] = (f4){(D[2 * c][0] + D[2 * c][1]) * ka, (D[2 * c][2] + D[2 * c][3]) * kb,
+                            (D[2 * c + 1][0] + D[2 * c + 1][1]) * ka, (D[2 * c + 1][2] + D[2 * c + 1][3]) * kb};
+    }
 }
 
 // Lane (n, g)'s fields of its row's block from the item's LDS slot.
@@ -339,7 +349,7 @@ __device__ __forceinline__ f2 item_value(const Q6Raw &r, const BlkX &bx) {
 // most tiles a work-group of the launch holds (the tile loop is unrolled that
 // far).  smem: per wave D item slots and a block slot; at the end the sums.
 template <int T, int TWC>
-__device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, int M, const McSegs &sg,
+__device__ __forceinline__ void mc_body(const float *__restrict__ x, int K, int M, const McSegs &sg,
                                         int64_t row_bytes, int wg, int nwg, char *smem) {
     typedef Geo<T> G;
     typedef typename McRaw<T>::type Raw;
@@ -351,7 +361,7 @@ __device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, i
     const int nbw = wave < nb ? (nb - wave + 7) / 8 : 0;
     char *ring = smem + wave * (G::D * G::SLOT + BSLOT);
     char *bslot = ring + G::D * G::SLOT;
-    const rsrc_t wsr = make_rsrc(ws, (u32)nb * BLK_BYTES);
+    const rsrc_t xr = make_rsrc(x, 4u * (u32)M * (u32)K);
 
     f2 acc[TWC];
 #pragma unroll
@@ -370,7 +380,7 @@ __device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, i
         }
         if (++islot == G::D) islot = 0;
     };
-    issue_blk(wsr, wave, nbw > 0, M, bslot, lane);
+    issue_blk(xr, K, wave, nbw > 0, M, bslot, lane);
 #pragma unroll
     for (int d = 0; d < G::D - 1; ++d) issue();
     for (int bi = 0; bi < nbw; ++bi) {
@@ -381,10 +391,17 @@ __device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, i
             wait_vm<2 * G::NLD>();
         else
             wait_vm<G::NLD>();
-        BlkX cx;
-        read_blk<T>(cx, bslot, lane);
+        f4 xv[8];
+        {
+            const int p = (lane & 15) >> 1, limb = lane & 1, gg = lane >> 4;
+#pragma unroll
+            for (int J = 0; J < 8; ++J)
+                xv[J] = *reinterpret_cast<const f4 *>(bslot + 1024 * p + 4 * (32 * J + 16 * limb + 4 * gg));
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_blk(wsr, wave + 8 * (bi + 1), bi + 1 < nbw, M, bslot, lane);
+        issue_blk(xr, K, wave + 8 * (bi + 1), bi + 1 < nbw, M, bslot, lane);
+        BlkX cx;
+        conv_blk<T>(cx, xv, lane);
         const int b = wave + 8 * bi;
 #pragma unroll
         for (int ti = 0; ti < TWC; ++ti) {
@@ -431,23 +448,23 @@ __device__ __forceinline__ void mc_body(const uint8_t *__restrict__ ws, int K, i
 }
 
 template <int T, int TWC>
-__global__ __launch_bounds__(THREADS) void mc_kernel(const uint8_t *__restrict__ ws, int K, int M, const McSegs sg,
+__global__ __launch_bounds__(THREADS) void mc_kernel(const float *__restrict__ x, int K, int M, const McSegs sg,
                                                      int64_t row_bytes) {
     extern __shared__ __align__(16) char smem[];
-    mc_body<T, TWC>(ws, K, M, sg, row_bytes, blockIdx.x, gridDim.x, smem);
+    mc_body<T, TWC>(x, K, M, sg, row_bytes, blockIdx.x, gridDim.x, smem);
 }
 
 // Q4_K and Q6_K matrices in one launch (a layer's k and q beside v): the
 // first gb work-groups serve the Q6_K tiles, the others the Q4_K tiles.
 template <int TWA, int TWB>
-__global__ __launch_bounds__(THREADS) void mc_mixed_kernel(const uint8_t *__restrict__ ws, int K, int M,
+__global__ __launch_bounds__(THREADS) void mc_mixed_kernel(const float *__restrict__ x, int K, int M,
                                                            const McSegs sa, int64_t rba, const McSegs sb,
                                                            int64_t rbb, int gb) {
     extern __shared__ __align__(16) char smem[];
     if ((int)blockIdx.x < gb)
-        mc_body<T_Q6_K, TWB>(ws, K, M, sb, rbb, blockIdx.x, gb, smem);
+        mc_body<T_Q6_K, TWB>(x, K, M, sb, rbb, blockIdx.x, gb, smem);
     else
-        mc_body<T_Q4_K, TWA>(ws, K, M, sa, rba, blockIdx.x - gb, gridDim.x - gb, smem);
+        mc_body<T_Q4_K, TWA>(x, K, M, sa, rba, blockIdx.x - gb, gridDim.x - gb, smem);
 }
 
 template <int T> constexpr size_t ring_lds() { return (size_t)8 * (Geo<T>::D * Geo<T>::SLOT + BSLOT); }
@@ -474,31 +491,31 @@ inline int mixed_split(int64_t ta, int64_t tb, int G, int64_t *twa, int64_t *twb
 }
 
 template <int TWA, int TWB>
-int launch_mixed_tw(const McSegs &sa, int64_t rba, const McSegs &sb, int64_t rbb, int K, int M, const uint8_t *ws,
+int launch_mixed_tw(const McSegs &sa, int64_t rba, const McSegs &sb, int64_t rbb, int K, int M, const float *x,
                     int gb, int G, size_t lds, hipStream_t st) {
     auto kern = mc_mixed_kernel<TWA, TWB>;
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(THREADS), lds, st, ws, K, M, sa, rba, sb, rbb, gb);
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(THREADS), lds, st, x, K, M, sa, rba, sb, rbb, gb);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
 }
 
 // KQ_ERR_ARG when the two do not share one launch well (then separately).
 inline int launch_mc_mixed(const McSegs &sa, int64_t rba, const McSegs &sb, int64_t rbb, int K, int M,
-                           const uint8_t *ws, hipStream_t st) {
+                           const float *x, hipStream_t st) {
     const int G = cu_count();
     int64_t twa = 0, twb = 0;
     const int gb = mixed_split(sa.tstart[sa.n], sb.tstart[sb.n], G, &twa, &twb);
     if (!gb) return KQ_ERR_ARG;
     const size_t lds = std::max({ring_lds<T_Q4_K>(), ring_lds<T_Q6_K>(), (size_t)std::max(twa, twb) * 8 * 64 * sizeof(f2)});
     if (twa <= 4)
-        return twb <= 2 ? launch_mixed_tw<4, 2>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st)
-                        : launch_mixed_tw<4, TW_MAX>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st);
-    return twb <= 2 ? launch_mixed_tw<TW_MAX, 2>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st)
-                    : launch_mixed_tw<TW_MAX, TW_MAX>(sa, rba, sb, rbb, K, M, ws, gb, G, lds, st);
+        return twb <= 2 ? launch_mixed_tw<4, 2>(sa, rba, sb, rbb, K, M, x, gb, G, lds, st)
+                        : launch_mixed_tw<4, TW_MAX>(sa, rba, sb, rbb, K, M, x, gb, G, lds, st);
+    return twb <= 2 ? launch_mixed_tw<TW_MAX, 2>(sa, rba, sb, rbb, K, M, x, gb, G, lds, st)
+                    : launch_mixed_tw<TW_MAX, TW_MAX>(sa, rba, sb, rbb, K, M, x, gb, G, lds, st);
 }
 
 template <int T>
-int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *ws, hipStream_t st) {
+int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const float *x, hipStream_t st) {
     const int64_t tiles = sg.tstart[sg.n];
     if (tiles == 0) return KQ_OK;
     int64_t nwg = std::min<int64_t>(tiles, cu_count());
@@ -507,7 +524,7 @@ int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *
     const size_t lds = std::max<size_t>(ring_lds<T>(), (size_t)tw * 8 * 64 * sizeof(f2));
     auto run = [&](auto kern) {
         if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;
-        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, ws, K, M, sg, row_bytes);
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(THREADS), lds, st, x, K, M, sg, row_bytes);
         return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH;
     };
     if (tw <= 2) return run(mc_kernel<T, 2>);
@@ -518,21 +535,12 @@ int launch_mc(const McSegs &sg, int64_t row_bytes, int K, int M, const uint8_t *
 
 } // namespace mc
 
-size_t mc_workspace_bytes(int64_t K) {
-    if (K <= 0 || K % 256 || K > ((int64_t)1 << 20)) return 0;
-    return (size_t)(K / 256) * mc::BLK_BYTES;
-}
-
 // The grouped matrix-core GEMV once its arguments are checked: one
 // preparation launch for x, then the matrices: Q4_K and Q6_K ones together in
 // one launch when each format has at most 8 and the grid splits well between
 // them, otherwise one launch per format and up to 8 matrices.
 int mc_run(int count, const int *types, const void *const *W, const int64_t *N, int K, const float *x, int M,
-           float *const *y, void *workspace, hipStream_t st) {
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    const int nb = K / 256;
-    hipLaunchKernelGGL(mc::mc_prep_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, x, K, M, ws);
-    if (hipGetLastError() != hipSuccess) return KQ_ERR_LAUNCH;
+           float *const *y, hipStream_t st) {
     std::vector<int> by[2];
     for (int i = 0; i < count; ++i) {
         if (N[i] == 0) continue;
@@ -553,14 +561,14 @@ int mc_run(int count, const int *types, const void *const *W, const int64_t *N, 
     };
     if (!by[0].empty() && !by[1].empty() && by[0].size() <= (size_t)MAX_SEGS && by[1].size() <= (size_t)MAX_SEGS) {
         const int r = mc::launch_mc_mixed(segs(0, 0, by[0].size()), rb[0], segs(1, 0, by[1].size()), rb[1], K, M,
-                                          ws, st);
+                                          x, st);
         if (r != KQ_ERR_ARG) return r;
     }
     for (int f = 0; f < 2; ++f)
         for (size_t j = 0; j < by[f].size(); j += MAX_SEGS) {
             const mc::McSegs sg = segs(f, j, std::min(by[f].size(), j + MAX_SEGS));
-            const int r = f == 0 ? mc::launch_mc<T_Q4_K>(sg, rb[0], K, M, ws, st)
-                                 : mc::launch_mc<T_Q6_K>(sg, rb[1], K, M, ws, st);
+            const int r = f == 0 ? mc::launch_mc<T_Q4_K>(sg, rb[0], K, M, x, st)
+                                 : mc::launch_mc<T_Q6_K>(sg, rb[1], K, M, x, st);
             if (r) return r;
         }
     return KQ_OK;

@@ -244,10 +244,8 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W, const int6
     return KQ_OK;
 }
 
-size_t kq_qgemv_mc_workspace_bytes(int64_t K) { return mc_workspace_bytes(K); }
-
 int kq_qgemv_mc_multi(int count, const int *types, const void *const *W, const int64_t *N, int64_t K,
-                      const float *x, int M, float *const *y, void *workspace, void *stream) {
+                      const float *x, int M, float *const *y, void *stream) {
     const int chk = kq_multi_check(count, types, W, N, K, x, M, y);
     if (chk || count == 0) return chk;
     bool any = false;
@@ -256,19 +254,16 @@ int kq_qgemv_mc_multi(int count, const int *types, const void *const *W, const i
         any = any || N[i] > 0;
     }
     if (!any) return KQ_OK;
-    if (!workspace) return KQ_ERR_NULL;
-    if (!aligned(workspace, 16)) return KQ_ERR_ALIGN;
     if (device_check()) return KQ_ERR_DEVICE;
-    return mc_run(count, types, W, N, (int)K, x, M, y, workspace, (hipStream_t)stream);
+    return mc_run(count, types, W, N, (int)K, x, M, y, (hipStream_t)stream);
 }
 
-int kq_qgemv_mc(int type, const void *W, int64_t N, int64_t K, const float *x, int M, float *y, void *workspace,
-                void *stream) {
+int kq_qgemv_mc(int type, const void *W, int64_t N, int64_t K, const float *x, int M, float *y, void *stream) {
     const int types[1] = {type};
     const void *const Ws[1] = {W};
     const int64_t Ns[1] = {N};
     float *const ys[1] = {y};
-    return kq_qgemv_mc_multi(1, types, Ws, Ns, K, x, M, ys, workspace, stream);
+    return kq_qgemv_mc_multi(1, types, Ws, Ns, K, x, M, ys, stream);
 }
 
 size_t kq_qmoe_workspace_bytes(int T, int k, int64_t N) {

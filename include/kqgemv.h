@@ -149,39 +149,31 @@ int kq_qgemv_multi(int count, const int *types, const void *const *W,
                    const int64_t *N, int64_t K, const float *x, int M,
                    float *const *y, void *stream);
 
-/* Workspace bytes kq_qgemv_mc and kq_qgemv_mc_multi need for K columns
- * ((K/256) * 8480: the activations of one call in the matrix instructions'
- * operand layout); 0 unless K is a positive multiple of 256, K <= 2^20.
- * Host-only, no HIP call. */
-size_t kq_qgemv_mc_workspace_bytes(int64_t K);
-
 /* Matrix-core fused dequant-GEMV for the few positions of a speculative-verify
  * pass (Kortex summary, "Out-of-core LLM inference engine written from scratch
  * in Rust", section Approach: several positions run through the weights in one
  * pass), for Q4_K and Q6_K matrices: the products and sums go to the 16x16
- * f16 matrix instructions, the vector unit only unpacks quants and applies
- * scales, so the cost per weight hardly grows with M.  Same operation,
- * arguments and limits as kq_qgemv_multi (types must be KQ_TYPE_Q4_K or
- * KQ_TYPE_Q6_K, else KQ_ERR_TYPE), plus
- *   workspace  device memory of kq_qgemv_mc_workspace_bytes(K) bytes,
- *              16-B aligned, overwritten (scratch; calls that may run at the
- *              same time need workspaces of their own).  NULL: KQ_ERR_NULL
- *              (unless no matrix has rows).
- * Every argument is checked before anything is launched.  Accuracy: every
- * output is within 1e-4 * sum_i |w*x| + 1e-6 of the exact sum for finite x
- * with |x| < 2^116 (activations enter as two fp16 limbs, 22 bits, scaled per
- * 256 columns; products and sums in fp32).  Row m of the result does not
- * depend on M or on the other rows of x, and reruns are bit-identical, but
- * the summation order is not that of kq_qgemv: results are not bit-identical
- * to kq_qgemv's.  One launch prepares the activations, then one launch per
- * format (up to 8 matrices each). */
+ * f16 matrix instructions, the vector unit only unpacks quants, splits the
+ * activations and applies scales, so the cost per weight hardly grows with M
+ * (from M = 4 on it is faster than kq_qgemv_multi at 70B shapes).  Same
+ * operation, arguments and limits as kq_qgemv_multi; types must be
+ * KQ_TYPE_Q4_K or KQ_TYPE_Q6_K (else KQ_ERR_TYPE).  Every argument is checked
+ * before anything is launched.  Accuracy: every output is within
+ * 1e-4 * sum_i |w*x| + 1e-6 of the exact sum for finite x with |x| < 2^116
+ * (activations enter as two fp16 limbs, about 21 bits, scaled per 256
+ * columns; products and sums in fp32).  Row m of the result does not depend
+ * on M or on the other rows of x, and reruns are bit-identical, but the
+ * summation order is not that of kq_qgemv: results are not bit-identical to
+ * kq_qgemv's.  Q4_K and Q6_K matrices (up to 8 of each) share one launch when
+ * the grid splits well between them, else one launch per format and up to 8
+ * matrices. */
 int kq_qgemv_mc_multi(int count, const int *types, const void *const *W,
                       const int64_t *N, int64_t K, const float *x, int M,
-                      float *const *y, void *workspace, void *stream);
+                      float *const *y, void *stream);
 
 /* kq_qgemv_mc_multi for one matrix. */
 int kq_qgemv_mc(int type, const void *W, int64_t N, int64_t K, const float *x,
-                int M, float *y, void *workspace, void *stream);
+                int M, float *y, void *stream);
 
 /* Workspace bytes kq_qmoe_gemv needs for T tokens, k slots and N rows when a
  * routing-weighted combine is requested (T*k*N*4); 0 on invalid sizes. */

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kq_version", "kq_status_string", "kq_block_info", "kq_row_bytes",
                             "kq_dequant", "kq_qgemv", "kq_qgemv_multi", "kq_qmoe_workspace_bytes",
-                            "kq_qgemv_mc_workspace_bytes", "kq_qgemv_mc", "kq_qgemv_mc_multi",
+                            "kq_qgemv_mc", "kq_qgemv_mc_multi",
                             "kq_qmoe_gemv", "kq_qmoe_gemv_multi", "kq_qmoe_gemv_noalloc",
                             "kq_gguf_open", "kq_gguf_close", "kq_gguf_version", "kq_gguf_alignment",
                             "kq_gguf_tensor_count", "kq_gguf_find_tensor", "kq_gguf_tensor_info",

@@ -40,15 +40,11 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def workspace(K):
-    return torch.empty(kq.kq_qgemv_mc_workspace_bytes(K), dtype=torch.uint8, device="cuda")
-
-
-def mc_gemv(qtype, W, N, K, x, ws=None):
+def mc_gemv(qtype, W, N, K, x):
     M = x.shape[0]
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     kq.kq_qgemv_mc(qtype, W if isinstance(W, torch.Tensor) else dev(W), N, K,
-                   x if isinstance(x, torch.Tensor) else dev(x), M, y, workspace(K) if ws is None else ws)
+                   x if isinstance(x, torch.Tensor) else dev(x), M, y)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -130,7 +126,7 @@ def test_mc_multi_equals_separate_calls(mats, M):
         host.append(Wh)
         Ws.append(dev(Wh) if N else None)
         ys.append(torch.empty((M, N), dtype=torch.float32, device="cuda") if N else None)
-    kq.kq_qgemv_mc_multi([qt for qt, _ in mats], Ws, [N for _, N in mats], K, xd, M, ys, workspace(K))
+    kq.kq_qgemv_mc_multi([qt for qt, _ in mats], Ws, [N for _, N in mats], K, xd, M, ys)
     torch.cuda.synchronize()
     for (qt, N), Wh, Wd, y in zip(mats, host, Ws, ys):
         if not N:
@@ -158,7 +154,7 @@ def test_mc_full_size_sampled_rows(name, qtype, Ns, K, M):
     Ws = [kqsynth.device_matrix(qtype, N, K, seed=4321 + i + qtype, device="cuda") for i, N in enumerate(Ns)]
     x = kqsynth.activations(M, K, kqsynth.rng_for(17, M, K))
     ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
-    kq.kq_qgemv_mc_multi(qtype, Ws, Ns, K, dev(x), M, ys, workspace(K))
+    kq.kq_qgemv_mc_multi(qtype, Ws, Ns, K, dev(x), M, ys)
     torch.cuda.synchronize()
     for N, W, y in zip(Ns, Ws, ys):
         rows = np.unique(np.concatenate([[0, 1, 15, 16, N - 1, N - 2],
@@ -178,12 +174,11 @@ def test_mc_argument_errors_launch_nothing():
     y = torch.full((2, 8), 7.0, device="cuda")
     L = kq.lib()
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    ws = workspace(K)
-    assert L.kq_qgemv_mc(kqsynth.Q2_K, P(W), 8, K, P(x), 2, P(y), P(ws), None) == -1
-    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 2, P(y), None, None) == -4
-    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 9, P(y), P(ws), None) == -3
-    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K + 32, P(x), 2, P(y), P(ws), None) == -2
-    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 2, P(y), P(ws) + 4, None) == -5
+    assert L.kq_qgemv_mc(kqsynth.Q2_K, P(W), 8, K, P(x), 2, P(y), None) == -1
+    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, None, 2, P(y), None) == -4
+    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 9, P(y), None) == -3
+    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K + 32, P(x), 2, P(y), None) == -2
+    assert L.kq_qgemv_mc(kqsynth.Q4_K, P(W), 8, K, P(x), 2, P(y) + 4, None) == -5
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
 
@@ -198,7 +193,7 @@ def test_mc_two_formats_in_one_launch(M):
     xd = dev(x)
     Ws = [kqsynth.device_matrix(qt, N, K, seed=77 + i, device="cuda") for i, (qt, N) in enumerate(mats)]
     ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N in mats]
-    kq.kq_qgemv_mc_multi([qt for qt, _ in mats], Ws, [N for _, N in mats], K, xd, M, ys, workspace(K))
+    kq.kq_qgemv_mc_multi([qt for qt, _ in mats], Ws, [N for _, N in mats], K, xd, M, ys)
     torch.cuda.synchronize()
     for (qt, N), W, y in zip(mats, Ws, ys):
         alone = mc_gemv(qt, W, N, K, xd)
