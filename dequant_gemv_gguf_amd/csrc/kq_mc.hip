@@ -103,6 +103,8 @@ struct TileBuf {
     int nr;
 };
 __device__ __forceinline__ TileBuf tile_buf(const McSegs &sg, int64_t row_bytes, int t, bool ok) {
+    t = __builtin_amdgcn_readfirstlane(t);
+    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
     int s = 0;
 #pragma unroll
     for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
