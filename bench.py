@@ -214,7 +214,8 @@ def summarize_pmc(args):
     if not args.dominant or not args.launch_class:
         raise SystemExit("--summarize-pmc needs --dominant KERNEL_NAME_START and --launch-class CLASS")
     result = {"kernel": args.dominant, "launch": args.launch_class, "library_sha256_16": library_hash(),
-              "workload": args.workload, "m": args.m, "command": args.pmc_command}
+              "workload": args.workload, "m": args.m, "mc": bool(getattr(args, "mc", False)),
+              "command": args.pmc_command}
     per = {}
     for key, path, counter in (("fetch", args.summarize_pmc[0], "FETCH_SIZE"),
                                ("write", args.summarize_pmc[1], "WRITE_SIZE")):
@@ -903,7 +904,7 @@ def main():
         with open(tfile) as f:
             t = json.load(f)
         if (t.get("library_sha256_16") == library_hash() and t.get("launch") == dom["launch"]
-                and t.get("m", 1) == args.m):
+                and t.get("m", 1) == args.m and bool(t.get("mc", False)) == bool(args.mc)):
             traffic = t.get("bytes_per_launch")
 
     out = {
