@@ -202,3 +202,41 @@ def test_mc_two_formats_in_one_launch(M):
         Wr = W[torch.from_numpy(rows).cuda()].cpu().numpy()
         yo, S = oracle.gemv(qt, Wr, len(rows), K, x)
         check_close(y.cpu().numpy()[:, rows], yo, S, "two formats %s N=%d" % (kqsynth.TYPE_NAMES[qt], N))
+
+
+def test_mc_concurrent_host_threads_give_the_same_bits():
+    # calls from several host threads on their own streams (every launch needs
+    # more than 64 KB of LDS, a limit raised per kernel and device): each
+    # result equals the single-threaded one bit for bit
+    import threading
+    cases = []
+    for i, (qt, N, K, M) in enumerate([(kqsynth.Q4_K, 3000, 8192, 8), (kqsynth.Q6_K, 700, 28672, 4),
+                                       (kqsynth.Q4_K, 64, 4096, 2), (kqsynth.Q6_K, 5000, 2048, 8)]):
+        W = dev(kqsynth.matrix(qt, N, K, kqsynth.rng_for(30, i, qt)))
+        x = dev(kqsynth.activations(M, K, kqsynth.rng_for(31, i)))
+        cases.append((qt, N, K, M, W, x))
+    ref = [mc_gemv(qt, W, N, K, x) for (qt, N, K, M, W, x) in cases]
+    errors = []
+
+    def work(c):
+        try:
+            st = torch.cuda.Stream()
+            qt, N, K, M, W, x = cases[c]
+            outs = [torch.empty((M, N), device="cuda") for _ in range(5)]
+            with torch.cuda.stream(st):
+                for y in outs:
+                    kq.kq_qgemv_mc(qt, W, N, K, x, M, y, st)
+            st.synchronize()
+            for y in outs:
+                if not np.array_equal(y.cpu().numpy().view(np.uint32), ref[c].view(np.uint32)):
+                    errors.append(c)
+        except Exception as e:          # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(c,)) for c in range(len(cases)) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
