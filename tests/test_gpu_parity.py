@@ -255,12 +255,19 @@ def test_qgemv_multi_mixed_formats(case, M):
 
 @pytest.mark.parametrize("K,mats", [(8192, [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 8192)]),
                                     (8192, [(kqsynth.Q4_K, 20480), (kqsynth.Q6_K, 1024)]),
-                                    (4096, [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 4096)])],
-                         ids=["70B-wk+wv+wq", "long-Q4_K", "8B-wk+wv+wq"])
+                                    (4096, [(kqsynth.Q4_K, 1024), (kqsynth.Q6_K, 1024), (kqsynth.Q4_K, 4096)]),
+                                    (2048, [(kqsynth.Q4_K, 24000), (kqsynth.Q6_K, 3000)]),
+                                    (1024, [(kqsynth.Q6_K, 6000), (kqsynth.Q4_K, 48000)]),
+                                    (2048, [(kqsynth.Q5_K, 24000), (kqsynth.Q3_K, 3000)])],
+                         ids=["70B-wk+wv+wq", "long-Q4_K", "8B-wk+wv+wq", "K2048-Q4_K+Q6_K", "K1024-Q6_K+Q4_K",
+                              "K2048-Q5_K+Q3_K"])
 def test_qgemv_multi_mixed_full_size(K, mats):
     # a 70B and an 8B layer's k, v and q projections in one launch (Q4_K,
     # Q6_K, Q4_K: the 8-wave configuration), and Q4_K rows too many for it
-    # beside Q6_K rows (the 16-wave one)
+    # beside Q6_K rows (the 16-wave one); rows shorter than 64 units (two or
+    # four rows per wave: the kernels with the lane count set at run time) in
+    # launches too large for the small-launch kernel (over 20 MB), with and
+    # without a Q4_K side
     say("qgemv_multi mixed full size", mats)
     Ws = [kqsynth.device_matrix(t, n, K, seed=70 + i, device="cuda") for i, (t, n) in enumerate(mats)]
     x = kqsynth.activations(1, K, kqsynth.rng_for(71))
