@@ -95,49 +95,64 @@ constexpr int BLD = 8, BSLOT = BLD * 1024;   // a block's activations: one 1-KB 
 
 #define MC_LDS __attribute__((address_space(3)))
 
-// The buffer over tile t's rows, aligned down to 16 bytes (dt: the tile's
-// first byte in it); nr = 0 (nothing read) for a missing item.
-struct TileBuf {
-    rsrc_t rs;
-    u32 dt;
+// The buffers over a work-group's tiles, looked up once: lane i holds tile
+// wg + i * nwg's (i < tw) -- its rows' first byte aligned down to 16 bytes
+// (lo, hi), that byte's offset dt in the buffer, the rows it has (nr, at most
+// 16) and the buffer's size.  An item reads its tile's entries with one
+// lane-select each, instead of finding the tile's matrix among the segments.
+struct TileTab {
+    u32 lo, hi, dt, size;
     int nr;
 };
-__device__ __forceinline__ TileBuf tile_buf(const McSegs &sg, int64_t row_bytes, int t, bool ok) {
-    t = __builtin_amdgcn_readfirstlane(t);
-    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+__device__ __forceinline__ TileTab tile_tab(const McSegs &sg, int64_t row_bytes, int wg, int nwg, int tw, int lane) {
+    const int t = wg + (lane < tw ? lane : 0) * nwg;   // (lanes past the tiles: a valid tile, unused)
     int s = 0;
 #pragma unroll
     for (int i = 1; i < MAX_SEGS; ++i) s += (i < sg.n && t >= sg.tstart[i]) ? 1 : 0;
-    const int row0 = (t - sg.tstart[s]) * 16;
-    const int left = sg.rows[s] - row0;
-    // (all of it is uniform over the wave: kept in scalar registers, so the
-    // loads need no loop over distinct descriptors)
-    TileBuf tb;
-    tb.nr = __builtin_amdgcn_readfirstlane((!ok || left <= 0) ? 0 : (left < 16 ? left : 16));
-    const uint64_t base = (uint64_t)(uintptr_t)(sg.W[s] + (int64_t)row0 * row_bytes);
-    tb.dt = __builtin_amdgcn_readfirstlane((u32)(base & 15u));
-    const u32 lo = __builtin_amdgcn_readfirstlane((u32)(base & ~(uint64_t)15));
-    const u32 hi = __builtin_amdgcn_readfirstlane((u32)(base >> 32));
-    const u32 size = __builtin_amdgcn_readfirstlane(tb.nr ? tb.dt + (u32)(tb.nr * row_bytes) : 0u);
-    tb.rs = make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), size);
-    return tb;
+    int ts = 0, rows = 0;
+    const uint8_t *W = sg.W[0];
+#pragma unroll
+    for (int i = 0; i < MAX_SEGS; ++i)
+        if (s == i) {
+            ts = sg.tstart[i];
+            rows = sg.rows[i];
+            W = sg.W[i];
+        }
+    const int row0 = (t - ts) * 16;
+    const int left = rows - row0;
+    TileTab tt;
+    tt.nr = (lane >= tw || left <= 0) ? 0 : (left < 16 ? left : 16);
+    const uint64_t base = (uint64_t)(uintptr_t)(W + (int64_t)row0 * row_bytes);
+    tt.dt = (u32)(base & 15u);
+    tt.lo = (u32)(base & ~(uint64_t)15);
+    tt.hi = (u32)(base >> 32);
+    tt.size = tt.nr ? tt.dt + (u32)(tt.nr * row_bytes) : 0u;
+    return tt;
 }
 
-// Copies item (tile t, block b) into an LDS slot (every lane takes part; the
-// NLD loads are issued whatever `ok`, so the wait counts below hold).
+// Copies item (the work-group's tile i, block b) into an LDS slot (every lane
+// takes part; the NLD loads are issued whatever `ok`, so the wait counts
+// below hold; a missing item reads nothing).  i is uniform over the wave.
 template <int T>
-__device__ __forceinline__ void issue_item(const McSegs &sg, int64_t row_bytes, int t, int b, bool ok, char *slot,
+__device__ __forceinline__ void issue_item(const TileTab &tt, int64_t row_bytes, int i, int b, bool ok, char *slot,
                                            int lane) {
     typedef Geo<T> G;
-    const TileBuf tb = tile_buf(sg, row_bytes, t, ok);
+    // (every value uniform: kept in scalar registers, so the loads need no
+    // loop over distinct descriptors)
+    const int nr = ok ? __builtin_amdgcn_readlane(tt.nr, i) : 0;
+    const u32 dt = (u32)__builtin_amdgcn_readlane((int)tt.dt, i);
+    const u32 lo = (u32)__builtin_amdgcn_readlane((int)tt.lo, i);
+    const u32 hi = (u32)__builtin_amdgcn_readlane((int)tt.hi, i);
+    const u32 size = ok ? (u32)__builtin_amdgcn_readlane((int)tt.size, i) : 0u;
+    const rsrc_t rs = make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), size);
 #pragma unroll
     for (int k = 0; k < G::NLD; ++k) {
         const int p = 64 * k + lane;
         const int r = p / G::PC, pc = p - r * G::PC;
-        const u32 first = tb.dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
-        const u32 o = (r < tb.nr && pc < G::NP) ? (first & ~15u) + 16u * pc : OOB;
+        const u32 first = dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
+        const u32 o = (r < nr && pc < G::NP) ? (first & ~15u) + 16u * pc : OOB;
         if (k < G::NLD - 1 || lane < G::REM)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(tb.rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0,
                                                      2 /* nt */);
     }
 }
@@ -364,6 +379,7 @@ __device__ __forceinline__ void mc_body(const float *__restrict__ x, int K, int 
     char *ring = smem + wave * (G::D * G::SLOT + BSLOT);
     char *bslot = ring + G::D * G::SLOT;
     const rsrc_t xr = make_rsrc(x, 4u * (u32)M * (u32)K);
+    const TileTab tt = tile_tab(sg, row_bytes, wg, nwg, tw, lane);
 
     f2 acc[TWC];
 #pragma unroll
@@ -371,11 +387,14 @@ __device__ __forceinline__ void mc_body(const float *__restrict__ x, int K, int 
 
     // Every item issues the item D - 1 ahead (past the end: nothing read, the
     // same number of loads), so before computing an item at most (D - 1) NLD
-    // later loads may be outstanding; a block's operands were issued one
-    // block (tw items) before they are read.
+    // later loads may be outstanding (loads complete in issue order; in a
+    // block's first D - 1 items this also waits for part of the next block's
+    // activations, issued in between -- counting those loads too measured no
+    // faster); a block's operands were issued one block (tw items) before
+    // they are read.
     int iti = 0, ibi = 0, islot = 0, cslot = 0;
     auto issue = [&]() {
-        issue_item<T>(sg, row_bytes, wg + iti * nwg, wave + 8 * ibi, ibi < nbw, ring + islot * G::SLOT, lane);
+        issue_item<T>(tt, row_bytes, iti, wave + 8 * ibi, ibi < nbw, ring + islot * G::SLOT, lane);
         if (++iti == tw) {
             iti = 0;
             ++ibi;
