@@ -85,6 +85,10 @@ template <> struct McRaw<T_Q6_K> { typedef Q6Raw type; };
 // pieces that cover it, its first byte `delta` bytes into the row.
 // The last of the NLD loads runs on its first REM lanes only (a lane that is
 // switched off writes nothing to LDS), so the slots hold exactly the pieces.
+// The loads go through the caches as usual (no non-temporal hint): a block's
+// first and last 128-byte lines are shared with the blocks beside it, which
+// other waves read a little later, and kept in the caches they are fetched
+// from memory again less often.
 template <int T> struct Geo;
 // NP of the PC pieces of a row are read.
 template <> struct Geo<T_Q4_K> { static constexpr int RS = 144, PC = 9, NP = 9, NLD = 3, REM = 16, SLOT = 2304, D = 4; };
@@ -152,8 +156,7 @@ __device__ __forceinline__ void issue_item(const TileTab &tt, int64_t row_bytes,
         const u32 first = dt + (u32)(r * row_bytes) + (u32)b * Fmt<T>::BYTES;
         const u32 o = (r < nr && pc < G::NP) ? (first & ~15u) + 16u * pc : OOB;
         if (k < G::NLD - 1 || lane < G::REM)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0,
-                                                     2 /* nt */);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MC_LDS void *)(slot + 1024 * k), 16, o, 0, 0, 0);
     }
 }
 
