@@ -2931,14 +2931,6 @@ template <int T> bool batch1_wide_cfg(int K, B1Cfg *c) {
     return K / 16 <= 2 * 64 * c->ns * c->rs;
 }
 
-// Ring depth of a side (format T, the other side's format O) of the 16-wave
-// mixed kernel with the register ring and the lane count set at run time:
-// beside a large-unit format's ring Q4_K keeps one step in flight there (two
-// spilled 4-5 registers).
-template <int T, int O> constexpr int MIXED_WIDE_RT_D() {
-    return (T == T_Q4_K && BIG_UNIT<O>()) ? 1 : PREFETCH<T, true>();
-}
-
 // Two K-quant formats (type ids TA < TB) with the same K in one launch: up to
 // MAX_SEGS matrices of each; returns how many of each it served.
 template <int TA, int TB>
@@ -2950,6 +2942,7 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
         return KQ_ERR_ARG;
     const int G = 64 / ca.lpr;
     Segs sa, sb;
+    const size_t pa0 = *pa, pb0 = *pb;
     next_segs(ia, pa, W, N, y, G, &sa);
     next_segs(ib, pb, W, N, y, G, &sb);
     int64_t bytes = 0;
@@ -2957,25 +2950,32 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     for (int i = 0; i < sb.n; ++i) bytes += sb.rows[i] * rba_of<TB>(K);
     if (small_launch(K, bytes)) return launch_seg_small<TA, TB>(sa, rba_of<TA>(K), sb, rba_of<TB>(K), K, x, st);
     // the 8-wave configuration when each format would take it for its own rows
-    // (short launches of Q4_K, Q3_K and Q2_K; rows of few stripes otherwise)
+    // (short launches of Q4_K, Q3_K and Q2_K; rows of few stripes otherwise);
+    // else the formats go to launches of their own: two formats' code in one
+    // 16-wave kernel needs more than the 128 registers a lane has there (it
+    // spilled 44-116 bytes a lane)
     B1Cfg na, nb;
     const bool narrow = batch1_cfg<TA>(K, sa.start[sa.n], &na, true) && batch1_cfg<TB>(K, sb.start[sb.n], &nb, true) &&
                         !na.wide && !nb.wide && na.rs == nb.rs;
-    if (narrow) ca = na;
+    if (!narrow) {
+        *pa = pa0;
+        *pb = pb0;
+        return KQ_ERR_ARG;
+    }
+    ca = na;
     const int64_t rba = Fmt<TA>::BYTES * (int64_t)(K / Fmt<TA>::QK), rbb = Fmt<TB>::BYTES * (int64_t)(K / Fmt<TB>::QK);
     // work-groups each format needs for one step per row slot; when both do
     // not fit one per compute unit, the units are split so that the slowest
     // work-group finishes first: a work-group makes a whole number of row
     // steps, each costing its format's row bytes weighted by the format's
     // relative time per byte, and ties go to the split closer to proportional.
-    // The large-unit formats keep one row step in flight in the 16-wave
-    // configuration (weight 1.8) and two in the 8-wave one (weight 1.1).
+    // The large-unit formats keep two row steps in flight (weight 1.1).
     const int64_t need_a = (((int64_t)sa.start[sa.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t need_b = (((int64_t)sb.start[sb.n] + G - 1) / G + ca.rs - 1) / ca.rs;
     const int64_t cap = cu_count();
     int64_t ga = need_a, gb = need_b;
     if (ga + gb > cap) {
-        const double big = narrow ? 1.1 : 1.8;
+        const double big = 1.1;
         const double wa = (BIG_UNIT<TA>() ? big : 1.0) * rba, wb = (BIG_UNIT<TB>() ? big : 1.0) * rbb;
         double best = 0, best_even = 0;
         for (int64_t b = 1; b < cap && b <= need_b; ++b) {
@@ -2995,21 +2995,16 @@ int launch_mixed(const std::vector<int> &ia, size_t *pa, const std::vector<int> 
     size_t lds = ca.lds > cb.lds ? ca.lds : cb.lds;
     // rows of 64 units or more (lpr 64) get the kernels with the lane count fixed
     const bool l64 = ca.lpr == 64;
-    auto kern = narrow ? (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 64>
-                              : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 0>)
-                       : (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, false, 64>
-                              : qgemv1_mixed_kernel<TA, MIXED_WIDE_RT_D<TA, TB>(), TB, MIXED_WIDE_RT_D<TB, TA>(),
-                                                    1024, false, 0>);
+    auto kern = l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 64>
+                    : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, false, 0>;
     if constexpr (TA == T_Q4_K || TB == T_Q4_K) {
         // the Q4_K side through the LDS ring
         B1Cfg cq = ca;
-        cq.wide = !narrow;
+        cq.wide = false;
         if (dma_ok<T_Q4_K>(cq, TA == T_Q4_K ? sa : sb, TA == T_Q4_K ? rba : rbb, K)) {
             lds = std::max(lds, dma_lds<T_Q4_K>(cq, K));
-            kern = narrow ? (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 64>
-                                 : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 0>)
-                          : (l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true, 64>
-                                 : qgemv1_mixed_kernel<TA, PREFETCH<TA, true>(), TB, PREFETCH<TB, true>(), 1024, true, 0>);
+            kern = l64 ? qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 64>
+                       : qgemv1_mixed_kernel<TA, PREFETCH<TA, false>(), TB, PREFETCH<TB, false>(), 512, true, 0>;
         }
     }
     if (allow_lds(kern, lds) != hipSuccess) return KQ_ERR_LAUNCH;

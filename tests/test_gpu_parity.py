@@ -221,7 +221,8 @@ MIXED = [
             (kqsynth.Q4_K, 7)]),
     (1280, [(kqsynth.Q4_0, 7), (kqsynth.Q5_K, 64), (kqsynth.Q4_K, 3), (kqsynth.Q8_0, 5)]),
     (768, [(kqsynth.Q3_K, 70), (kqsynth.Q4_K, 9)]),
-    # five stripes per row: the 16-wave configuration for both formats
+    # five stripes per row: each format would take the 16-wave configuration,
+    # so the two go to launches of their own
     (20480, [(kqsynth.Q5_K, 40), (kqsynth.Q6_K, 21), (kqsynth.Q5_K, 7)]),
     # more matrices of one format than a launch takes: a mixed launch of 8 + 3,
     # then the remaining two in a grouped launch
@@ -264,7 +265,7 @@ def test_qgemv_multi_mixed_formats(case, M):
 def test_qgemv_multi_mixed_full_size(K, mats):
     # a 70B and an 8B layer's k, v and q projections in one launch (Q4_K,
     # Q6_K, Q4_K: the 8-wave configuration), and Q4_K rows too many for it
-    # beside Q6_K rows (the 16-wave one); rows shorter than 64 units (two or
+    # beside Q6_K rows (separate 16-wave launches); rows shorter than 64 units (two or
     # four rows per wave: the kernels with the lane count set at run time) in
     # launches too large for the small-launch kernel (over 20 MB), with and
     # without a Q4_K side
